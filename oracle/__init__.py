@@ -1,0 +1,172 @@
+"""CPU oracle for the block-quantized decode GEMV — test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports it, and it imports nothing from the product.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64 decode and fp64
+accumulation in ascending k).  This module only marshals numpy arrays into
+it, splits output rows across threads when asked (each thread runs the same
+plain loop on its own rows, so the result does not depend on the split), and
+loops over expert slots for the routed-expert case.
+
+Every function is pinned by ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-std=c99",
+                               "-fno-fast-math", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        p = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        lib.oracle_q8g64.argtypes = [p, p, i64, i64, p, i64, i64, i64, i64, p, p, i64]
+        lib.oracle_q8g64.restype = ctypes.c_int
+        lib.oracle_q4g32.argtypes = [p, p, p, i64, i64, p, i64, i64, i64, i64, p, p, i64]
+        lib.oracle_q4g32.restype = ctypes.c_int
+        lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_half_to_double.restype = ctypes.c_double
+        lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_double.restype = ctypes.c_double
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def half_to_double(bits: int) -> float:
+    return _load().oracle_half_to_double(int(bits))
+
+
+def bf16_to_double(bits: int) -> float:
+    return _load().oracle_bf16_to_double(int(bits))
+
+
+def _row_splits(N: int, threads: int):
+    threads = max(1, min(int(threads), N if N > 0 else 1))
+    edges = [N * t // threads for t in range(threads + 1)]
+    return [(edges[t], edges[t + 1]) for t in range(threads)]
+
+
+def _check_x(x: np.ndarray, K: int):
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    if x.ndim == 1:
+        x = x[None, :]
+    if x.shape[1] < K:
+        raise ValueError("x rows shorter than K")
+    return x
+
+
+def q8g64(q: np.ndarray, scale: np.ndarray, x: np.ndarray, threads: int = 1):
+    """y, a = oracle Q8G64 GEMV.
+
+    q [N][K] int8, scale [N][K/64] uint16 (fp16 bits), x [m][>=K] uint16
+    (bf16 bits).  Returns (y, a), each float64 [m][N]."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    scale = np.ascontiguousarray(scale, dtype=np.uint16)
+    N, K = q.shape
+    if K % 64 or scale.shape != (N, K // 64):
+        raise ValueError("bad Q8G64 shapes")
+    x = _check_x(x, K)
+    m, ldx = x.shape
+    y = np.zeros((m, N), np.float64)
+    a = np.zeros((m, N), np.float64)
+    lib = _load()
+
+    def run(rng):
+        rc = lib.oracle_q8g64(_ptr(q), _ptr(scale), N, K, _ptr(x), m, ldx,
+                              rng[0], rng[1], _ptr(y), _ptr(a), N)
+        if rc != 0:
+            raise RuntimeError("oracle_q8g64 failed")
+
+    splits = _row_splits(N, threads)
+    if len(splits) == 1:
+        run(splits[0])
+    else:
+        with ThreadPoolExecutor(len(splits)) as ex:
+            list(ex.map(run, splits))
+    return y, a
+
+
+def q4g32(codes: np.ndarray, scale: np.ndarray, minv: np.ndarray, x: np.ndarray,
+          threads: int = 1):
+    """y, a = oracle Q4G32 GEMV.
+
+    codes [N][K/2] uint8 (even k in the low nibble), scale/minv [N][K/32]
+    uint16 (fp16 bits), x [m][>=K] uint16 (bf16 bits)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scale = np.ascontiguousarray(scale, dtype=np.uint16)
+    minv = np.ascontiguousarray(minv, dtype=np.uint16)
+    N, half_k = codes.shape
+    K = 2 * half_k
+    if K % 32 or scale.shape != (N, K // 32) or minv.shape != (N, K // 32):
+        raise ValueError("bad Q4G32 shapes")
+    x = _check_x(x, K)
+    m, ldx = x.shape
+    y = np.zeros((m, N), np.float64)
+    a = np.zeros((m, N), np.float64)
+    lib = _load()
+
+    def run(rng):
+        rc = lib.oracle_q4g32(_ptr(codes), _ptr(scale), _ptr(minv), N, K, _ptr(x),
+                              m, ldx, rng[0], rng[1], _ptr(y), _ptr(a), N)
+        if rc != 0:
+            raise RuntimeError("oracle_q4g32 failed")
+
+    splits = _row_splits(N, threads)
+    if len(splits) == 1:
+        run(splits[0])
+    else:
+        with ThreadPoolExecutor(len(splits)) as ex:
+            list(ex.map(run, splits))
+    return y, a
+
+
+def grouped_q4g32(experts, ids, x_slots, threads: int = 1):
+    """Routed-expert decode: slot j uses expert ids[j] and its own x row.
+
+    experts: sequence of (codes, scale, minv) canonical arrays, one per expert
+    ids:     expert index per slot
+    x_slots: [n_slots][>=K] bf16 bits (row j is slot j's activation)
+    Returns (y, a), each float64 [n_slots][N]; each slot is computed and
+    written separately, with no weighting across slots."""
+    x_slots = np.ascontiguousarray(x_slots, dtype=np.uint16)
+    ys, as_ = [], []
+    for j, e in enumerate(ids):
+        codes, scale, minv = experts[int(e)]
+        y, a = q4g32(codes, scale, minv, x_slots[j:j + 1], threads=threads)
+        ys.append(y[0])
+        as_.append(a[0])
+    return np.stack(ys), np.stack(as_)
+
+
+def within_tolerance(y_test, y_ref, a_ref, rel: float = 2e-3):
+    """The acceptance test: |y - y_ref| <= rel * sum_k |w x| per output,
+    evaluated in fp64; y must be finite.  Returns a boolean mask."""
+    y_test = np.asarray(y_test, np.float64)
+    return np.isfinite(y_test) & (np.abs(y_test - y_ref) <= rel * a_ref)

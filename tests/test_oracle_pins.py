@@ -1,0 +1,307 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test checks the oracle against something other than itself: values
+worked by hand from the format definition, closed forms, invariants,
+special cases that reduce to numpy's own fp16/bf16 decoding and float64
+matmul, and exact-arithmetic inputs where any summation order is exact.
+Together they catch a dropped term, a wrong sign, a wrong group or nibble
+index, or a transposed operand anywhere in the oracle.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from weight_only_block_amd import synth
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_fp16_decoder_matches_numpy_on_every_pattern():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.half_to_double(b) for b in bits])
+    finite = np.isfinite(ref)
+    assert np.array_equal(got[finite], ref[finite])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[np.isinf(ref)], ref[np.isinf(ref)])
+
+
+def test_bf16_decoder_matches_numpy_on_every_pattern():
+    bits = np.arange(65536, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        ref = (bits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    got = np.array([oracle.bf16_to_double(b) for b in bits])
+    finite = np.isfinite(ref)
+    assert np.array_equal(got[finite], ref[finite])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+
+
+# ------------------------------------------------------- hand-worked values
+
+def test_q8g64_two_group_worked_example(golden_dir):
+    g = _load(golden_dir, "q8g64_two_group.json")
+    K = g["K"]
+    q = np.where(np.arange(K) < 64, 1, -2).astype(np.int8)[None, :]
+    s = np.array(g["scale_fp16_bits"], np.uint16)
+    x = np.zeros((g["m"], K), np.uint16)
+    for i, (lo, hi) in enumerate(g["x_bf16_bits_by_row"]):
+        x[i, :64] = lo
+        x[i, 64:] = hi
+    y, a = oracle.q8g64(q, s, x)
+    assert np.array_equal(y, np.array(g["y"]))
+    assert np.array_equal(a, np.array(g["a"]))
+
+
+def test_q4g32_two_group_worked_example(golden_dir):
+    g = _load(golden_dir, "q4g32_two_group.json")
+    codes = np.stack([np.frombuffer(bytes.fromhex(h), np.uint8) for h in g["codes_hex_by_row"]])
+    s = np.array(g["scale_fp16_bits"], np.uint16)
+    mn = np.array(g["min_fp16_bits"], np.uint16)
+    K = g["K"]
+    x = np.zeros((2, K), np.uint16)
+    x[0, 0::2] = 0x3F80          # 1.0 on even k
+    x[1, :] = 0x3F80             # 1.0 everywhere
+    y, a = oracle.q4g32(codes, s, mn, x)
+    assert np.array_equal(y, np.array(g["y"]))
+    assert np.array_equal(a, np.array(g["a"]))
+
+
+# ------------------------------------------------------------ closed forms
+
+def test_zero_scales_give_exact_zero():
+    rng = synth.rng_for(99, 1)
+    q, s = synth.q8g64_weights(rng, 37, 256)
+    x = synth.activations(rng, 3, 256)
+    y, a = oracle.q8g64(q, np.zeros_like(s), x)
+    assert np.all(y == 0.0) and np.all(a == 0.0)
+    codes, s4, mn4 = synth.q4g32_weights(rng, 37, 256)
+    y, a = oracle.q4g32(codes, np.zeros_like(s4), np.zeros_like(mn4), x)
+    assert np.all(y == 0.0) and np.all(a == 0.0)
+
+
+def test_q4_zero_scale_reduces_to_min_times_group_sums():
+    # With every scale 0, w[n][k] = min[n][k/32] and the codes drop out:
+    # y[i][n] = sum_g min[n][g] * (sum of x[i] over group g).
+    rng = synth.rng_for(99, 2)
+    N, K, m = 11, 160, 2
+    codes, _, mn = synth.q4g32_weights(rng, N, K)
+    x = synth.activations(rng, m, K)
+    y, _ = oracle.q4g32(codes, np.zeros((N, K // 32), np.uint16), mn, x)
+    xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    gsum = xf.reshape(m, K // 32, 32).sum(axis=2)              # [m][G]
+    mins = mn.view(np.float16).astype(np.float64)              # [N][G]
+    expect = gsum @ mins.T
+    assert np.allclose(y, expect, rtol=0, atol=1e-12 * np.abs(xf).sum())
+
+
+def test_constant_codes_closed_form():
+    # q[n][k] = c for all k: y[i][n] = c * sum_g scale[n][g] * groupsum_g(x_i).
+    rng = synth.rng_for(99, 3)
+    N, K = 5, 320
+    _, s = synth.q8g64_weights(rng, N, K)
+    x = synth.activations(rng, 2, K)
+    for c in (-128, -1, 0, 1, 127):
+        q = np.full((N, K), c, np.int8)
+        y, _ = oracle.q8g64(q, s, x)
+        xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        gsum = xf.reshape(2, K // 64, 64).sum(axis=2)
+        expect = c * (gsum @ s.view(np.float16).astype(np.float64).T)
+        assert np.allclose(y, expect, rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------- invariants
+
+def _split_even_odd(x):
+    x1 = x.copy(); x1[:, 1::2] = 0
+    x2 = x.copy(); x2[:, 0::2] = 0
+    return x1, x2
+
+
+def test_linearity_in_x_q8():
+    rng = synth.rng_for(99, 4)
+    q, s = synth.q8g64_weights(rng, 23, 512)
+    x = synth.activations(rng, 2, 512)
+    x1, x2 = _split_even_odd(x)                 # disjoint supports: x1 + x2 == x exactly
+    y, a = oracle.q8g64(q, s, x)
+    y1, _ = oracle.q8g64(q, s, x1)
+    y2, _ = oracle.q8g64(q, s, x2)
+    assert np.all(np.abs(y - (y1 + y2)) <= 1e-12 * a)
+    # y(2x) == 2 y(x) exactly: doubling a bf16 is exact (exponent + 1).
+    x2x = (x.astype(np.uint32) + (1 << 7)).astype(np.uint16)
+    y2x, a2x = oracle.q8g64(q, s, x2x)
+    assert np.array_equal(y2x, 2 * y) and np.array_equal(a2x, 2 * a)
+
+
+def test_linearity_in_x_q4():
+    rng = synth.rng_for(99, 5)
+    codes, s, mn = synth.q4g32_weights(rng, 23, 512)
+    x = synth.activations(rng, 2, 512)
+    x1, x2 = _split_even_odd(x)
+    y, a = oracle.q4g32(codes, s, mn, x)
+    y1, _ = oracle.q4g32(codes, s, mn, x1)
+    y2, _ = oracle.q4g32(codes, s, mn, x2)
+    assert np.all(np.abs(y - (y1 + y2)) <= 1e-12 * a)
+    neg = (x ^ 0x8000).astype(np.uint16)        # flip every sign bit
+    yn, an = oracle.q4g32(codes, s, mn, neg)
+    assert np.array_equal(yn, -y) and np.array_equal(an, a)
+
+
+def test_linearity_in_scales():
+    rng = synth.rng_for(99, 6)
+    q, s = synth.q8g64_weights(rng, 9, 256)
+    x = synth.activations(rng, 1, 256)
+    y, a = oracle.q8g64(q, s, x)
+    s2 = (s.astype(np.uint32) + (1 << 10)).astype(np.uint16)    # fp16 exponent + 1
+    assert np.array_equal(s2.view(np.float16).astype(np.float64),
+                          2 * s.view(np.float16).astype(np.float64))
+    y2, a2 = oracle.q8g64(q, s2, x)
+    assert np.array_equal(y2, 2 * y) and np.array_equal(a2, 2 * a)
+    codes, s4, mn4 = synth.q4g32_weights(rng, 9, 256)
+    y, a = oracle.q4g32(codes, s4, mn4, x)
+    s4b = (s4.astype(np.uint32) + (1 << 10)).astype(np.uint16)
+    mn4b = np.where(mn4 & 0x7FFF, mn4.astype(np.uint32) + (1 << 10), mn4).astype(np.uint16)
+    y2, a2 = oracle.q4g32(codes, s4b, mn4b, x)
+    assert np.array_equal(y2, 2 * y) and np.array_equal(a2, 2 * a)
+
+
+def test_abs_sum_bounds_and_sign_cases():
+    rng = synth.rng_for(99, 7)
+    q, s = synth.q8g64_weights(rng, 17, 192)
+    x = synth.activations(rng, 2, 192)
+    y, a = oracle.q8g64(q, s, x)
+    assert np.all(np.abs(y) <= a)
+    qpos = np.abs(q.astype(np.int16)).astype(np.int8)
+    xpos = (x & 0x7FFF).astype(np.uint16)
+    yp, ap = oracle.q8g64(qpos, s, xpos)
+    assert np.allclose(yp, ap, rtol=1e-15, atol=0)
+
+
+def test_row_thread_split_is_bitwise_invariant():
+    rng = synth.rng_for(99, 8)
+    q, s = synth.q8g64_weights(rng, 301, 640)
+    x = synth.activations(rng, 3, 640)
+    y1, a1 = oracle.q8g64(q, s, x, threads=1)
+    y4, a4 = oracle.q8g64(q, s, x, threads=7)
+    assert np.array_equal(y1, y4) and np.array_equal(a1, a4)
+
+
+# ------------------------------------------------- library special cases
+
+def _dense_q8(q, s):
+    return q.astype(np.float64) * np.repeat(s.view(np.float16).astype(np.float64), 64, axis=1)
+
+
+def _dense_q4(codes, s, mn):
+    c = np.empty((codes.shape[0], codes.shape[1] * 2), np.float64)
+    c[:, 0::2] = codes & 0x0F
+    c[:, 1::2] = codes >> 4
+    return (c * np.repeat(s.view(np.float16).astype(np.float64), 32, axis=1)
+            + np.repeat(mn.view(np.float16).astype(np.float64), 32, axis=1))
+
+
+def _xf(x):
+    return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_brute_force_q8_every_int8_value():
+    rng = synth.rng_for(99, 9)
+    q = rng.permutation(np.arange(-128, 128)).astype(np.int8).reshape(4, 64)
+    s = synth.to_fp16_bits(rng.uniform(1e-3, 2e-2, size=(4, 1)))
+    x = synth.activations(rng, 4, 64)
+    y, a = oracle.q8g64(q, s, x)
+    ref = _xf(x) @ _dense_q8(q, s).T
+    assert np.all(np.abs(y - ref) <= 1e-12 * a)
+    assert np.allclose(a, np.abs(_xf(x)) @ np.abs(_dense_q8(q, s)).T, rtol=1e-12)
+
+
+def test_brute_force_q4_every_code():
+    rng = synth.rng_for(99, 10)
+    c = rng.permutation(np.repeat(np.arange(16), 16)).astype(np.uint8).reshape(4, 64)
+    codes = synth.pack_nibbles(c)
+    s = synth.to_fp16_bits(rng.uniform(1e-3, 2e-2, size=(4, 2)))
+    mn = synth.to_fp16_bits(rng.uniform(-0.1, 0.0, size=(4, 2)))
+    x = synth.activations(rng, 4, 64)
+    y, a = oracle.q4g32(codes, s, mn, x)
+    ref = _xf(x) @ _dense_q4(codes, s, mn).T
+    assert np.all(np.abs(y - ref) <= 1e-12 * a)
+
+
+def test_one_hot_pins_group_and_nibble_index():
+    # x = e_k picks column k of W: pins which scale/min/nibble each k uses.
+    N, K = 3, 192
+    n_idx = np.arange(N)[:, None]
+    k_idx = np.arange(K)[None, :]
+    q = (((7 * k_idx + 3 * n_idx) % 255) - 127).astype(np.int8)
+    s = synth.to_fp16_bits(2.0 ** (np.arange(K // 64)[None, :] - n_idx))
+    x = np.zeros((K, K), np.uint16)
+    x[np.arange(K), np.arange(K)] = 0x3F80
+    y, _ = oracle.q8g64(q, s, x)                    # y[k][n] = W[n][k]
+    expect = q.astype(np.float64) * 2.0 ** (k_idx // 64 - n_idx)
+    assert np.array_equal(y, expect.T)
+
+    K4 = 96
+    k4 = np.arange(K4)[None, :]
+    c = ((k4 + 5 * n_idx) % 16).astype(np.uint8)
+    codes = synth.pack_nibbles(c)
+    s4 = synth.to_fp16_bits(2.0 ** (np.arange(K4 // 32)[None, :] - n_idx))
+    mn4 = synth.to_fp16_bits(-(np.arange(K4 // 32)[None, :] + n_idx + 1) / 4.0)
+    x4 = np.zeros((K4, K4), np.uint16)
+    x4[np.arange(K4), np.arange(K4)] = 0x3F80
+    y4, _ = oracle.q4g32(codes, s4, mn4, x4)
+    expect4 = c * 2.0 ** (k4 // 32 - n_idx) - (k4 // 32 + n_idx + 1) / 4.0
+    assert np.array_equal(y4, expect4.T)
+
+
+@pytest.mark.parametrize("N,K", [(3072, 1024), (1024, 3072), (2048, 2560)])
+def test_unit_scale_q8_equals_integer_matmul_exactly(N, K):
+    # scale == 1 and integer x in [-4, 4]: every partial sum is an exact
+    # integer, so the oracle must equal numpy's float64 matmul bit for bit.
+    rng = synth.rng_for(99, 11, N, K)
+    q = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+    s = np.full((N, K // 64), 0x3C00, np.uint16)
+    xi = rng.integers(-4, 5, size=(1, K)).astype(np.float32)
+    x = synth.to_bf16_bits(xi)
+    y, _ = oracle.q8g64(q, s, x, threads=8)
+    assert np.array_equal(y, xi.astype(np.float64) @ q.astype(np.float64).T)
+
+
+@pytest.mark.parametrize("N,K", [(2560, 9216), (1536, 4096)])
+def test_unit_scale_q4_equals_integer_matmul_exactly(N, K):
+    rng = synth.rng_for(99, 12, N, K)
+    codes, _, _ = synth.q4g32_weights(rng, N, K)
+    s = np.full((N, K // 32), 0x3C00, np.uint16)        # 1.0
+    mn = np.full((N, K // 32), 0xC800, np.uint16)       # -8.0
+    xi = rng.integers(-4, 5, size=(2, K)).astype(np.float32)
+    y, _ = oracle.q4g32(codes, s, mn, synth.to_bf16_bits(xi), threads=8)
+    c = np.empty((N, K), np.float64)
+    c[:, 0::2] = codes & 0x0F
+    c[:, 1::2] = codes >> 4
+    assert np.array_equal(y, xi.astype(np.float64) @ (c - 8.0).T)
+
+
+def test_grouped_slot_equals_single_call():
+    rng = synth.rng_for(99, 13)
+    experts = [synth.q4g32_weights(rng, 40, 128) for _ in range(6)]
+    ids = np.array([4, 0, 5], np.int32)
+    xs = synth.activations(rng, 3, 128)
+    y, a = oracle.grouped_q4g32(experts, ids, xs)
+    for j, e in enumerate(ids):
+        yj, aj = oracle.q4g32(*experts[e], xs[j:j + 1])
+        assert np.array_equal(y[j], yj[0]) and np.array_equal(a[j], aj[0])
+
+
+def test_within_tolerance_rule():
+    y_ref = np.array([1.0, -2.0, 0.0])
+    a_ref = np.array([10.0, 10.0, 0.0])
+    assert oracle.within_tolerance([1.019, -2.0, 0.0], y_ref, a_ref).all()
+    assert not oracle.within_tolerance([1.021, -2.0, 0.0], y_ref, a_ref)[0]
+    assert not oracle.within_tolerance([1.0, -2.0, 1e-30], y_ref, a_ref)[2]
+    assert not oracle.within_tolerance([np.nan, -2.0, 0.0], y_ref, a_ref)[0]
