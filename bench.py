@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Decode GEMV benchmark: effective weight GB/s and fraction of HBM peak.
+
+One step = one decode GEMV over the workload's weights (for the routed-expert
+workload: the gate, up and down grouped calls of one token).  Inputs are
+seeded synthetic data already resident in HBM when the timed region starts;
+the weights rotate over enough copies that the 256 MB last-level cache
+cannot serve them, and every routed-expert step draws fresh expert ids.
+
+Prints ONE JSON line.  Effective GB/s = algorithmic bytes (packed codes +
+scales/mins + x + y) / time.  The CPU baseline is the fp64 oracle timed on
+the host cores on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+LLC_BYTES = 256 << 20          # MI355X last-level (Infinity) cache
+METRIC = "effective weight GB/s and % of HBM peak, m=1 quantized GEMV (µs/call)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(torch, a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to("cuda")
+
+
+def time_steps(torch, step, warmup, steps):
+    """W untimed steps, then exactly K timed steps bracketed by synchronize
+    and HIP events on torch's current stream (the stream the kernels use)."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        step(warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e-3       # seconds
+
+
+# ------------------------------------------------------------------ lm_head
+
+def setup_lm_head(torch, Q, synth):
+    _, _, N, K = synth.LM_HEAD
+    rng = synth.rng_for(synth.WORKLOAD_IDS["lm_head"], 0)
+    q, s = synth.q8g64_weights(rng, N, K)
+    x = synth.activations(rng, 1, K)
+    packed = Q.qpack_q8g64(q, s)
+    copies = max(2, -(-2 * LLC_BYTES // packed.nbytes))
+    w = [dev(torch, packed) for _ in range(copies)]
+    del packed
+    xd = dev(torch, x)
+    y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    weight_bytes = synth.bytes_q8g64(N, K)
+    alg_bytes = weight_bytes + 2 * K + 4 * N
+
+    def step(i):
+        Q.qgemv_q8g64(w[i % copies], xd, y, N, K)
+
+    info = {"workload": "lm_head Q8G64 GEMV m=1, N=151936 x K=2560 (Qwen3-4B vocabulary)",
+            "format": "q8g64", "m": 1, "N": N, "K": K, "weight_copies": copies,
+            "kernel": Q.variant_name(Q.FMT_Q8G64, 1, N, K)}
+    cpu = {"q": q, "s": s, "x": x}
+    return step, alg_bytes, weight_bytes, 1, info, cpu
+
+
+def cpu_lm_head(oracle, cpu, threads, reps):
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.q8g64(cpu["q"], cpu["s"], cpu["x"], threads=threads)
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), "one full lm_head call (151936 x 2560, m=1), median of %d" % reps
+
+
+# ----------------------------------------------------------- routed experts
+
+def setup_moe(torch, Q, synth, id_sets=256):
+    n_exp, n_slots = synth.MOE["n_experts"], synth.MOE["n_slots"]
+    wid = synth.WORKLOAD_IDS["moe_experts"]
+    bufs, shapes = {}, {}
+    cpu_experts = {}
+    for pj, proj in enumerate(("gate", "up", "down")):
+        N, K = synth.MOE[proj]
+        stride = Q.expert_stride(N, K)
+        buf = torch.empty(n_exp * stride, dtype=torch.uint8, device="cuda")
+        for e in range(n_exp):
+            ex = synth.q4g32_weights(synth.rng_for(wid, pj, e), N, K)
+            buf[e * stride:(e + 1) * stride].copy_(torch.from_numpy(Q.qpack_q4g32(*ex)))
+            if e < 8:
+                cpu_experts.setdefault(proj, []).append(ex)
+        bufs[proj] = (buf, stride)
+        shapes[proj] = (N, K)
+    ids = np.stack([synth.expert_ids(synth.rng_for(wid, 1000, t), n_exp, n_slots)
+                    for t in range(id_sets)])
+    ids_d = dev(torch, ids)
+    rng = synth.rng_for(wid, 2000)
+    x_tok = dev(torch, synth.activations(rng, 1, synth.MOE["gate"][1]))
+    x_down = dev(torch, synth.activations(rng, n_slots, synth.MOE["down"][1]))
+    y_gu = torch.empty((n_slots, synth.MOE["gate"][0]), dtype=torch.float32, device="cuda")
+    y_dn = torch.empty((n_slots, synth.MOE["down"][0]), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        idv = ids_d[i % id_sets]
+        for proj in ("gate", "up"):
+            buf, stride = bufs[proj]
+            N, K = shapes[proj]
+            Q.qgemv_grouped_q4g32(buf, stride, n_exp, idv, x_tok, 0, y_gu, N, N, K)
+        buf, stride = bufs["down"]
+        N, K = shapes["down"]
+        Q.qgemv_grouped_q4g32(buf, stride, n_exp, idv, x_down, K, y_dn, N, N, K)
+
+    weight_bytes = sum(n_slots * synth.bytes_q4g32(*shapes[p]) for p in shapes)
+    io_bytes = (2 * 2 * 4096 + 4 * 2 * n_slots * 1536) + (2 * n_slots * 1536 + 4 * n_slots * 4096)
+    info = {"workload": "routed-expert decode, Q4G32, 128 experts, 8 per token: "
+                        "gate/up 4096->1536 and down 1536->4096 grouped calls",
+            "format": "q4g32", "m": 1, "experts": n_exp, "slots": n_slots,
+            "kernel": [Q.variant_name(Q.FMT_GROUPED_Q4G32, 1, *shapes[p]) for p in ("gate", "down")]}
+    return step, weight_bytes + io_bytes, weight_bytes, 3, info, {"experts": cpu_experts}
+
+
+def cpu_moe(oracle, cpu, threads, reps, synth):
+    # The oracle on one token's eight routed experts (gate, up, down).
+    ex = cpu["experts"]
+    rng = synth.rng_for(99, 5)
+    xg = np.repeat(synth.activations(rng, 1, 4096), 8, axis=0)
+    xd = synth.activations(rng, 8, 1536)
+    ids = np.arange(8)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.grouped_q4g32(ex["gate"], ids, xg, threads=threads)
+        oracle.grouped_q4g32(ex["up"], ids, xg, threads=threads)
+        oracle.grouped_q4g32(ex["down"], ids, xd, threads=threads)
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), "one token's 8 routed experts (gate, up, down), median of %d" % reps
+
+
+# --------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", choices=["lm_head", "moe_experts"], default="lm_head")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--no-secondary", dest="secondary", action="store_false",
+                    help="skip timing the other workload beside the headline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the decode GEMV is single-GPU work here "
+              "(--gpus %d requested). Rows of N shard across GPUs with no exchange; "
+              "run with --gpus 1." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from weight_only_block_amd import qgemv as Q
+    from weight_only_block_amd import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    Q.lib()
+
+    def measure(name):
+        t0 = time.time()
+        if name == "lm_head":
+            step, alg, wbytes, launches, info, cpu = setup_lm_head(torch, Q, synth)
+        else:
+            step, alg, wbytes, launches, info, cpu = setup_moe(torch, Q, synth)
+        log("setup %s: %.1f s" % (name, time.time() - t0))
+        secs = time_steps(torch, step, args.warmup, args.steps)
+        return dict(secs=secs, alg=alg, wbytes=wbytes, launches=launches, info=info, cpu=cpu)
+
+    head = measure(args.workload)
+    secs, steps = head["secs"], args.steps
+    per_step = secs / steps
+    per_launch = per_step / head["launches"]
+    value = head["alg"] * steps / secs / 1e9
+    achieved = head["alg"] / head["launches"] / per_launch / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(per_step * 1e3, 5),
+        "us_per_call": round(per_launch * 1e6, 3),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; int8/4-bit codes, fp16 scales and mins, N(0,1) bf16 x)",
+        "config": dict(head["info"], algorithmic_bytes_per_step=head["alg"]),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu:
+        import oracle
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        if args.workload == "lm_head":
+            t, sample = cpu_lm_head(oracle, head["cpu"], threads, args.cpu_reps)
+        else:
+            t, sample = cpu_moe(oracle, head["cpu"], threads, args.cpu_reps, synth)
+        out["cpu_baseline"] = {"value": round(head["alg"] / t / 1e9, 4), "unit": "GB/s",
+                               "cores": threads, "kind": "oracle", "sample": sample,
+                               "seconds_per_step": round(t, 4)}
+    if args.secondary:
+        other = "moe_experts" if args.workload == "lm_head" else "lm_head"
+        del head
+        torch.cuda.empty_cache()
+        sec = measure(other)
+        ps = sec["secs"] / steps
+        out["secondary"] = {"workload": sec["info"]["workload"],
+                            "us_per_call": round(ps / sec["launches"] * 1e6, 3),
+                            "effective_GBs": round(sec["alg"] / ps / 1e9, 2),
+                            "pct_hbm_peak": round(100 * sec["alg"] / ps / 1e9 / HBM_PEAK_GBS, 2)}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,150 @@
+/*
+ * qgemv — block-quantized decode GEMV for AMD Instinct MI355X (gfx950).
+ *
+ * Single-token (and up to 4-token) autoregressive decode turns each
+ * projection into a matrix-vector product over weights that stay in their
+ * quantized form in HBM and are widened only in registers, next to the
+ * multiply.  Sources for the operation:
+ *   - "Decode 只有一行" (decode has only one row) and the "W8 直读"
+ *     (W8 direct read) section of the zLLM GLM-5.3 ROCm decode post on
+ *     juejin: decode is a GEMV bound by weight bandwidth, and the kernel
+ *     should consume W8 codes plus scales directly rather than a widened
+ *     copy; the post's bottleneck table names contiguous wide reads of the
+ *     weight stream as the lever.
+ *   - "Qwen3-14B TP4 W8A16 Decode" in the Qwen3 C++ Reference Runtime
+ *     (MetaInfer-cpp) README: signed int8 weights, bf16 activations, fp32
+ *     accumulation; "Decode small-M Linear": M = 1..4 activation rows share
+ *     one pass over the weights, with a strided input row.
+ *   - The W4A16 reading in the commit log of vllm.cpp pull request #1936
+ *     ("perf(GFX1100-TG200)"): activations stay bf16 and the weights are
+ *     dequantized inside the GEMV's registers.
+ *
+ * Formats (canonical, row-major, one output row n per weight row):
+ *   Q8G64: q[N][K] int8; scale[N][K/64] fp16 bit patterns;
+ *          w[n][k] = q[n][k] * scale[n][k/64]
+ *   Q4G32: codes[N][K/2] bytes, element k in the low nibble of byte k/2 when
+ *          k is even, the high nibble when k is odd; scale[N][K/32] and
+ *          min[N][K/32] fp16 bit patterns; w[n][k] = code * scale + min
+ * The GEMV computes, for activation rows i < m,
+ *          y[i*ldy + n] = sum_k w[n][k] * x[i*ldx + k]
+ * with x in bf16 bit patterns and y in fp32.  Accumulation is fp32 in an
+ * unspecified but fixed order: a result is bit-identical from run to run.
+ *
+ * Ownership: the caller owns every buffer.  The library never allocates,
+ * frees or synchronizes.  qpack_* and qunpack_* work on host memory only;
+ * qgemv_* take device pointers, validate everything they can on the host,
+ * enqueue one kernel on the given HIP stream (NULL = the default stream) and
+ * return without waiting.  On any error nothing is enqueued.  No C++
+ * exception crosses this interface.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QG_ABI_VERSION 1
+
+typedef enum qg_status {
+    QG_OK = 0,
+    QG_ERR_INVALID_ARG = 1,  /* null pointer, bad size, stride or buffer length */
+    QG_ERR_UNSUPPORTED = 2,  /* valid request outside what is built (m > 4, ...) */
+    QG_ERR_ALIGNMENT = 3,    /* a pointer or stride breaks an alignment rule */
+    QG_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
+} qg_status;
+
+/* Human-readable name of a status code; never NULL. */
+const char *qg_status_string(int status);
+
+/* QG_ABI_VERSION of the built library. */
+int qg_abi_version(void);
+
+/* ------------------------------------------------------------------ packing
+ * qpack_* re-tile canonical weights, once per matrix, into the layout the
+ * kernels stream with 16-byte loads per lane.  Row order and the grouping
+ * along K are kept; the packed buffer is opaque and its size depends only
+ * on (N, K).  Both formats need K to be a whole number of groups (64 for
+ * Q8G64, 32 for Q4G32) and 1 <= N, K < 2^31.
+ *
+ * *_size returns the packed size in bytes (a multiple of 256), or 0 for an
+ * invalid shape.  The device copy of a packed buffer must be 256-byte
+ * aligned.  qpack_* return QG_ERR_INVALID_ARG for a null pointer, an invalid
+ * shape or out_bytes < *_size(N, K); they write exactly *_size bytes.
+ * qunpack_* invert qpack_* byte for byte (for inspection and tests). */
+size_t    qpack_q8g64_size(int64_t N, int64_t K);
+qg_status qpack_q8g64(const int8_t *q, const uint16_t *scales_f16,
+                      int64_t N, int64_t K, void *out, size_t out_bytes);
+qg_status qunpack_q8g64(const void *packed, size_t packed_bytes, int64_t N, int64_t K,
+                        int8_t *q, uint16_t *scales_f16);
+
+size_t    qpack_q4g32_size(int64_t N, int64_t K);
+qg_status qpack_q4g32(const uint8_t *codes, const uint16_t *scales_f16,
+                      const uint16_t *mins_f16, int64_t N, int64_t K,
+                      void *out, size_t out_bytes);
+qg_status qunpack_q4g32(const void *packed, size_t packed_bytes, int64_t N, int64_t K,
+                        uint8_t *codes, uint16_t *scales_f16, uint16_t *mins_f16);
+
+/* ------------------------------------------------------------------- GEMV
+ * y[i*ldy + n] = sum_k W[n][k] * x[i*ldx + k] for 0 <= i < m, 0 <= n < N.
+ *   w_packed  device, qpack_*_size(N, K) bytes from qpack_*, 256-B aligned
+ *   x_bf16    device, m rows of K bf16 values, row stride ldx elements;
+ *             4-byte aligned, ldx even when m > 1
+ *   y         device fp32, m rows of N values, row stride ldy elements;
+ *             4-byte aligned; only y[i*ldy + n] for n < N is written
+ *   m         1..4 (QG_ERR_UNSUPPORTED otherwise)
+ *   ldx >= K, ldy >= N
+ *   hip_stream  a hipStream_t, or NULL for the default stream
+ * K * m is further limited by the 160 KB of LDS a work-group may hold
+ * (activations plus per-unit activation sums); larger requests return
+ * QG_ERR_UNSUPPORTED. */
+qg_status qgemv_q8g64(const void *w_packed, const uint16_t *x_bf16, float *y,
+                      int64_t m, int64_t N, int64_t K, int64_t ldx, int64_t ldy,
+                      void *hip_stream);
+qg_status qgemv_q4g32(const void *w_packed, const uint16_t *x_bf16, float *y,
+                      int64_t m, int64_t N, int64_t K, int64_t ldx, int64_t ldy,
+                      void *hip_stream);
+
+/* Routed-expert decode (one token, several experts), Q4G32:
+ *   for each slot j < n_slots, with e = expert_ids_dev[j]:
+ *     y[j*y_slot_stride + n] = sum_k W_e[n][k] * x[j*x_slot_stride + k]
+ *   Each slot's output is written separately; nothing is combined across
+ *   slots.  The sources motivate this as the routed-expert weight streams of
+ *   the zLLM post's bottleneck table and per-operator format map.
+ *   w_experts_packed  device, n_experts packed matrices (each from
+ *                     qpack_q4g32 with this N, K), matrix e at byte offset
+ *                     e * expert_stride_bytes; 256-B aligned
+ *   expert_stride_bytes  multiple of 256, >= qpack_q4g32_size(N, K)
+ *   expert_ids_dev    device int32[n_slots]; read by the kernel, not the
+ *                     host.  A slot whose id is outside [0, n_experts) reads
+ *                     no weights and has its N outputs set to NaN.
+ *   n_slots           1..64
+ *   x_slot_stride     elements between slot activations; 0 = one shared x
+ *                     (gate and up projections); even
+ *   y_slot_stride     elements between slot outputs, >= N
+ * Same alignment and LDS rules as qgemv_q4g32 with m = 1. */
+qg_status qgemv_grouped_q4g32(const void *w_experts_packed, int64_t expert_stride_bytes,
+                              int32_t n_experts, const int32_t *expert_ids_dev,
+                              int32_t n_slots, const uint16_t *x_bf16, int64_t x_slot_stride,
+                              float *y, int64_t y_slot_stride, int64_t N, int64_t K,
+                              void *hip_stream);
+
+/* ------------------------------------------------------------- test hooks
+ * Every successful qgemv_* call bumps the counter of the kernel variant it
+ * launched.  Variant names: "<fmt>[_grouped]_m<m>_g<G>_r<R>", e.g.
+ * "q8g64_m1_g32_r2".  qg_route_count returns 0 for unknown names. */
+void     qg_route_counts_reset(void);
+uint64_t qg_route_count(const char *variant);
+/* Writes the name of the variant qgemv_* would launch for (fmt, m, N, K)
+ * into buf (fmt 0 = Q8G64, 1 = Q4G32, 2 = grouped Q4G32).  Returns QG_OK or
+ * the status the call itself would return for that shape. */
+qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char *buf, size_t buf_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

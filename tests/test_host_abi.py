@@ -1,0 +1,174 @@
+"""Host-side tests of the C-ABI library (no GPU needed).
+
+* every function declared in include/qgemv.h is exported by libqgemv.so
+* qpack/qunpack round-trip byte for byte, are deterministic, and use the
+  documented sizes (every weight byte once, plus tail-tile padding)
+* argument validation returns its status before anything is enqueued:
+  only calls that must be rejected are made here, with fake device
+  addresses that are never dereferenced
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from weight_only_block_amd import qgemv as Q
+from weight_only_block_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "qgemv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    keywords = {"if", "sizeof", "defined"}
+    return sorted({n for n in names if n not in keywords})
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert "qgemv_q8g64" in names and "qgemv_grouped_q4g32" in names
+    out = subprocess.check_output(["nm", "-D", "--defined-only", Q.LIB_PATH]).decode()
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = Q.lib()
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_version_and_status_strings():
+    assert Q.lib().qg_abi_version() == 1
+    for s in range(5):
+        assert Q.status_string(s)
+    assert Q.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("N,K", [(1, 64), (7, 192), (129, 64), (1024, 1024), (3, 2560), (33, 3072)])
+def test_q8_pack_roundtrip(N, K):
+    rng = synth.rng_for(7, N, K)
+    q = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+    s = rng.integers(0, 65536, size=(N, K // 64), dtype=np.uint16)
+    packed = Q.qpack_q8g64(q, s)
+    assert packed.nbytes == Q.qpack_q8g64_size(N, K)
+    assert packed.nbytes % 256 == 0
+    q2, s2 = Q.qunpack_q8g64(packed, N, K)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+    assert np.array_equal(packed, Q.qpack_q8g64(q, s))      # deterministic
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (7, 96), (129, 32), (5, 1536), (9, 9216), (33, 2560)])
+def test_q4_pack_roundtrip(N, K):
+    rng = synth.rng_for(8, N, K)
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    s = rng.integers(0, 65536, size=(N, K // 32), dtype=np.uint16)
+    mn = rng.integers(0, 65536, size=(N, K // 32), dtype=np.uint16)
+    packed = Q.qpack_q4g32(codes, s, mn)
+    assert packed.nbytes == Q.qpack_q4g32_size(N, K)
+    c2, s2, mn2 = Q.qunpack_q4g32(packed, N, K)
+    assert np.array_equal(codes, c2) and np.array_equal(s, s2) and np.array_equal(mn, mn2)
+
+
+def test_packed_size_is_algorithmic_bytes_plus_tail_padding():
+    # lm_head: N = 151936 is a whole number of tiles, so no padding at all.
+    N, K = 151936, 2560
+    assert Q.qpack_q8g64_size(N, K) == synth.bytes_q8g64(N, K)
+    for (N, K) in [(9216, 2560), (2560, 9216), (1536, 4096), (4096, 1536)]:
+        assert Q.qpack_q4g32_size(N, K) == synth.bytes_q4g32(N, K)
+    for (N, K) in [(2048, 1024), (1024, 2048), (3072, 1024), (1024, 3072)]:
+        assert Q.qpack_q8g64_size(N, K) == synth.bytes_q8g64(N, K)
+    # ragged N: at most one partial tile of padding, rounded to 256 bytes
+    for N in (1, 7, 129, 1000):
+        per_row = synth.bytes_q8g64(1, 1024)
+        size = Q.qpack_q8g64_size(N, 1024)
+        assert synth.bytes_q8g64(N, 1024) <= size <= per_row * (N + 128) + 256
+
+
+def test_invalid_shapes_have_no_packed_size():
+    assert Q.qpack_q8g64_size(0, 64) == 0
+    assert Q.qpack_q8g64_size(4, 32) == 0      # not a whole 64-group
+    assert Q.qpack_q8g64_size(4, 0) == 0
+    assert Q.qpack_q4g32_size(4, 48) == 0      # not a whole 32-group
+    assert Q.qpack_q4g32_size(-1, 32) == 0
+    assert Q.qpack_q4g32_size(1 << 31, 32) == 0
+
+
+def test_qpack_rejects_short_output_and_nulls():
+    L = Q.lib()
+    q = np.zeros((4, 64), np.int8)
+    s = np.zeros((4, 1), np.uint16)
+    out = np.zeros(Q.qpack_q8g64_size(4, 64), np.uint8)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    assert L.qpack_q8g64(p(q), p(s), 4, 64, p(out), out.nbytes - 1) == Q.QG_ERR_INVALID_ARG
+    assert L.qpack_q8g64(None, p(s), 4, 64, p(out), out.nbytes) == Q.QG_ERR_INVALID_ARG
+    assert L.qpack_q8g64(p(q), p(s), 4, 64, p(out), out.nbytes) == Q.QG_OK
+
+
+# Fake device addresses: the library must reject each call below before it
+# dereferences or launches anything.
+W, X, Y, IDS = 1 << 20, 1 << 21, 1 << 22, 1 << 23
+
+
+@pytest.mark.parametrize("fn", ["qgemv_q8g64", "qgemv_q4g32"])
+def test_dense_validation(fn):
+    f = getattr(Q.lib(), fn)
+    K = 128
+    assert f(None, X, Y, 1, 16, K, K, 16, None) == Q.QG_ERR_INVALID_ARG
+    assert f(W, None, Y, 1, 16, K, K, 16, None) == Q.QG_ERR_INVALID_ARG
+    assert f(W, X, None, 1, 16, K, K, 16, None) == Q.QG_ERR_INVALID_ARG
+    assert f(W, X, Y, 5, 16, K, K, 16, None) == Q.QG_ERR_UNSUPPORTED          # m gate
+    assert f(W, X, Y, -1, 16, K, K, 16, None) == Q.QG_ERR_UNSUPPORTED
+    assert f(W, X, Y, 1, 0, K, K, 16, None) == Q.QG_ERR_INVALID_ARG           # N < 1
+    assert f(W, X, Y, 1, 16, 0, K, 16, None) == Q.QG_ERR_INVALID_ARG
+    assert f(W, X, Y, 1, 16, K + 16, K + 16, 16, None) == Q.QG_ERR_INVALID_ARG  # ragged group
+    assert f(W, X, Y, 2, 16, K, K - 2, 16, None) == Q.QG_ERR_INVALID_ARG      # ldx < K
+    assert f(W, X, Y, 2, 16, K, K, 15, None) == Q.QG_ERR_INVALID_ARG          # ldy < N
+    assert f(W + 16, X, Y, 1, 16, K, K, 16, None) == Q.QG_ERR_ALIGNMENT
+    assert f(W, X + 2, Y, 1, 16, K, K, 16, None) == Q.QG_ERR_ALIGNMENT
+    assert f(W, X, Y + 2, 1, 16, K, K, 16, None) == Q.QG_ERR_ALIGNMENT
+    assert f(W, X, Y, 2, 16, K, K + 1, 16, None) == Q.QG_ERR_ALIGNMENT        # odd ldx
+    assert f(W, X, Y, 4, 16, 32768, 32768, 16, None) == Q.QG_ERR_UNSUPPORTED  # LDS limit
+    assert f(W, X, Y, 0, 16, K, K, 16, None) == Q.QG_OK                       # empty batch
+
+
+def test_grouped_validation():
+    f = Q.lib().qgemv_grouped_q4g32
+    N, K = 64, 128
+    stride = Q.qpack_q4g32_size(N, K)
+    ok = dict(w=W, st=stride, ne=4, ids=IDS, ns=2, x=X, xs=0, y=Y, ys=N, N=N, K=K)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["w"], a["st"], a["ne"], a["ids"], a["ns"], a["x"], a["xs"], a["y"], a["ys"],
+                 a["N"], a["K"], None)
+
+    assert call(ids=None) == Q.QG_ERR_INVALID_ARG
+    assert call(ns=65) == Q.QG_ERR_UNSUPPORTED
+    assert call(ns=0) == Q.QG_OK
+    assert call(ne=0) == Q.QG_ERR_INVALID_ARG
+    assert call(st=stride - 256) == Q.QG_ERR_INVALID_ARG
+    assert call(st=stride + 16) == Q.QG_ERR_ALIGNMENT
+    assert call(ys=N - 1) == Q.QG_ERR_INVALID_ARG
+    assert call(xs=-2) == Q.QG_ERR_INVALID_ARG
+    assert call(xs=3) == Q.QG_ERR_ALIGNMENT
+    assert call(K=48) == Q.QG_ERR_INVALID_ARG
+    assert call(w=W + 128) == Q.QG_ERR_ALIGNMENT
+    assert call(ids=IDS + 2) == Q.QG_ERR_ALIGNMENT
+
+
+def test_variant_names_follow_layout():
+    assert Q.variant_name(0, 1, 151936, 2560) == "q8g64_m1_g32_r2"
+    assert Q.variant_name(0, 1, 1024, 1024) == "q8g64_m1_g32_r2"
+    assert Q.variant_name(1, 4, 9216, 2560) == "q4g32_m4_g16_r2"
+    assert Q.variant_name(1, 1, 2560, 9216) == "q4g32_m1_g32_r2"
+    assert Q.variant_name(2, 1, 1536, 4096) == "q4g32_grouped_m1_g64_r2"
+    assert Q.variant_name(2, 1, 4096, 1536) == "q4g32_grouped_m1_g16_r2"
+    assert Q.variant_name(1, 1, 8, 96) == "q4g32_m1_g1_r2"     # 3 units: G = 1
+    with pytest.raises(Q.QGError):
+        Q.variant_name(0, 5, 16, 64)
+    assert Q.route_count("no_such_variant") == 0

@@ -1,0 +1,188 @@
+// C ABI of the decode GEMV library: argument validation on the host, the
+// variant choice, and one kernel launch on the caller's stream.  Nothing
+// here allocates or synchronizes.  Returning a status for every rejected
+// request instead of falling back to another path follows the Qwen3 C++
+// Reference Runtime README (its HIP backend reports Unsupported rather than
+// silently running elsewhere); gating the number of activation rows on the
+// GEMV itself follows the m-gate fix in the commit log of vllm.cpp pull
+// request #1936, where a GEMV that only wrote row 0 was reached with m > 1.
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/qgemv.h"
+#include "launch.h"
+
+namespace {
+
+// Route counters: one per (kind, m, log2 G).  kind 0 Q8G64, 1 Q4G32,
+// 2 grouped Q4G32.
+constexpr int kKinds = 3, kMs = 4, kGs = 7;
+std::atomic<uint64_t> g_route[kKinds][kMs][kGs];
+
+int log2i(int v)
+{
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return l;
+}
+
+const char* kind_name(int kind)
+{
+    return kind == 0 ? "q8g64" : kind == 1 ? "q4g32" : "q4g32_grouped";
+}
+
+void format_variant(int kind, int m, int G, char* buf, size_t len)
+{
+    snprintf(buf, len, "%s_m%d_g%d_r%d", kind_name(kind), m, G, qg::kRowSlots);
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape checks shared by the call and by qg_variant_name.
+qg_status check_shape(int fmt, int64_t m, int64_t N, int64_t K, qg::Layout* L)
+{
+    if (m < 1 || m > 4) return QG_ERR_UNSUPPORTED;
+    if (!qg::make_layout(fmt, N, K, L)) return QG_ERR_INVALID_ARG;
+    if (qg::lds_bytes_for(*L, int(m)) > qg::kMaxLdsBytes) return QG_ERR_UNSUPPORTED;
+    return QG_OK;
+}
+
+qg_status run_dense(int fmt, const void* w_packed, const uint16_t* x, float* y, int64_t m,
+                    int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* stream)
+{
+    if (!w_packed || !x || !y) return QG_ERR_INVALID_ARG;
+    if (m == 0) return QG_OK;  // an empty batch: nothing to compute
+    qg::Layout L;
+    const qg_status st = check_shape(fmt, m, N, K, &L);
+    if (st != QG_OK) return st;
+    if (ldx < K || ldy < N) return QG_ERR_INVALID_ARG;
+    if (!aligned(w_packed, 256) || !aligned(x, 4) || !aligned(y, 4)) return QG_ERR_ALIGNMENT;
+    if (m > 1 && (ldx % 2) != 0) return QG_ERR_ALIGNMENT;
+    qg::LaunchArgs a;
+    a.layout = L;
+    a.grouped = false;
+    a.m = int(m);
+    a.w = w_packed;
+    a.expert_stride = 0;
+    a.ids = nullptr;
+    a.n_experts = 1;
+    a.n_slots = 1;
+    a.x = x;
+    a.ldx = ldx;
+    a.x_slot_stride = 0;
+    a.y = y;
+    a.ldy = ldy;
+    a.y_slot_stride = 0;
+    a.stream = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();  // clear a stale error so the check below is ours
+    if (qg::launch(a) != hipSuccess) return QG_ERR_HIP;
+    g_route[fmt][m - 1][log2i(L.G)].fetch_add(1, std::memory_order_relaxed);
+    return QG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qg_status_string(int status)
+{
+    switch (status) {
+    case QG_OK: return "ok";
+    case QG_ERR_INVALID_ARG: return "invalid argument";
+    case QG_ERR_UNSUPPORTED: return "unsupported";
+    case QG_ERR_ALIGNMENT: return "misaligned pointer or stride";
+    case QG_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int qg_abi_version(void) { return QG_ABI_VERSION; }
+
+qg_status qgemv_q8g64(const void* w_packed, const uint16_t* x_bf16, float* y, int64_t m,
+                      int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* hip_stream)
+{
+    return run_dense(qg::FMT_Q8G64, w_packed, x_bf16, y, m, N, K, ldx, ldy, hip_stream);
+}
+
+qg_status qgemv_q4g32(const void* w_packed, const uint16_t* x_bf16, float* y, int64_t m,
+                      int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* hip_stream)
+{
+    return run_dense(qg::FMT_Q4G32, w_packed, x_bf16, y, m, N, K, ldx, ldy, hip_stream);
+}
+
+qg_status qgemv_grouped_q4g32(const void* w_experts_packed, int64_t expert_stride_bytes,
+                              int32_t n_experts, const int32_t* expert_ids_dev, int32_t n_slots,
+                              const uint16_t* x_bf16, int64_t x_slot_stride, float* y,
+                              int64_t y_slot_stride, int64_t N, int64_t K, void* hip_stream)
+{
+    if (!w_experts_packed || !expert_ids_dev || !x_bf16 || !y) return QG_ERR_INVALID_ARG;
+    if (n_slots == 0) return QG_OK;  // no routed experts: nothing to compute
+    if (n_slots < 0 || n_slots > 64) return QG_ERR_UNSUPPORTED;
+    if (n_experts < 1) return QG_ERR_INVALID_ARG;
+    qg::Layout L;
+    const qg_status st = check_shape(qg::FMT_Q4G32, 1, N, K, &L);
+    if (st != QG_OK) return st;
+    if (expert_stride_bytes < L.total_bytes || x_slot_stride < 0 || y_slot_stride < N)
+        return QG_ERR_INVALID_ARG;
+    if (expert_stride_bytes % 256 != 0 || x_slot_stride % 2 != 0) return QG_ERR_ALIGNMENT;
+    if (!aligned(w_experts_packed, 256) || !aligned(x_bf16, 4) || !aligned(y, 4) ||
+        !aligned(expert_ids_dev, 4))
+        return QG_ERR_ALIGNMENT;
+    qg::LaunchArgs a;
+    a.layout = L;
+    a.grouped = true;
+    a.m = 1;
+    a.w = w_experts_packed;
+    a.expert_stride = expert_stride_bytes;
+    a.ids = expert_ids_dev;
+    a.n_experts = n_experts;
+    a.n_slots = n_slots;
+    a.x = x_bf16;
+    a.ldx = K;
+    a.x_slot_stride = x_slot_stride;
+    a.y = y;
+    a.ldy = N;
+    a.y_slot_stride = y_slot_stride;
+    a.stream = static_cast<hipStream_t>(hip_stream);
+    (void)hipGetLastError();
+    if (qg::launch(a) != hipSuccess) return QG_ERR_HIP;
+    g_route[2][0][log2i(L.G)].fetch_add(1, std::memory_order_relaxed);
+    return QG_OK;
+}
+
+void qg_route_counts_reset(void)
+{
+    for (int k = 0; k < kKinds; ++k)
+        for (int m = 0; m < kMs; ++m)
+            for (int g = 0; g < kGs; ++g) g_route[k][m][g].store(0);
+}
+
+uint64_t qg_route_count(const char* variant)
+{
+    if (!variant) return 0;
+    char buf[64];
+    for (int k = 0; k < kKinds; ++k)
+        for (int m = 0; m < kMs; ++m)
+            for (int g = 0; g < kGs; ++g) {
+                format_variant(k, m + 1, 1 << g, buf, sizeof buf);
+                if (strcmp(buf, variant) == 0) return g_route[k][m][g].load();
+            }
+    return 0;
+}
+
+qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char* buf, size_t buf_len)
+{
+    if (!buf || buf_len == 0) return QG_ERR_INVALID_ARG;
+    if (fmt < 0 || fmt > 2) return QG_ERR_INVALID_ARG;
+    if (fmt == 2 && m != 1) return QG_ERR_UNSUPPORTED;
+    qg::Layout L;
+    const qg_status st = check_shape(fmt == 0 ? qg::FMT_Q8G64 : qg::FMT_Q4G32, m, N, K, &L);
+    if (st != QG_OK) return st;
+    format_variant(fmt, int(m), L.G, buf, buf_len);
+    return QG_OK;
+}
+
+}  // extern "C"

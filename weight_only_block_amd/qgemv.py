@@ -1,0 +1,221 @@
+"""ctypes binding for libqgemv.so, with the names of the C ABI (include/qgemv.h).
+
+Argument marshalling only: every step of the GEMV runs in the library's HIP
+kernels.  Device buffers are torch tensors (torch supplies memory and the
+stream); host buffers for the packer are numpy arrays.  If the library has
+not been built this module raises on first use; there is no other path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqgemv.so")
+
+QG_OK = 0
+QG_ERR_INVALID_ARG = 1
+QG_ERR_UNSUPPORTED = 2
+QG_ERR_ALIGNMENT = 3
+QG_ERR_HIP = 4
+
+FMT_Q8G64 = 0
+FMT_Q4G32 = 1
+FMT_GROUPED_Q4G32 = 2
+
+_lib = None
+
+
+class QGError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        super().__init__("%s failed: %s (status %d)" % (where, status_string(status), status))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libqgemv.so is not built (run python -m weight_only_block_amd.build); "
+                               "there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, i32, sz, st = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t,
+                               ctypes.c_int)
+        sig = {
+            "qg_status_string": ([ctypes.c_int], ctypes.c_char_p),
+            "qg_abi_version": ([], ctypes.c_int),
+            "qpack_q8g64_size": ([i64, i64], sz),
+            "qpack_q8g64": ([p, p, i64, i64, p, sz], st),
+            "qunpack_q8g64": ([p, sz, i64, i64, p, p], st),
+            "qpack_q4g32_size": ([i64, i64], sz),
+            "qpack_q4g32": ([p, p, p, i64, i64, p, sz], st),
+            "qunpack_q4g32": ([p, sz, i64, i64, p, p, p], st),
+            "qgemv_q8g64": ([p, p, p, i64, i64, i64, i64, i64, p], st),
+            "qgemv_q4g32": ([p, p, p, i64, i64, i64, i64, i64, p], st),
+            "qgemv_grouped_q4g32": ([p, i64, i32, p, i32, p, i64, p, i64, i64, i64, p], st),
+            "qg_route_counts_reset": ([], None),
+            "qg_route_count": ([ctypes.c_char_p], ctypes.c_uint64),
+            "qg_variant_name": ([ctypes.c_int, i64, i64, i64, ctypes.c_char_p, sz], st),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().qg_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != QG_OK:
+        raise QGError(status, where)
+
+
+def _np_ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _stream_handle(stream):
+    """A torch stream, a raw hipStream_t integer, or None for torch's current stream."""
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------------ packing
+
+def qpack_q8g64_size(N: int, K: int) -> int:
+    return int(lib().qpack_q8g64_size(N, K))
+
+
+def qpack_q4g32_size(N: int, K: int) -> int:
+    return int(lib().qpack_q4g32_size(N, K))
+
+
+def qpack_q8g64(q: np.ndarray, scales_f16: np.ndarray) -> np.ndarray:
+    """Canonical q [N][K] int8 and scales [N][K/64] fp16 bits -> packed uint8 buffer."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s = np.ascontiguousarray(scales_f16, dtype=np.uint16)
+    N, K = q.shape
+    size = qpack_q8g64_size(N, K)
+    if size == 0 or s.shape != (N, K // 64):
+        raise QGError(QG_ERR_INVALID_ARG, "qpack_q8g64")
+    out = np.empty(size, np.uint8)
+    _check(lib().qpack_q8g64(_np_ptr(q), _np_ptr(s), N, K, _np_ptr(out), size), "qpack_q8g64")
+    return out
+
+
+def qunpack_q8g64(packed: np.ndarray, N: int, K: int):
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    q = np.empty((N, K), np.int8)
+    s = np.empty((N, K // 64), np.uint16)
+    _check(lib().qunpack_q8g64(_np_ptr(packed), packed.nbytes, N, K, _np_ptr(q), _np_ptr(s)),
+           "qunpack_q8g64")
+    return q, s
+
+
+def qpack_q4g32(codes: np.ndarray, scales_f16: np.ndarray, mins_f16: np.ndarray) -> np.ndarray:
+    """Canonical codes [N][K/2] (even k in the low nibble), scales and mins
+    [N][K/32] fp16 bits -> packed uint8 buffer."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    s = np.ascontiguousarray(scales_f16, dtype=np.uint16)
+    mn = np.ascontiguousarray(mins_f16, dtype=np.uint16)
+    N, half_k = codes.shape
+    K = 2 * half_k
+    size = qpack_q4g32_size(N, K)
+    if size == 0 or s.shape != (N, K // 32) or mn.shape != (N, K // 32):
+        raise QGError(QG_ERR_INVALID_ARG, "qpack_q4g32")
+    out = np.empty(size, np.uint8)
+    _check(lib().qpack_q4g32(_np_ptr(codes), _np_ptr(s), _np_ptr(mn), N, K, _np_ptr(out), size),
+           "qpack_q4g32")
+    return out
+
+
+def qunpack_q4g32(packed: np.ndarray, N: int, K: int):
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    codes = np.empty((N, K // 2), np.uint8)
+    s = np.empty((N, K // 32), np.uint16)
+    mn = np.empty((N, K // 32), np.uint16)
+    _check(lib().qunpack_q4g32(_np_ptr(packed), packed.nbytes, N, K, _np_ptr(codes), _np_ptr(s),
+                               _np_ptr(mn)), "qunpack_q4g32")
+    return codes, s, mn
+
+
+# --------------------------------------------------------------------- GEMV
+
+def _dense(fn_name, w_packed, x, y, N, K, m=None, ldx=None, ldy=None, stream=None, check=True):
+    if m is None:
+        m = 1 if x.dim() == 1 else x.shape[0]
+    if ldx is None:
+        ldx = x.stride(0) if x.dim() == 2 else K
+    if ldy is None:
+        ldy = y.stride(0) if y.dim() == 2 else N
+    st = getattr(lib(), fn_name)(w_packed.data_ptr(), x.data_ptr(), y.data_ptr(), m, N, K, ldx, ldy,
+                                 _stream_handle(stream))
+    if check:
+        _check(st, fn_name)
+    return st
+
+
+def qgemv_q8g64(w_packed, x, y, N: int, K: int, m=None, ldx=None, ldy=None, stream=None,
+                check=True):
+    """y[i*ldy + n] = sum_k W[n][k] x[i*ldx + k] with W packed Q8G64.
+
+    w_packed: device uint8 tensor from qpack_q8g64; x: device bf16 (or 16-bit
+    integer) tensor [m][>=K] or [K]; y: device float32 tensor [m][>=N] or [N].
+    Enqueued on ``stream`` (default: torch's current stream); returns the
+    status (raises on error when ``check``)."""
+    return _dense("qgemv_q8g64", w_packed, x, y, N, K, m, ldx, ldy, stream, check)
+
+
+def qgemv_q4g32(w_packed, x, y, N: int, K: int, m=None, ldx=None, ldy=None, stream=None,
+                check=True):
+    """As qgemv_q8g64 for Q4G32 weights packed by qpack_q4g32."""
+    return _dense("qgemv_q4g32", w_packed, x, y, N, K, m, ldx, ldy, stream, check)
+
+
+def qgemv_grouped_q4g32(w_experts, expert_stride_bytes: int, n_experts: int, expert_ids, x,
+                        x_slot_stride: int, y, y_slot_stride: int, N: int, K: int,
+                        n_slots=None, stream=None, check=True):
+    """Routed-expert decode: y[j*y_slot_stride + n] = W_{ids[j]}[n] . x[j*x_slot_stride:].
+
+    w_experts: device uint8 tensor holding n_experts packed matrices at
+    expert_stride_bytes; expert_ids: device int32 tensor [n_slots]."""
+    if n_slots is None:
+        n_slots = expert_ids.numel()
+    st = lib().qgemv_grouped_q4g32(w_experts.data_ptr(), expert_stride_bytes, n_experts,
+                                   expert_ids.data_ptr(), n_slots, x.data_ptr(), x_slot_stride,
+                                   y.data_ptr(), y_slot_stride, N, K, _stream_handle(stream))
+    if check:
+        _check(st, "qgemv_grouped_q4g32")
+    return st
+
+
+# --------------------------------------------------------------- test hooks
+
+def route_counts_reset() -> None:
+    lib().qg_route_counts_reset()
+
+
+def route_count(variant: str) -> int:
+    return int(lib().qg_route_count(variant.encode()))
+
+
+def variant_name(fmt: int, m: int, N: int, K: int) -> str:
+    buf = ctypes.create_string_buffer(64)
+    _check(lib().qg_variant_name(fmt, m, N, K, buf, 64), "qg_variant_name")
+    return buf.value.decode()
+
+
+def expert_stride(N: int, K: int) -> int:
+    """Smallest valid expert stride (packed size is already a multiple of 256)."""
+    return qpack_q4g32_size(N, K)
