@@ -30,6 +30,21 @@ LLC_BYTES = 256 << 20          # MI355X last-level (Infinity) cache
 METRIC = "effective weight GB/s and % of HBM peak, m=1 quantized GEMV (µs/call)"
 
 
+# HBM bytes per launch of the dominant kernel, from rocprofv3 --pmc FETCH_SIZE
+# and WRITE_SIZE runs scaled by the same counters on a plain copy kernel of
+# known size.  Valid only for the kernel sources they were taken on.
+TRAFFIC = {}
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "layout.h", "launch.h"):
+        with open(os.path.join(ROOT, "weight_only_block_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -90,6 +105,51 @@ def cpu_lm_head(oracle, cpu, threads, reps):
         oracle.q8g64(cpu["q"], cpu["s"], cpu["x"], threads=threads)
         times.append(time.perf_counter() - t0)
     return float(np.median(times)), "one full lm_head call (151936 x 2560, m=1), median of %d" % reps
+
+
+# ------------------------------------------------------ small dense configs
+
+def setup_dense(torch, Q, synth, name, m=1):
+    """q8_small (1 GEMV), qwen3_0.6b (7 GEMVs) or q4_k2560 (3 GEMVs) per step."""
+    wid = synth.WORKLOAD_IDS[name]
+    if name == "q8_small":
+        mats = [("w", "q8g64", 1024, 1024)]
+        desc = "Q8G64 GEMV m=1, N=K=1024"
+    elif name == "qwen3_0.6b":
+        mats = synth.QWEN3_06B_LAYER
+        desc = "Qwen3-0.6B-shaped decode layer, Q8G64 m=1: q, k, v, o, gate, up, down"
+    else:
+        mats = synth.Q4_K2560
+        desc = "Q4G32 K=2560 family m=%d: gate/up 2560->9216, down 9216->2560" % m
+    layer, wbytes, io = [], 0, 0
+    for j, (label, fmt, N, K) in enumerate(mats):
+        rng = synth.rng_for(wid, j)
+        if fmt == "q8g64":
+            packed = Q.qpack_q8g64(*synth.q8g64_weights(rng, N, K))
+            wbytes += synth.bytes_q8g64(N, K)
+        else:
+            packed = Q.qpack_q4g32(*synth.q4g32_weights(rng, N, K))
+            wbytes += synth.bytes_q4g32(N, K)
+        x = dev(torch, synth.activations(rng, m, K))
+        y = torch.empty((m, N), dtype=torch.float32, device="cuda")
+        io += m * (2 * K + 4 * N)
+        layer.append((fmt, N, K, packed, x, y))
+    set_bytes = sum(l[3].nbytes for l in layer)
+    copies = max(1, -(-2 * LLC_BYTES // set_bytes))
+    dev_sets = [[dev(torch, l[3]) for l in layer] for _ in range(copies)]
+
+    def step(i):
+        ws = dev_sets[i % copies]
+        for (fmt, N, K, _, x, y), w in zip(layer, ws):
+            if fmt == "q8g64":
+                Q.qgemv_q8g64(w, x, y, N, K, m=m)
+            else:
+                Q.qgemv_q4g32(w, x, y, N, K, m=m)
+
+    info = {"workload": desc, "format": mats[0][1], "m": m, "weight_copies": copies,
+            "kernel": sorted({Q.variant_name(0 if f == "q8g64" else 1, m, N, K)
+                              for (_, f, N, K) in mats})}
+    return step, wbytes + io, wbytes, len(mats), info, None
 
 
 # ----------------------------------------------------------- routed experts
@@ -162,7 +222,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", choices=["lm_head", "moe_experts"], default="lm_head")
+    ap.add_argument("--workload", default="lm_head",
+                    choices=["lm_head", "moe_experts", "q8_small", "qwen3_0.6b", "q4_k2560"])
+    ap.add_argument("--m", type=int, default=1, help="activation rows (q4_k2560 only)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this size (for HBM counter "
+                         "calibration under rocprofv3 --pmc)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-secondary", dest="secondary", action="store_false",
@@ -187,8 +252,10 @@ def main():
         t0 = time.time()
         if name == "lm_head":
             step, alg, wbytes, launches, info, cpu = setup_lm_head(torch, Q, synth)
-        else:
+        elif name == "moe_experts":
             step, alg, wbytes, launches, info, cpu = setup_moe(torch, Q, synth)
+        else:
+            step, alg, wbytes, launches, info, cpu = setup_dense(torch, Q, synth, name, args.m)
         log("setup %s: %.1f s" % (name, time.time() - t0))
         secs = time_steps(torch, step, args.warmup, args.steps)
         return dict(secs=secs, alg=alg, wbytes=wbytes, launches=launches, info=info, cpu=cpu)
@@ -218,7 +285,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
     }
-    if not args.no_cpu:
+    digest = kernel_source_digest()
+    if TRAFFIC.get(args.workload, {}).get("source_digest") == digest:
+        out["roofline"]["traffic"] = TRAFFIC[args.workload]["bytes_per_launch"]
+    out["config"]["kernel_source_digest"] = digest
+    if not args.no_cpu and head["cpu"] is not None:
         import oracle
         threads = max(1, min(16, len(os.sched_getaffinity(0))))
         if args.workload == "lm_head":
@@ -228,7 +299,16 @@ def main():
         out["cpu_baseline"] = {"value": round(head["alg"] / t / 1e9, 4), "unit": "GB/s",
                                "cores": threads, "kind": "oracle", "sample": sample,
                                "seconds_per_step": round(t, 4)}
-    if args.secondary:
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n
+        del src, dst
+    if args.secondary and args.workload in ("lm_head", "moe_experts"):
         other = "moe_experts" if args.workload == "lm_head" else "lm_head"
         del head
         torch.cuda.empty_cache()

@@ -28,6 +28,7 @@
 // MFMA is not used: at m <= 4 there is no matrix to feed it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "launch.h"
 
@@ -39,6 +40,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;                  // waves per work-group
+constexpr int kDepth = 4;                  // work items in flight per wave
+constexpr int64_t kTargetWaves = 256 * 16;  // ~16 waves per CU over 256 CUs
 constexpr int kThreads = 64 * kWaves;
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // (1.0, 1.0)
 constexpr uint32_t kMagicBf16x2 = 0x43004300u;  // (128.0, 128.0)
@@ -119,83 +122,352 @@ __device__ __forceinline__ void q4_pairs(const u32x4& c, uint32_t (&pr)[16])
     }
 }
 
-template <int FMT, int M, int G, int R, bool GROUPED>
-__global__ __launch_bounds__(kThreads) void qgemv_tile(const KernelParams p)
+// x rows -> LDS as bf16 pairs, with X[i][u] = sum of x over unit u formed by
+// the same v_dot2 chain (in the same order) the hot loop uses for D.  Thread
+// t handles units t, t + 256, ... of the flattened [M][U] array.  Its first
+// unit is fetched before anything else the kernel loads (XStage::fetch), so
+// that waiting for it does not also wait for the weight stream: vector
+// memory loads complete in issue order.
+template <int FMT, int M>
+struct XStage {
+    static constexpr int UD = FMT == FMT_Q8G64 ? 8 : 16;   // dwords per unit
+    uint32_t v[UD];
+    int first;                                             // flattened unit index
+
+    __device__ __forceinline__ void load_unit(const KernelParams& p, const uint16_t* x, int idx, int U)
+    {
+        // 4-byte loads: x rows only need 4-byte alignment, and x is read
+        // once per work-group (from L2 after the first work-group).
+        const int i = idx / U, u = idx - i * U;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(x + int64_t(i) * p.ldx + u * (2 * UD));
+#pragma unroll
+        for (int d = 0; d < UD; ++d) v[d] = src[d];
+    }
+
+    __device__ __forceinline__ void store_unit(uint32_t* xs, float* xsum, int idx, int KD, int U)
+    {
+        const int i = idx / U, u = idx - i * U;
+        float X = 0.0f;
+#pragma unroll
+        for (int d = 0; d < UD; ++d) X = dot2(v[d], kOnesBf16x2, X);
+        u32x4* dst = reinterpret_cast<u32x4*>(xs + i * KD + u * UD);
+#pragma unroll
+        for (int q = 0; q < UD / 4; ++q) {
+            u32x4 t;
+            t.x = v[4 * q]; t.y = v[4 * q + 1]; t.z = v[4 * q + 2]; t.w = v[4 * q + 3];
+            dst[q] = t;
+        }
+        xsum[idx] = X;
+    }
+
+    __device__ __forceinline__ void fetch(const KernelParams& p, const uint16_t* x, int U)
+    {
+        // Every lane loads (lanes past the end re-read the last unit), so the
+        // number of loads in flight is the same on every path and the wait
+        // for x can skip the weight loads issued after it.
+        first = threadIdx.x;
+        load_unit(p, x, first < M * U ? first : M * U - 1, U);
+    }
+
+    // Stores the unit fetched first.
+    __device__ __forceinline__ void finish_first(uint32_t* xs, float* xsum, int KD, int U)
+    {
+        if (first < M * U) store_unit(xs, xsum, first, KD, U);
+    }
+
+    // Loads and stores the units past the first (only when M*U > threads).
+    __device__ __forceinline__ void finish_rest(const KernelParams& p, const uint16_t* x, uint32_t* xs,
+                                                float* xsum, int KD, int U)
+    {
+        for (int idx = first + kThreads; idx < M * U; idx += kThreads) {
+            load_unit(p, x, idx, U);
+            store_unit(xs, xsum, idx, KD, U);
+        }
+    }
+};
+
+// One work item = one step of one tile: R 16-byte units per lane plus the
+// lane's meta word(s).  Items of a matrix are laid out back to back, so item
+// i's blocks start at i * R KiB and its meta at code_bytes + i * meta_step.
+template <int R, int META_BYTES>
+struct Item {
+    u32x4 c[R];
+    Meta<META_BYTES> m;
+    __device__ __forceinline__ void load(const uint8_t* code_lane, const uint8_t* meta_lane,
+                                         int64_t item, int64_t meta_step)
+    {
+        const uint8_t* cp = code_lane + item * (R * 1024);
+#pragma unroll
+        for (int r = 0; r < R; ++r) c[r] = load_stream16(cp + r * 1024);
+        m.load(meta_lane + item * meta_step);
+    }
+};
+
+template <int FMT, int M, int R, int META_BYTES>
+__device__ __forceinline__ void consume(const Item<R, META_BYTES>& it, const uint32_t* xs,
+                                        const float* xsum, int KD, int U, int u,
+                                        float (&acc)[R][M])
+{
+    constexpr int UD = FMT == FMT_Q8G64 ? 8 : 16;
+    uint32_t xd[M][UD];
+    float X[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(xs + i * KD + u * UD);
+#pragma unroll
+        for (int q = 0; q < UD / 4; ++q) {
+            const u32x4 v = src[q];
+            xd[i][4 * q] = v.x; xd[i][4 * q + 1] = v.y;
+            xd[i][4 * q + 2] = v.z; xd[i][4 * q + 3] = v.w;
+        }
+        X[i] = xsum[i * U + u];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (FMT == FMT_Q8G64) {
+            const float s = (r & 1) ? half_hi(it.m.w[r >> 1]) : half_lo(it.m.w[r >> 1]);
+            uint32_t pr[8];
+            q8_pairs(it.c[r], pr);
+#pragma unroll
+            for (int i = 0; i < M; ++i) {
+                float D = 0.0f;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) D = dot2(pr[t], xd[i][t], D);
+                const float c = fmaf(-128.0f, X[i], D);
+                acc[r][i] = fmaf(s, c, acc[r][i]);
+            }
+        } else {
+            const float s = half_lo(it.m.w[r]);
+            const float mn = half_hi(it.m.w[r]);
+            uint32_t pr[16];
+            q4_pairs(it.c[r], pr);
+#pragma unroll
+            for (int i = 0; i < M; ++i) {
+                float D = 0.0f;
+#pragma unroll
+                for (int t = 0; t < 16; ++t) D = dot2(pr[t], xd[i][t], D);
+                const float c = fmaf(-128.0f, X[i], D);
+                acc[r][i] = fmaf(s, c, acc[r][i]);
+                acc[r][i] = fmaf(mn, X[i], acc[r][i]);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ float dpp_add(float v, int ctrl_sel)
+{
+    int t;
+    const int bits = __builtin_bit_cast(int, v);
+    switch (ctrl_sel) {
+    case 0: t = __builtin_amdgcn_update_dpp(0, bits, 0xB1, 0xf, 0xf, false); break;   // lane ^ 1
+    case 1: t = __builtin_amdgcn_update_dpp(0, bits, 0x4E, 0xf, 0xf, false); break;   // lane ^ 2
+    case 2: t = __builtin_amdgcn_update_dpp(0, bits, 0x141, 0xf, 0xf, false); break;  // 7 - lane in 8
+    default: t = __builtin_amdgcn_update_dpp(0, bits, 0x140, 0xf, 0xf, false); break; // 15 - lane in 16
+    }
+    return v + __builtin_bit_cast(float, t);
+}
+
+// Sum over the 32-lane halves (BIT 5) or the 16-lane rows (BIT 4) of two
+// registers at once: lanes whose BIT is 0 get a's sum, the others b's.
+template <int BIT>
+__device__ __forceinline__ float swap_add(float a, float b)
+{
+    const int ia = __builtin_bit_cast(int, a), ib = __builtin_bit_cast(int, b);
+    // The two results are copied into plain locals before use: with this
+    // compiler, bit-casting s[1] straight out of a const result vector is
+    // lowered as s[0] (seen in the generated IR), which loses half the sum.
+    unsigned lo, hi;
+    if constexpr (BIT == 5) {
+        auto s = __builtin_amdgcn_permlane32_swap(ia, ib, false, false);
+        lo = s[0];
+        hi = s[1];
+    } else {
+        auto s = __builtin_amdgcn_permlane16_swap(ia, ib, false, false);
+        lo = s[0];
+        hi = s[1];
+    }
+    return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+}
+
+// All-lane sum over lane bit BIT of one register.
+template <int BIT>
+__device__ __forceinline__ float bit_add(float v)
+{
+    if constexpr (BIT >= 4) return swap_add<BIT>(v, v);
+    else return dpp_add(v, BIT);
+}
+
+// End of a tile: sum each of the V = R*M accumulators over the G lanes of its
+// row group (lane bits 0 .. log2 G - 1), then store.  With G >= 32 the top
+// lane bits are summed as a transpose: one swap + one add folds two
+// accumulators at once, after which lanes differ in which accumulator they
+// hold (bit 5 / bit 4 of the lane picks it).  The remaining bits are plain
+// butterflies (DPP inside a 16-lane row, swaps across rows).  Each sum is
+// then stored by the lanes whose untransposed group bits are zero.
+template <int M, int G, int R>
+__device__ __forceinline__ void finish_tile(float (&acc)[R][M], const KernelParams& p, float* y,
+                                            int64_t tile, int g, int rho, int lane)
+{
+    constexpr int RPS = 64 / G;
+    constexpr int TR = R * RPS;
+    constexpr int V = R * M;
+    constexpr int LOGG = G >= 64 ? 6 : G >= 32 ? 5 : G >= 16 ? 4 : G >= 8 ? 3 : G >= 4 ? 2 : G >= 2 ? 1 : 0;
+    constexpr bool T5 = LOGG == 6 && V % 2 == 0;                  // transpose on lane bit 5
+    constexpr int V1 = T5 ? V / 2 : V;
+    constexpr bool T4 = LOGG >= 5 && V1 % 2 == 0;                 // transpose on lane bit 4
+    constexpr int V2 = T4 ? V1 / 2 : V1;
+
+    float v0[V];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            v0[r * M + i] = acc[r][i];
+            acc[r][i] = 0.0f;
+        }
+    float v1[V1];
+    if constexpr (T5) {
+#pragma unroll
+        for (int k = 0; k < V1; ++k) v1[k] = swap_add<5>(v0[2 * k], v0[2 * k + 1]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < V1; ++k) v1[k] = LOGG == 6 ? bit_add<5>(v0[k]) : v0[k];
+    }
+    float v2[V2];
+    if constexpr (T4) {
+#pragma unroll
+        for (int k = 0; k < V2; ++k) v2[k] = swap_add<4>(v1[2 * k], v1[2 * k + 1]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < V2; ++k) v2[k] = LOGG >= 5 ? bit_add<4>(v1[k]) : v1[k];
+    }
+#pragma unroll
+    for (int k = 0; k < V2; ++k) {
+        if constexpr (LOGG >= 4) v2[k] = bit_add<3>(v2[k]);
+        if constexpr (LOGG >= 3) v2[k] = bit_add<2>(v2[k]);
+        if constexpr (LOGG >= 2) v2[k] = bit_add<1>(v2[k]);
+        if constexpr (LOGG >= 1) v2[k] = bit_add<0>(v2[k]);
+    }
+    // Which accumulator this lane holds for slot k, and whether it stores.
+    const int b5 = (lane >> 5) & 1, b4 = (lane >> 4) & 1;
+    int transposed_mask = 0;
+    if constexpr (T5) transposed_mask |= 32;
+    if constexpr (T4) transposed_mask |= 16;
+    const bool storer = (g & ~transposed_mask) == 0;
+#pragma unroll
+    for (int k = 0; k < V2; ++k) {
+        int o;
+        if constexpr (T5 && T4) o = 4 * k + 2 * b4 + b5;
+        else if constexpr (T5) o = 2 * k + b5;
+        else if constexpr (T4) o = 2 * k + b4;
+        else o = k;
+        const int r = o / M, i = o - (o / M) * M;
+        const int64_t row = tile * TR + r * RPS + rho;
+        if (storer && row < p.N) y[int64_t(i) * p.ldy + row] = v2[k];
+    }
+}
+
+// Waves sweep the matrix together: global wave gw of a slot streams tiles
+// gw, gw + W, gw + 2W, ... (W = waves per slot), so at any moment the whole
+// launch reads one contiguous window of the packed buffer.  That keeps the
+// HBM page locality of a plain linear read; giving each wave its own
+// contiguous region instead spreads the concurrent requests over the whole
+// matrix and measurably loses bandwidth.  Every wave gets the same number of
+// tiles up to one.  The work-group stages x once for its waves, and a ring of
+// DEPTH items in registers keeps up to DEPTH*R KiB of loads in flight per wave.
+template <int FMT, int M, int G, int R, int DEPTH, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void qgemv_stream(const KernelParams p)
 {
     extern __shared__ __align__(16) uint32_t lds[];
-    constexpr int UD = FMT == FMT_Q8G64 ? 8 : 16;      // x dwords per unit
-    constexpr int RPS = 64 / G;                        // rows per row slot
-    constexpr int TR = R * RPS;                        // rows per tile
     constexpr int META_BYTES = FMT == FMT_Q8G64 ? 2 * R : 4 * R;
+    constexpr int RPS = 64 / G;
+    constexpr int TR = R * RPS;
     static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "G must be a power of two <= 64");
     static_assert(FMT != FMT_Q8G64 || G >= 4, "Q8 lane groups span whole 64-code groups");
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // The wave index is the same in every lane; say so, so that all item
+    // bookkeeping below lives in scalar registers and branches uniformly.
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
     const int g = lane & (G - 1);
     const int rho = lane / G;
-    const int KD = p.K >> 1;                           // x dwords per row
-    const int U = p.K / (FMT == FMT_Q8G64 ? 16 : 32);  // units per row
-    uint32_t* xs = lds;                                // [M][KD] bf16 pairs
-    float* xsum = reinterpret_cast<float*>(lds + M * KD);  // [M][U]
+    const int KD = p.K >> 1;
+    const int U = p.K / (FMT == FMT_Q8G64 ? 16 : 32);
+    uint32_t* xs = lds;
+    float* xsum = reinterpret_cast<float*>(lds + M * KD);
 
     const int slot = GROUPED ? int(blockIdx.y) : 0;
-    const int64_t tile = int64_t(blockIdx.x) * kWaves + wave;
-    const bool active = tile < p.tiles;
+    const int64_t W = int64_t(gridDim.x) * kWaves;
+    const int64_t gw = int64_t(blockIdx.x) * kWaves + wave;
+    const int64_t my_tiles = gw < p.tiles ? (p.tiles - 1 - gw) / W + 1 : 0;
+    const int64_t n_items = my_tiles * p.J;
     float* y = p.y + int64_t(slot) * p.y_slot_stride;
+    const uint16_t* x = p.x + int64_t(slot) * p.x_slot_stride;
+
+    // Activations first (see XStage), then the expert id, then the weights.
+    XStage<FMT, M> xstage;
+    xstage.fetch(p, x, U);
+
     const uint8_t* w = p.w;
     if (GROUPED) {
         const int e = p.ids[slot];
         if (e < 0 || e >= p.n_experts) {
             // Out-of-range expert id: read no weights, report NaN outputs.
-            // The whole work-group takes this branch, so no barrier is skipped
-            // by part of it.
-            if (active) {
+            // The whole work-group takes this branch (e is per work-group),
+            // so no barrier below is skipped by part of it.
+            for (int64_t t = gw; t < p.tiles; t += W)
                 for (int idx = lane; idx < TR; idx += 64) {
-                    const int64_t row = tile * TR + idx;
+                    const int64_t row = t * TR + idx;
                     if (row < p.N) y[row] = __builtin_nanf("");
                 }
-            }
             return;
         }
         w += int64_t(e) * p.expert_stride;
     }
-    const uint16_t* x = p.x + int64_t(slot) * p.x_slot_stride;
 
-    // Per-lane stream pointers.  Step j, slot r: code at + (j*R + r) * 1024.
-    const uint8_t* code_ptr = w + tile * p.J * (R * 1024) + lane * 16;
+    const uint8_t* code_lane = w + lane * 16;
     int lane_meta;
     if (FMT == FMT_Q8G64) lane_meta = ((rho * (G / 4) + (g >> 2)) * R) * 2;
     else lane_meta = lane * R * 4;
-    const uint8_t* meta_ptr = w + p.code_bytes + tile * p.J * p.meta_step_bytes + lane_meta;
+    const uint8_t* meta_lane = w + p.code_bytes + lane_meta;
 
-    // Issue step 0's weight loads before the activation staging: they do
-    // not depend on x, so their latency overlaps the LDS fill.
-    u32x4 cur[R];
-    Meta<META_BYTES> cur_meta;
-    if (active) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) cur[r] = load_stream16(code_ptr + r * 1024);
-        cur_meta.load(meta_ptr);
-    }
+    // Load cursor: (tile, step) of the next item to fetch.
+    int64_t ld_tile = gw, ld_j = 0;
+    Item<R, META_BYTES> ring[DEPTH];
+#define QG_LOAD_NEXT(slot_)                                                                   \
+    do {                                                                                      \
+        ring[slot_].load(code_lane, meta_lane, ld_tile * p.J + ld_j, p.meta_step_bytes);     \
+        if (++ld_j == p.J) { ld_j = 0; ld_tile += W; }                                       \
+    } while (0)
 
-    // Stage x (M rows) into LDS, then the per-unit sums.
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-        const uint32_t* xr = reinterpret_cast<const uint32_t*>(x + int64_t(i) * p.ldx);
-        for (int d = threadIdx.x; d < KD; d += kThreads) xs[i * KD + d] = xr[d];
+    // Fill the ring unconditionally: a wave with fewer than DEPTH items loads
+    // item 0 of the matrix into the spare slots (never consumed), so the
+    // loads in flight are the same on every path and each wait below covers
+    // exactly the loads it needs.
+#define QG_FILL_RING()                                                                        \
+    do {                                                                                      \
+        _Pragma("unroll") for (int d = 0; d < DEPTH; ++d) {                                   \
+            if (d < n_items) {                                                                \
+                QG_LOAD_NEXT(d);                                                              \
+            } else {                                                                          \
+                ring[d].load(code_lane, meta_lane, 0, p.meta_step_bytes);                     \
+            }                                                                                 \
+        }                                                                                     \
+    } while (0)
+    if (M * U <= kThreads) {
+        // One x unit per thread at most: it was fetched first; finish staging
+        // it while the weights are in flight.
+        QG_FILL_RING();
+        xstage.finish_first(xs, xsum, KD, U);
+    } else {
+        // Long activations: stage all of x, then start the weight stream.
+        xstage.finish_first(xs, xsum, KD, U);
+        xstage.finish_rest(p, x, xs, xsum, KD, U);
+        QG_FILL_RING();
     }
+#undef QG_FILL_RING
     __syncthreads();
-    for (int idx = threadIdx.x; idx < M * U; idx += kThreads) {
-        const int i = idx / U, u = idx - i * U;
-        const uint32_t* src = xs + i * KD + u * UD;
-        float X = 0.0f;
-#pragma unroll
-        for (int d = 0; d < UD; ++d) X = dot2(src[d], kOnesBf16x2, X);
-        xsum[idx] = X;
-    }
-    __syncthreads();
-    if (!active) return;
+    if (n_items == 0) return;
 
     float acc[R][M];
 #pragma unroll
@@ -203,93 +475,57 @@ __global__ __launch_bounds__(kThreads) void qgemv_tile(const KernelParams p)
 #pragma unroll
         for (int i = 0; i < M; ++i) acc[r][i] = 0.0f;
 
-    for (int64_t j = 0; j < p.J; ++j) {
-        u32x4 nxt[R];
-        Meta<META_BYTES> nxt_meta;
-        if (j + 1 < p.J) {
-            const uint8_t* cp = code_ptr + (j + 1) * (R * 1024);
+    // Consume cursor.
+    int64_t tile = gw, j = 0;
+#define QG_CONSUME(slot_)                                                                     \
+    do {                                                                                      \
+        consume<FMT, M, R, META_BYTES>(ring[slot_], xs, xsum, KD, U, int(j) * G + g, acc);  \
+    } while (0)
+#define QG_ADVANCE()                                                                          \
+    do {                                                                                      \
+        if (++j == p.J) {                                                                     \
+            finish_tile<M, G, R>(acc, p, y, tile, g, rho, lane);                                    \
+            tile += W;                                                                        \
+            j = 0;                                                                            \
+        }                                                                                     \
+    } while (0)
+
+    int64_t n = 0;
+    // Steady state: every consumed slot is refilled unconditionally.
+    for (; n + 2 * DEPTH <= n_items; n += DEPTH) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) nxt[r] = load_stream16(cp + r * 1024);
-            nxt_meta.load(meta_ptr + (j + 1) * p.meta_step_bytes);
-        }
-        const int u = int(j) * G + g;
-        uint32_t xd[M][UD];
-        float X[M];
-#pragma unroll
-        for (int i = 0; i < M; ++i) {
-            const uint4* src = reinterpret_cast<const uint4*>(xs + i * KD + u * UD);
-#pragma unroll
-            for (int q = 0; q < UD / 4; ++q) {
-                const uint4 v = src[q];
-                xd[i][4 * q] = v.x; xd[i][4 * q + 1] = v.y;
-                xd[i][4 * q + 2] = v.z; xd[i][4 * q + 3] = v.w;
-            }
-            X[i] = xsum[i * U + u];
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if (FMT == FMT_Q8G64) {
-                const float s = (r & 1) ? half_hi(cur_meta.w[r >> 1]) : half_lo(cur_meta.w[r >> 1]);
-                uint32_t pr[8];
-                q8_pairs(cur[r], pr);
-#pragma unroll
-                for (int i = 0; i < M; ++i) {
-                    float D = 0.0f;
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) D = dot2(pr[t], xd[i][t], D);
-                    const float c = fmaf(-128.0f, X[i], D);
-                    acc[r][i] = fmaf(s, c, acc[r][i]);
-                }
-            } else {
-                const float s = half_lo(cur_meta.w[r]);
-                const float mn = half_hi(cur_meta.w[r]);
-                uint32_t pr[16];
-                q4_pairs(cur[r], pr);
-#pragma unroll
-                for (int i = 0; i < M; ++i) {
-                    float D = 0.0f;
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) D = dot2(pr[t], xd[i][t], D);
-                    const float c = fmaf(-128.0f, X[i], D);
-                    acc[r][i] = fmaf(s, c, acc[r][i]);
-                    acc[r][i] = fmaf(mn, X[i], acc[r][i]);
-                }
-            }
-        }
-        if (j + 1 < p.J) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) cur[r] = nxt[r];
-            cur_meta = nxt_meta;
+        for (int d = 0; d < DEPTH; ++d) {
+            QG_CONSUME(d);
+            QG_LOAD_NEXT(d);
+            QG_ADVANCE();
         }
     }
-
-    // Butterfly over the G lanes of each row group.
+    // Tail: fewer than 2*DEPTH items remain; the first min(DEPTH, rest) are
+    // already in the ring.
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int i = 0; i < M; ++i) {
-            float v = acc[r][i];
-#pragma unroll
-            for (int off = G >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-            acc[r][i] = v;
+    for (int d = 0; d < DEPTH; ++d) {
+        if (n + d < n_items) {
+            QG_CONSUME(d);
+            if (n + DEPTH + d < n_items) QG_LOAD_NEXT(d);
+            QG_ADVANCE();
         }
-
-    // Every lane of a group now holds all R*M sums; spread the stores.
+    }
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int i = 0; i < M; ++i) {
-            if ((r * M + i) % G == g) {
-                const int64_t row = tile * TR + r * RPS + rho;
-                if (row < p.N) y[int64_t(i) * p.ldy + row] = acc[r][i];
-            }
+    for (int d = 0; d < DEPTH; ++d) {
+        if (n + DEPTH + d < n_items) {
+            QG_CONSUME(d);
+            QG_ADVANCE();
         }
+    }
+#undef QG_LOAD_NEXT
+#undef QG_CONSUME
+#undef QG_ADVANCE
 }
 
 template <int FMT, int M, int G, bool GROUPED>
 hipError_t launch_variant(const KernelParams& kp, dim3 grid, size_t lds_bytes, hipStream_t stream)
 {
-    auto kern = qgemv_tile<FMT, M, G, kRowSlots, GROUPED>;
+    auto kern = qgemv_stream<FMT, M, G, kRowSlots, kDepth, GROUPED>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
         int(kMaxLdsBytes));
@@ -346,7 +582,23 @@ hipError_t launch(const LaunchArgs& a)
     kp.tiles = L.tiles;
     kp.code_bytes = L.code_bytes;
     kp.meta_step_bytes = L.meta_step_bytes;
-    const dim3 grid(unsigned((L.tiles + kWaves - 1) / kWaves), unsigned(a.grouped ? a.n_slots : 1));
+    const int slots = a.grouped ? a.n_slots : 1;
+    // About kTargetWaves waves in total (QG_TARGET_WAVES overrides it, for
+    // tuning sweeps), and never more waves than tiles.
+    static const int64_t target_waves = [] {
+        const char* e = getenv("QG_TARGET_WAVES");
+        const long v = e ? strtol(e, nullptr, 10) : 0;
+        return v > 0 ? int64_t(v) : kTargetWaves;
+    }();
+    // k tiles per wave, then the fewest waves that cover the tiles with k
+    // each: all waves get k tiles (a few k-1), never k for some and k/2 for
+    // others.
+    int64_t cap = target_waves / slots;
+    if (cap < 1) cap = 1;
+    const int64_t k = (L.tiles + cap - 1) / cap;
+    const int64_t waves_per_slot = (L.tiles + k - 1) / k;
+    const dim3 grid(unsigned((waves_per_slot + kWaves - 1) / kWaves), unsigned(slots));
+
     const size_t lds = lds_bytes_for(L, a.m);
     const hipStream_t s = a.stream;
     if (a.grouped) {
