@@ -33,7 +33,10 @@ METRIC = "effective weight GB/s and % of HBM peak, m=1 quantized GEMV (µs/call)
 # HBM bytes per launch of the dominant kernel, from rocprofv3 --pmc FETCH_SIZE
 # and WRITE_SIZE runs scaled by the same counters on a plain copy kernel of
 # known size.  Valid only for the kernel sources they were taken on.
-TRAFFIC = {}
+TRAFFIC = {
+    "lm_head": {"source_digest": "2adb0b2ce3d09b86", "bytes_per_launch": 401972000},
+    "moe_experts": {"source_digest": "2adb0b2ce3d09b86", "bytes_per_launch": 31932000},
+}
 
 
 def kernel_source_digest():
