@@ -39,10 +39,14 @@ namespace {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;                  // waves per work-group
-constexpr int kDepth = 4;                  // work items in flight per wave
-constexpr int64_t kTargetWaves = 256 * 16;  // ~16 waves per CU over 256 CUs
-constexpr int kThreads = 64 * kWaves;
+// Launch shapes (waves per work-group, ring depth) are template parameters;
+// launch() picks one per matrix shape.  Wave counts are per compute unit:
+// a dense sweep runs one 4-wave work-group per CU (every CU streams the same
+// bytes and the launch reads one window of about CUs*4 tiles at a time),
+// routed-expert launches two.  Both were measured best on MI355X; uneven
+// work-groups per CU (some CUs holding two) measured up to 25% slower.
+constexpr int64_t kWavesPerCuDense = 4;
+constexpr int64_t kWavesPerCuGrouped = 8;
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // (1.0, 1.0)
 constexpr uint32_t kMagicBf16x2 = 0x43004300u;  // (128.0, 128.0)
 
@@ -128,7 +132,7 @@ __device__ __forceinline__ void q4_pairs(const u32x4& c, uint32_t (&pr)[16])
 // unit is fetched before anything else the kernel loads (XStage::fetch), so
 // that waiting for it does not also wait for the weight stream: vector
 // memory loads complete in issue order.
-template <int FMT, int M>
+template <int FMT, int M, int THREADS>
 struct XStage {
     static constexpr int UD = FMT == FMT_Q8G64 ? 8 : 16;   // dwords per unit
     uint32_t v[UD];
@@ -179,7 +183,7 @@ struct XStage {
     __device__ __forceinline__ void finish_rest(const KernelParams& p, const uint16_t* x, uint32_t* xs,
                                                 float* xsum, int KD, int U)
     {
-        for (int idx = first + kThreads; idx < M * U; idx += kThreads) {
+        for (int idx = first + THREADS; idx < M * U; idx += THREADS) {
             load_unit(p, x, idx, U);
             store_unit(xs, xsum, idx, KD, U);
         }
@@ -375,9 +379,11 @@ __device__ __forceinline__ void finish_tile(float (&acc)[R][M], const KernelPara
 // matrix and measurably loses bandwidth.  Every wave gets the same number of
 // tiles up to one.  The work-group stages x once for its waves, and a ring of
 // DEPTH items in registers keeps up to DEPTH*R KiB of loads in flight per wave.
-template <int FMT, int M, int G, int R, int DEPTH, bool GROUPED>
-__global__ __launch_bounds__(kThreads) void qgemv_stream(const KernelParams p)
+template <int FMT, int M, int G, int R, int DEPTH, int WAVES, bool GROUPED>
+__global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
 {
+    constexpr int kWaves = WAVES;
+    constexpr int kThreads = 64 * WAVES;
     extern __shared__ __align__(16) uint32_t lds[];
     constexpr int META_BYTES = FMT == FMT_Q8G64 ? 2 * R : 4 * R;
     constexpr int RPS = 64 / G;
@@ -405,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void qgemv_stream(const KernelParams p)
     const uint16_t* x = p.x + int64_t(slot) * p.x_slot_stride;
 
     // Activations first (see XStage), then the expert id, then the weights.
-    XStage<FMT, M> xstage;
+    XStage<FMT, M, kThreads> xstage;
     xstage.fetch(p, x, U);
 
     const uint8_t* w = p.w;
@@ -522,33 +528,52 @@ __global__ __launch_bounds__(kThreads) void qgemv_stream(const KernelParams p)
 #undef QG_ADVANCE
 }
 
-template <int FMT, int M, int G, bool GROUPED>
-hipError_t launch_variant(const KernelParams& kp, dim3 grid, size_t lds_bytes, hipStream_t stream)
+// Launch shape: ring depth 2 when a tile has at most 3 steps (a deeper
+// ring would prefetch into the wave's next tile, far away in memory, and
+// measured slower), else 4.  Work-groups are 4 waves.
+enum Shape { SHAPE_D2_W4 = 0, SHAPE_D4_W4 = 1 };
+
+template <int FMT, int M, int G, int DEPTH, int WAVES, bool GROUPED>
+hipError_t launch_variant(const KernelParams& kp, int64_t waves, int slots, size_t lds_bytes,
+                          hipStream_t stream)
 {
-    auto kern = qgemv_stream<FMT, M, G, kRowSlots, kDepth, GROUPED>;
+    auto kern = qgemv_stream<FMT, M, G, kRowSlots, DEPTH, WAVES, GROUPED>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
         int(kMaxLdsBytes));
     (void)attr;
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds_bytes, stream, kp);
+    const dim3 grid(unsigned((waves + WAVES - 1) / WAVES), unsigned(slots));
+    hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), lds_bytes, stream, kp);
     return hipGetLastError();
 }
 
+template <int FMT, int M, int G, bool GROUPED>
+hipError_t launch_shape(int shape, const KernelParams& kp, int64_t waves, int slots, size_t lds,
+                        hipStream_t s)
+{
+    switch (shape) {
+    case SHAPE_D2_W4: return launch_variant<FMT, M, G, 2, 4, GROUPED>(kp, waves, slots, lds, s);
+    case SHAPE_D4_W4: return launch_variant<FMT, M, G, 4, 4, GROUPED>(kp, waves, slots, lds, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int FMT, int M, bool GROUPED>
-hipError_t launch_g(int G, const KernelParams& kp, dim3 grid, size_t lds, hipStream_t s)
+hipError_t launch_g(int G, int shape, const KernelParams& kp, int64_t waves, int slots, size_t lds,
+                    hipStream_t s)
 {
     switch (G) {
-    case 64: return launch_variant<FMT, M, 64, GROUPED>(kp, grid, lds, s);
-    case 32: return launch_variant<FMT, M, 32, GROUPED>(kp, grid, lds, s);
-    case 16: return launch_variant<FMT, M, 16, GROUPED>(kp, grid, lds, s);
-    case 8: return launch_variant<FMT, M, 8, GROUPED>(kp, grid, lds, s);
-    case 4: return launch_variant<FMT, M, 4, GROUPED>(kp, grid, lds, s);
+    case 64: return launch_shape<FMT, M, 64, GROUPED>(shape, kp, waves, slots, lds, s);
+    case 32: return launch_shape<FMT, M, 32, GROUPED>(shape, kp, waves, slots, lds, s);
+    case 16: return launch_shape<FMT, M, 16, GROUPED>(shape, kp, waves, slots, lds, s);
+    case 8: return launch_shape<FMT, M, 8, GROUPED>(shape, kp, waves, slots, lds, s);
+    case 4: return launch_shape<FMT, M, 4, GROUPED>(shape, kp, waves, slots, lds, s);
     default: break;
     }
     if constexpr (FMT == FMT_Q4G32) {
         switch (G) {
-        case 2: return launch_variant<FMT, M, 2, GROUPED>(kp, grid, lds, s);
-        case 1: return launch_variant<FMT, M, 1, GROUPED>(kp, grid, lds, s);
+        case 2: return launch_shape<FMT, M, 2, GROUPED>(shape, kp, waves, slots, lds, s);
+        case 1: return launch_shape<FMT, M, 1, GROUPED>(shape, kp, waves, slots, lds, s);
         default: break;
         }
     }
@@ -556,6 +581,21 @@ hipError_t launch_g(int G, const KernelParams& kp, dim3 grid, size_t lds, hipStr
 }
 
 }  // namespace
+
+// Compute units of the current device, looked up once per device.
+static int64_t compute_units()
+{
+    static int64_t cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 size_t lds_bytes_for(const Layout& L, int m)
 {
@@ -583,42 +623,53 @@ hipError_t launch(const LaunchArgs& a)
     kp.code_bytes = L.code_bytes;
     kp.meta_step_bytes = L.meta_step_bytes;
     const int slots = a.grouped ? a.n_slots : 1;
-    // About kTargetWaves waves in total (QG_TARGET_WAVES overrides it, for
-    // tuning sweeps), and never more waves than tiles.
-    static const int64_t target_waves = [] {
+    // About target_waves waves in total (QG_TARGET_WAVES overrides it, for
+    // tuning sweeps), never more waves than tiles; k tiles per wave, then the
+    // fewest waves that cover the tiles with k each, so all waves get k tiles
+    // (a few k-1), never k for some and k/2 for others.
+    static const int64_t env_waves = [] {
         const char* e = getenv("QG_TARGET_WAVES");
         const long v = e ? strtol(e, nullptr, 10) : 0;
-        return v > 0 ? int64_t(v) : kTargetWaves;
+        return v > 0 ? int64_t(v) : int64_t(0);
     }();
-    // k tiles per wave, then the fewest waves that cover the tiles with k
-    // each: all waves get k tiles (a few k-1), never k for some and k/2 for
-    // others.
+    const int64_t cus = compute_units();
+    const int64_t target_waves =
+        env_waves ? env_waves : cus * (a.grouped ? kWavesPerCuGrouped : kWavesPerCuDense);
     int64_t cap = target_waves / slots;
     if (cap < 1) cap = 1;
-    const int64_t k = (L.tiles + cap - 1) / cap;
+    // Up to twice the cap, a dense launch is latency-bound rather than
+    // stream-bound: one tile per wave gives it the most parallelism.
+    const int64_t k = (!a.grouped && L.tiles <= 2 * cap) ? 1 : (L.tiles + cap - 1) / cap;
     const int64_t waves_per_slot = (L.tiles + k - 1) / k;
-    const dim3 grid(unsigned((waves_per_slot + kWaves - 1) / kWaves), unsigned(slots));
-
+    // A ring of 2 only when the wave streams several shallow tiles; with a
+    // single tile per wave the whole tile goes in flight at once.
+    int shape = (L.J <= 3 && k >= 2) ? SHAPE_D2_W4 : SHAPE_D4_W4;
+    static const int env_shape = [] {
+        const char* e = getenv("QG_SHAPE");   // tuning sweeps only
+        return e ? int(strtol(e, nullptr, 10)) : -1;
+    }();
+    if (env_shape == SHAPE_D2_W4 || env_shape == SHAPE_D4_W4) shape = env_shape;
     const size_t lds = lds_bytes_for(L, a.m);
     const hipStream_t s = a.stream;
+    const int64_t w = waves_per_slot;
     if (a.grouped) {
         if (L.fmt != FMT_Q4G32 || a.m != 1) return hipErrorInvalidValue;
-        return launch_g<FMT_Q4G32, 1, true>(L.G, kp, grid, lds, s);
+        return launch_g<FMT_Q4G32, 1, true>(L.G, shape, kp, w, slots, lds, s);
     }
     if (L.fmt == FMT_Q8G64) {
         switch (a.m) {
-        case 1: return launch_g<FMT_Q8G64, 1, false>(L.G, kp, grid, lds, s);
-        case 2: return launch_g<FMT_Q8G64, 2, false>(L.G, kp, grid, lds, s);
-        case 3: return launch_g<FMT_Q8G64, 3, false>(L.G, kp, grid, lds, s);
-        case 4: return launch_g<FMT_Q8G64, 4, false>(L.G, kp, grid, lds, s);
+        case 1: return launch_g<FMT_Q8G64, 1, false>(L.G, shape, kp, w, slots, lds, s);
+        case 2: return launch_g<FMT_Q8G64, 2, false>(L.G, shape, kp, w, slots, lds, s);
+        case 3: return launch_g<FMT_Q8G64, 3, false>(L.G, shape, kp, w, slots, lds, s);
+        case 4: return launch_g<FMT_Q8G64, 4, false>(L.G, shape, kp, w, slots, lds, s);
         default: return hipErrorInvalidValue;
         }
     }
     switch (a.m) {
-    case 1: return launch_g<FMT_Q4G32, 1, false>(L.G, kp, grid, lds, s);
-    case 2: return launch_g<FMT_Q4G32, 2, false>(L.G, kp, grid, lds, s);
-    case 3: return launch_g<FMT_Q4G32, 3, false>(L.G, kp, grid, lds, s);
-    case 4: return launch_g<FMT_Q4G32, 4, false>(L.G, kp, grid, lds, s);
+    case 1: return launch_g<FMT_Q4G32, 1, false>(L.G, shape, kp, w, slots, lds, s);
+    case 2: return launch_g<FMT_Q4G32, 2, false>(L.G, shape, kp, w, slots, lds, s);
+    case 3: return launch_g<FMT_Q4G32, 3, false>(L.G, shape, kp, w, slots, lds, s);
+    case 4: return launch_g<FMT_Q4G32, 4, false>(L.G, shape, kp, w, slots, lds, s);
     default: return hipErrorInvalidValue;
     }
 }
