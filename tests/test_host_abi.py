@@ -172,3 +172,26 @@ def test_variant_names_follow_layout():
     with pytest.raises(Q.QGError):
         Q.variant_name(0, 5, 16, 64)
     assert Q.route_count("no_such_variant") == 0
+
+
+def test_bound_calls_keep_their_buffers_alive():
+    # A prepared call passes raw device addresses; it must own the tensors
+    # behind them, or torch may release the memory (graph capture empties
+    # torch's cache) while the call can still be replayed.
+    import gc
+    import weakref
+
+    import torch
+    w = torch.zeros(4096, dtype=torch.uint8)
+    x = torch.zeros(64, dtype=torch.int16)
+    y = torch.zeros(16, dtype=torch.float32)
+    ids = torch.zeros(2, dtype=torch.int32)
+    refs = [weakref.ref(t) for t in (w, x, y, ids)]
+    dense = Q.bound_q8g64(w, x, y, 16, 64, stream=0)
+    grouped = Q.bound_grouped_q4g32(w, 256, 1, ids, x, 0, y, 16, 16, 32, stream=0)
+    del w, x, y, ids
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    del dense, grouped
+    gc.collect()
+    assert all(r() is None for r in refs)

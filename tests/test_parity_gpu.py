@@ -327,3 +327,43 @@ def test_route_counters_name_the_launched_variant():
     run_q8(q, s, synth.activations(rng, 3, 2560))
     assert Q.route_count(Q.variant_name(0, 3, 64, 2560)) == 1
     assert Q.route_count(Q.variant_name(0, 1, 64, 2560)) == 0
+
+
+def test_graph_replays_match_eager_calls():
+    # Decode loops replay captured launches.  Capture one dense and one
+    # grouped call, replay several times with eager work (new activations)
+    # between replays, and compare every replay with the eager result.
+    rng = synth.rng_for(18, 0)
+    q, s = synth.q8g64_weights(rng, 1000, 2560)
+    w = dev(Q.qpack_q8g64(q, s))
+    experts = [synth.q4g32_weights(synth.rng_for(18, e), 256, 1536) for e in range(6)]
+    buf, stride = _upload_experts(experts, 256, 1536)
+    ids = dev(np.array([5, 2, 0], np.int32))
+    x = dev(synth.activations(rng, 1, 2560))
+    xg = dev(synth.activations(rng, 3, 1536))
+    y = canary((1, 1000))
+    yg = canary((3, 256))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dense = Q.bound_q8g64(w, x, y, 1000, 2560)
+        grouped = Q.bound_grouped_q4g32(buf, stride, 6, ids, xg, 1536, yg, 256, 256, 1536)
+        dense()
+        grouped()                                   # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        dense()
+        grouped()
+    for r in range(4):
+        x.copy_(dev(synth.activations(synth.rng_for(18, 100 + r), 1, 2560)))
+        xg.copy_(dev(synth.activations(synth.rng_for(18, 200 + r), 3, 1536)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got, got_g = host(y).copy(), host(yg).copy()
+        ye, yge = canary((1, 1000)), canary((3, 256))
+        Q.qgemv_q8g64(w, x, ye, 1000, 2560)
+        Q.qgemv_grouped_q4g32(buf, stride, 6, ids, xg, 1536, yge, 256, 256, 1536)
+        assert np.array_equal(got, host(ye)), "replay %d dense" % r
+        assert np.array_equal(got_g, host(yge)), "replay %d grouped" % r

@@ -200,6 +200,61 @@ def qgemv_grouped_q4g32(w_experts, expert_stride_bytes: int, n_experts: int, exp
     return st
 
 
+# ------------------------------------------------------- prepared launches
+
+class BoundCall:
+    """One library call with its arguments marshalled once.
+
+    It holds references to every tensor whose device address it passes, so
+    the memory cannot be released (for example by torch's empty_cache, which
+    graph capture runs) while the call can still be issued."""
+
+    __slots__ = ("fn", "args", "name", "tensors")
+
+    def __init__(self, fn, args, name, tensors):
+        self.fn = fn
+        self.args = args
+        self.name = name
+        self.tensors = tuple(tensors)
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != QG_OK:
+            raise QGError(st, self.name)
+
+
+def bound_q8g64(w_packed, x, y, N: int, K: int, m: int = 1, ldx=None, ldy=None, stream=None):
+    """Marshal the arguments of one qgemv_q8g64 call once; the returned
+    BoundCall re-issues exactly that call (for decode loops that repeat the
+    same launch, and for graph capture).  Each call checks the status."""
+    return _bind("qgemv_q8g64", w_packed, x, y, N, K, m, ldx, ldy, stream)
+
+
+def bound_q4g32(w_packed, x, y, N: int, K: int, m: int = 1, ldx=None, ldy=None, stream=None):
+    """As bound_q8g64 for qgemv_q4g32."""
+    return _bind("qgemv_q4g32", w_packed, x, y, N, K, m, ldx, ldy, stream)
+
+
+def _bind(fn_name, w_packed, x, y, N, K, m, ldx, ldy, stream):
+    ldx = K if ldx is None else ldx
+    ldy = N if ldy is None else ldy
+    args = (w_packed.data_ptr(), x.data_ptr(), y.data_ptr(), m, N, K, ldx, ldy,
+            _stream_handle(stream))
+    return BoundCall(getattr(lib(), fn_name), args, fn_name, (w_packed, x, y))
+
+
+def bound_grouped_q4g32(w_experts, expert_stride_bytes: int, n_experts: int, expert_ids, x,
+                        x_slot_stride: int, y, y_slot_stride: int, N: int, K: int,
+                        n_slots=None, stream=None):
+    """As bound_q8g64 for qgemv_grouped_q4g32."""
+    if n_slots is None:
+        n_slots = expert_ids.numel()
+    args = (w_experts.data_ptr(), expert_stride_bytes, n_experts, expert_ids.data_ptr(), n_slots,
+            x.data_ptr(), x_slot_stride, y.data_ptr(), y_slot_stride, N, K, _stream_handle(stream))
+    return BoundCall(lib().qgemv_grouped_q4g32, args, "qgemv_grouped_q4g32",
+                     (w_experts, expert_ids, x, y))
+
+
 # --------------------------------------------------------------- test hooks
 
 def route_counts_reset() -> None:
