@@ -367,3 +367,24 @@ def test_graph_replays_match_eager_calls():
         Q.qgemv_grouped_q4g32(buf, stride, 6, ids, xg, 1536, yge, 256, 256, 1536)
         assert np.array_equal(got, host(ye)), "replay %d dense" % r
         assert np.array_equal(got_g, host(yge)), "replay %d grouped" % r
+
+
+def test_merged_gate_up_equals_separate_calls_bitwise():
+    # Stacking each expert's gate and up rows into one [2N][K] matrix is a row
+    # concatenation; every output row is computed the same way, so the merged
+    # grouped call must equal the two separate calls bit for bit.
+    n_experts, N, K = 5, 384, 4096
+    gate = [synth.q4g32_weights(synth.rng_for(19, 0, e), N, K) for e in range(n_experts)]
+    up = [synth.q4g32_weights(synth.rng_for(19, 1, e), N, K) for e in range(n_experts)]
+    merged = [tuple(np.concatenate([a, b]) for a, b in zip(g, u)) for g, u in zip(gate, up)]
+    bg, sg = _upload_experts(gate, N, K)
+    bu, su = _upload_experts(up, N, K)
+    bm, sm = _upload_experts(merged, 2 * N, K)
+    ids = dev(np.array([4, 1, 3], np.int32))
+    x = dev(synth.activations(synth.rng_for(19, 9), 1, K))
+    yg, yu, ym = canary((3, N)), canary((3, N)), canary((3, 2 * N))
+    Q.qgemv_grouped_q4g32(bg, sg, n_experts, ids, x, 0, yg, N, N, K)
+    Q.qgemv_grouped_q4g32(bu, su, n_experts, ids, x, 0, yu, N, N, K)
+    Q.qgemv_grouped_q4g32(bm, sm, n_experts, ids, x, 0, ym, 2 * N, 2 * N, K)
+    ym = host(ym)
+    assert np.array_equal(ym[:, :N], host(yg)) and np.array_equal(ym[:, N:], host(yu))
