@@ -405,7 +405,18 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     const int slot = GROUPED ? int(blockIdx.y) : 0;
     const int64_t W = int64_t(gridDim.x) * kWaves;
     const int64_t gw = int64_t(blockIdx.x) * kWaves + wave;
-    const int64_t my_tiles = gw < p.tiles ? (p.tiles - 1 - gw) / W + 1 : 0;
+    // Tile mapping: grid-stride (tiles gw, gw + W, ...) or, with contig_k > 0,
+    // a contiguous run of contig_k tiles per wave.
+    int64_t t0, tstep, my_tiles;
+    if (p.contig_k > 0) {
+        t0 = gw * p.contig_k;
+        tstep = 1;
+        my_tiles = t0 < p.tiles ? (p.tiles - t0 < p.contig_k ? p.tiles - t0 : p.contig_k) : 0;
+    } else {
+        t0 = gw;
+        tstep = W;
+        my_tiles = gw < p.tiles ? (p.tiles - 1 - gw) / W + 1 : 0;
+    }
     const int64_t n_items = my_tiles * p.J;
     float* y = p.y + int64_t(slot) * p.y_slot_stride;
     const uint16_t* x = p.x + int64_t(slot) * p.x_slot_stride;
@@ -421,7 +432,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
             // Out-of-range expert id: read no weights, report NaN outputs.
             // The whole work-group takes this branch (e is per work-group),
             // so no barrier below is skipped by part of it.
-            for (int64_t t = gw; t < p.tiles; t += W)
+            for (int64_t n = 0, t = t0; n < my_tiles; ++n, t += tstep)
                 for (int idx = lane; idx < TR; idx += 64) {
                     const int64_t row = t * TR + idx;
                     if (row < p.N) y[row] = __builtin_nanf("");
@@ -438,12 +449,12 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     const uint8_t* meta_lane = w + p.code_bytes + lane_meta;
 
     // Load cursor: (tile, step) of the next item to fetch.
-    int64_t ld_tile = gw, ld_j = 0;
+    int64_t ld_tile = t0, ld_j = 0;
     Item<R, META_BYTES> ring[DEPTH];
 #define QG_LOAD_NEXT(slot_)                                                                   \
     do {                                                                                      \
         ring[slot_].load(code_lane, meta_lane, ld_tile * p.J + ld_j, p.meta_step_bytes);     \
-        if (++ld_j == p.J) { ld_j = 0; ld_tile += W; }                                       \
+        if (++ld_j == p.J) { ld_j = 0; ld_tile += tstep; }                                   \
     } while (0)
 
     // Fill the ring unconditionally: a wave with fewer than DEPTH items loads
@@ -482,7 +493,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
         for (int i = 0; i < M; ++i) acc[r][i] = 0.0f;
 
     // Consume cursor.
-    int64_t tile = gw, j = 0;
+    int64_t tile = t0, j = 0;
 #define QG_CONSUME(slot_)                                                                     \
     do {                                                                                      \
         consume<FMT, M, R, META_BYTES>(ring[slot_], xs, xsum, KD, U, int(j) * G + g, acc);  \
@@ -491,7 +502,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     do {                                                                                      \
         if (++j == p.J) {                                                                     \
             finish_tile<M, G, R>(acc, p, y, tile, g, rho, lane);                                    \
-            tile += W;                                                                        \
+            tile += tstep;                                                                    \
             j = 0;                                                                            \
         }                                                                                     \
     } while (0)
@@ -644,6 +655,16 @@ hipError_t launch(const LaunchArgs& a)
     // A ring of 2 only when the wave streams several shallow tiles; with a
     // single tile per wave the whole tile goes in flight at once.
     int shape = (L.J <= 3 && k >= 2) ? SHAPE_D2_W4 : SHAPE_D4_W4;
+    // Routed-expert launches give each wave a contiguous run of k tiles (the
+    // whole 31.5 MB call is in flight at once anyway, so a common window
+    // buys nothing, and adjacent tiles measured ~3% faster); dense sweeps
+    // keep the grid-stride window.  QG_CONTIG=0/1 overrides (tuning sweeps).
+    static const int env_contig = [] {
+        const char* e = getenv("QG_CONTIG");
+        return e ? int(strtol(e, nullptr, 10)) : -1;
+    }();
+    const bool contig = env_contig >= 0 ? env_contig != 0 : a.grouped;
+    kp.contig_k = contig ? k : 0;
     static const int env_shape = [] {
         const char* e = getenv("QG_SHAPE");   // tuning sweeps only
         return e ? int(strtol(e, nullptr, 10)) : -1;

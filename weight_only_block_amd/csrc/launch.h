@@ -30,6 +30,7 @@ struct KernelParams {
     int64_t tiles;
     int64_t code_bytes;        // offset of the meta blocks
     int64_t meta_step_bytes;
+    int64_t contig_k;          // > 0: each wave streams contig_k consecutive tiles
 };
 
 struct LaunchArgs {
