@@ -47,6 +47,12 @@ def _load():
         lib.oracle_q8g64.restype = ctypes.c_int
         lib.oracle_q4g32.argtypes = [p, p, p, i64, i64, p, i64, i64, i64, i64, p, p, i64]
         lib.oracle_q4g32.restype = ctypes.c_int
+        lib.oracle_q8g128.argtypes = [p, p, i64, i64, p, i64, i64, i64, i64, p, p, i64]
+        lib.oracle_q8g128.restype = ctypes.c_int
+        lib.oracle_q8pc.argtypes = [p, p, i64, i64, p, i64, i64, i64, i64, p, p, i64]
+        lib.oracle_q8pc.restype = ctypes.c_int
+        lib.oracle_f32_to_double.argtypes = [ctypes.c_uint32]
+        lib.oracle_f32_to_double.restype = ctypes.c_double
         lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
         lib.oracle_half_to_double.restype = ctypes.c_double
         lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -65,6 +71,10 @@ def half_to_double(bits: int) -> float:
 
 def bf16_to_double(bits: int) -> float:
     return _load().oracle_bf16_to_double(int(bits))
+
+
+def f32_to_double(bits: int) -> float:
+    return _load().oracle_f32_to_double(int(bits))
 
 
 def _row_splits(N: int, threads: int):
@@ -111,6 +121,44 @@ def q8g64(q: np.ndarray, scale: np.ndarray, x: np.ndarray, threads: int = 1):
         with ThreadPoolExecutor(len(splits)) as ex:
             list(ex.map(run, splits))
     return y, a
+
+
+def _q8_generic(fn_name, q, scale, x, threads, scale_dtype, scale_shape):
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    scale = np.ascontiguousarray(scale, dtype=scale_dtype)
+    N, K = q.shape
+    if scale.shape != scale_shape(N, K):
+        raise ValueError("bad scale shape for " + fn_name)
+    x = _check_x(x, K)
+    m, ldx = x.shape
+    y = np.zeros((m, N), np.float64)
+    a = np.zeros((m, N), np.float64)
+    fn = getattr(_load(), fn_name)
+
+    def run(rng):
+        if fn(_ptr(q), _ptr(scale), N, K, _ptr(x), m, ldx, rng[0], rng[1], _ptr(y), _ptr(a), N) != 0:
+            raise RuntimeError(fn_name + " failed")
+
+    splits = _row_splits(N, threads)
+    if len(splits) == 1:
+        run(splits[0])
+    else:
+        with ThreadPoolExecutor(len(splits)) as ex:
+            list(ex.map(run, splits))
+    return y, a
+
+
+def q8g128(q: np.ndarray, scale: np.ndarray, x: np.ndarray, threads: int = 1):
+    """Q8G128: q [N][K] int8, scale [N][K/128] fp16 bits, x [m][>=K] bf16 bits."""
+    if q.shape[1] % 128:
+        raise ValueError("K must be a multiple of 128")
+    return _q8_generic("oracle_q8g128", q, scale, x, threads, np.uint16,
+                       lambda N, K: (N, K // 128))
+
+
+def q8pc(q: np.ndarray, scale_f32: np.ndarray, x: np.ndarray, threads: int = 1):
+    """Q8 per output channel: q [N][K] int8, scale [N] fp32 bit patterns (uint32)."""
+    return _q8_generic("oracle_q8pc", q, scale_f32, x, threads, np.uint32, lambda N, K: (N,))
 
 
 def q4g32(codes: np.ndarray, scale: np.ndarray, minv: np.ndarray, x: np.ndarray,

@@ -19,6 +19,10 @@
  *     y[i][n] = sum_k w[n][k] * x[i][k]          (x is bf16)
  *     a[i][n] = sum_k |w[n][k] * x[i][k]|        (the tolerance scale)
  *
+ * Further formats (same structure, same plain loops):
+ *   Q8G128 w[n][k] = q[n][k] * scale[n][k/128]          (fp16 scale)
+ *   Q8PC   w[n][k] = q[n][k] * scale[n]                  (fp32 scale per row)
+ *
  * Sources.  The W8 reading (signed int8 weight codes, bf16 activations,
  * weights consumed in their quantized form and widened only inside the dot
  * product) follows the "Qwen3-14B TP4 W8A16 Decode" section of the Qwen3 C++
@@ -129,6 +133,79 @@ int oracle_q4g32(const uint8_t *codes, const uint16_t *scale, const uint16_t *mi
                 double s = half_bits_to_double(scale[n * groups + k / 32]);
                 double mn = half_bits_to_double(minv[n * groups + k / 32]);
                 double w = (double)c * s + mn;
+                double xv = bf16_bits_to_double(x[i * ldx + k]);
+                sum += w * xv;
+                abs_sum += fabs(w * xv);
+            }
+            y[i * ldy + n] = sum;
+            a[i * ldy + n] = abs_sum;
+        }
+    }
+    return 0;
+}
+
+/* IEEE-754 binary32 bit pattern -> exact double.
+ * 1 sign bit, 8 exponent bits (bias 127), 23 fraction bits. */
+static double f32_bits_to_double(uint32_t f)
+{
+    int sign = (f >> 31) & 1;
+    int expo = (f >> 23) & 0xff;
+    uint32_t frac = f & 0x7fffffu;
+    double v;
+    if (expo == 0) {
+        v = ldexp((double)frac, -149);                      /* zero or subnormal */
+    } else if (expo == 255) {
+        v = frac ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(0x800000u + frac), expo - 150);  /* (1.f) * 2^(e-127) */
+    }
+    return sign ? -v : v;
+}
+
+double oracle_f32_to_double(uint32_t f) { return f32_bits_to_double(f); }
+
+/* Q8G128 decode GEMV: int8 codes, one fp16 scale per 128 consecutive k of a
+ * row (the LM-head format of the per-operator format map in the zLLM
+ * GLM-5.3 ROCm decode post).  Arguments as for oracle_q8g64, with
+ * scale [N][K/128]. */
+int oracle_q8g128(const int8_t *q, const uint16_t *scale, int64_t N, int64_t K,
+                  const uint16_t *x, int64_t m, int64_t ldx,
+                  int64_t n0, int64_t n1, double *y, double *a, int64_t ldy)
+{
+    if (K % 128 != 0 || n0 < 0 || n1 > N || n0 > n1) return -1;
+    const int64_t groups = K / 128;
+    for (int64_t i = 0; i < m; ++i) {
+        for (int64_t n = n0; n < n1; ++n) {
+            double sum = 0.0, abs_sum = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double code = (double)q[n * K + k];
+                double s = half_bits_to_double(scale[n * groups + k / 128]);
+                double w = code * s;
+                double xv = bf16_bits_to_double(x[i * ldx + k]);
+                sum += w * xv;
+                abs_sum += fabs(w * xv);
+            }
+            y[i * ldy + n] = sum;
+            a[i * ldy + n] = abs_sum;
+        }
+    }
+    return 0;
+}
+
+/* Q8 per output channel (W8A16 of the "Qwen3-14B TP4 W8A16 Decode" section
+ * of the Qwen3 C++ Reference Runtime README): int8 codes, one fp32 scale per
+ * output row, bf16 activations.  scale is [N] binary32 bit patterns. */
+int oracle_q8pc(const int8_t *q, const uint32_t *scale, int64_t N, int64_t K,
+                const uint16_t *x, int64_t m, int64_t ldx,
+                int64_t n0, int64_t n1, double *y, double *a, int64_t ldy)
+{
+    if (n0 < 0 || n1 > N || n0 > n1) return -1;
+    for (int64_t i = 0; i < m; ++i) {
+        for (int64_t n = n0; n < n1; ++n) {
+            double s = f32_bits_to_double(scale[n]);
+            double sum = 0.0, abs_sum = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double w = (double)q[n * K + k] * s;
                 double xv = bf16_bits_to_double(x[i * ldx + k]);
                 sum += w * xv;
                 abs_sum += fabs(w * xv);

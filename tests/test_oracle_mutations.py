@@ -32,6 +32,11 @@ MUTATIONS = {
     "code_as_unsigned": ("double code = (double)q[n * K + k];",
                          "double code = (double)(uint8_t)q[n * K + k];"),
     "row_stride": ("y[i * ldy + n] = sum;", "y[i * ldy + (n0 + n1 - 1 - n)] = sum;"),
+    "q8g128_group_index": ("scale[n * groups + k / 128]", "scale[n * groups + (k / 64) % groups]"),
+    "q8pc_row_scale": ("double s = f32_bits_to_double(scale[n]);",
+                       "double s = f32_bits_to_double(scale[N - 1 - n]);"),
+    "f32_exponent": ("expo - 150", "expo - 149"),
+    "f32_implicit_one": ("(0x800000u + frac)", "(frac)"),
 }
 
 PIN_TESTS = [
@@ -46,6 +51,12 @@ PIN_TESTS = [
     (pins.test_brute_force_q4_every_code, False),
     (pins.test_one_hot_pins_group_and_nibble_index, False),
     (pins.test_abs_sum_bounds_and_sign_cases, False),
+    (pins.test_f32_decoder_matches_numpy, False),
+    (pins.test_q8g128_two_group_worked_example, True),
+    (pins.test_q8pc_two_row_worked_example, True),
+    (pins.test_q8g128_equals_q8g64_with_duplicated_scales, False),
+    (pins.test_q8pc_equals_q8g64_with_row_constant_scales, False),
+    (pins.test_q8g128_one_hot_group_index, False),
 ]
 
 
@@ -61,7 +72,8 @@ def test_pins_catch_planted_mistake(name, tmp_path, golden_dir):
                            str(mutated), "-lm"])
     real = oracle._load()
     lib = ctypes.CDLL(str(so))
-    for fn in ("oracle_q8g64", "oracle_q4g32", "oracle_half_to_double", "oracle_bf16_to_double"):
+    for fn in ("oracle_q8g64", "oracle_q4g32", "oracle_q8g128", "oracle_q8pc",
+               "oracle_half_to_double", "oracle_bf16_to_double", "oracle_f32_to_double"):
         getattr(lib, fn).argtypes = getattr(real, fn).argtypes
         getattr(lib, fn).restype = getattr(real, fn).restype
     caught = []

@@ -305,3 +305,88 @@ def test_within_tolerance_rule():
     assert not oracle.within_tolerance([1.021, -2.0, 0.0], y_ref, a_ref)[0]
     assert not oracle.within_tolerance([1.0, -2.0, 1e-30], y_ref, a_ref)[2]
     assert not oracle.within_tolerance([np.nan, -2.0, 0.0], y_ref, a_ref)[0]
+
+
+# ----------------------------------------------- Q8G128 and per-channel Q8
+
+def test_f32_decoder_matches_numpy():
+    rng = np.random.default_rng(5)
+    bits = np.concatenate([
+        rng.integers(0, 2**32, size=200000, dtype=np.uint64).astype(np.uint32),
+        np.array([0, 1, 0x7FFFFF, 0x800000, 0x3F800000, 0x7F7FFFFF, 0x80000001, 0xFF7FFFFF,
+                  0x7F800000, 0xFF800000], np.uint32)])
+    with np.errstate(invalid="ignore"):
+        ref = bits.view(np.float32).astype(np.float64)
+    got = np.array([oracle.f32_to_double(b) for b in bits])
+    finite = np.isfinite(ref)
+    assert np.array_equal(got[finite], ref[finite])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[np.isinf(ref)], ref[np.isinf(ref)])
+
+
+def test_q8g128_two_group_worked_example(golden_dir):
+    g = _load(golden_dir, "q8g128_two_group.json")
+    K = g["K"]
+    q = np.where(np.arange(K) < 128, 1, -2).astype(np.int8)[None, :]
+    s = np.array(g["scale_fp16_bits"], np.uint16)
+    x = np.where(np.arange(K) < 128, 0x3F80, 0x4000).astype(np.uint16)[None, :]
+    y, a = oracle.q8g128(q, s, x)
+    assert np.array_equal(y, np.array(g["y"])) and np.array_equal(a, np.array(g["a"]))
+
+
+def test_q8pc_two_row_worked_example(golden_dir):
+    g = _load(golden_dir, "q8pc_two_rows.json")
+    k = np.arange(g["K"])
+    q = np.stack([k - 32, 31 - k]).astype(np.int8)
+    s = np.array(g["scale_f32_bits"], np.uint32)
+    x = np.full((1, g["K"]), 0x3F80, np.uint16)
+    y, a = oracle.q8pc(q, s, x)
+    assert np.array_equal(y, np.array(g["y"])) and np.array_equal(a, np.array(g["a"]))
+
+
+def test_q8g128_equals_q8g64_with_duplicated_scales():
+    # A 128-wide group is two 64-wide groups with the same scale.
+    rng = synth.rng_for(99, 20)
+    N, K = 37, 640
+    q = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+    s128 = synth.to_fp16_bits(rng.uniform(1e-3, 2e-2, size=(N, K // 128)))
+    x = synth.activations(rng, 3, K)
+    y128, a128 = oracle.q8g128(q, s128, x)
+    y64, a64 = oracle.q8g64(q, np.repeat(s128, 2, axis=1), x)
+    assert np.array_equal(y128, y64) and np.array_equal(a128, a64)
+
+
+def test_q8pc_equals_q8g64_with_row_constant_scales():
+    # A per-row scale is a Q8G64 scale repeated over the row's groups (scales
+    # chosen exactly representable in fp16).
+    rng = synth.rng_for(99, 21)
+    N, K = 29, 512
+    q = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+    s16 = synth.to_fp16_bits(rng.uniform(1e-3, 2e-2, size=(N,)))
+    s32 = s16.view(np.float16).astype(np.float32).view(np.uint32)
+    x = synth.activations(rng, 2, K)
+    ypc, apc = oracle.q8pc(q, s32, x)
+    y64, a64 = oracle.q8g64(q, np.repeat(s16[:, None], K // 64, axis=1), x)
+    assert np.array_equal(ypc, y64) and np.array_equal(apc, a64)
+
+
+def test_q8pc_unit_scale_equals_integer_matmul_exactly():
+    rng = synth.rng_for(99, 22)
+    N, K = 1792, 5120                       # a TP4 QKV rank-local shape of the README
+    q = rng.integers(-127, 128, size=(N, K), dtype=np.int8)
+    s = np.full(N, 0x3F800000, np.uint32)   # 1.0
+    xi = rng.integers(-4, 5, size=(1, K)).astype(np.float32)
+    y, _ = oracle.q8pc(q, s, synth.to_bf16_bits(xi), threads=8)
+    assert np.array_equal(y, xi.astype(np.float64) @ q.astype(np.float64).T)
+
+
+def test_q8g128_one_hot_group_index():
+    N, K = 2, 384
+    n_idx = np.arange(N)[:, None]
+    k_idx = np.arange(K)[None, :]
+    q = (((5 * k_idx + 11 * n_idx) % 255) - 127).astype(np.int8)
+    s = synth.to_fp16_bits(2.0 ** (np.arange(K // 128)[None, :] - 2 * n_idx))
+    x = np.zeros((K, K), np.uint16)
+    x[np.arange(K), np.arange(K)] = 0x3F80
+    y, _ = oracle.q8g128(q, s, x)
+    assert np.array_equal(y, (q.astype(np.float64) * 2.0 ** (k_idx // 128 - 2 * n_idx)).T)
