@@ -40,10 +40,14 @@ TRAFFIC = {
 }
 
 
+KERNEL_SOURCES = ("kernel_body.h", "kern_q8g64.hip", "kern_q4g32.hip", "kern_q8g128.hip",
+                  "kern_q8pc.hip", "launch.hip", "layout.h", "launch.h")
+
+
 def kernel_source_digest():
     import hashlib
     h = hashlib.sha256()
-    for f in ("kernels.hip", "layout.h", "launch.h"):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "weight_only_block_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -104,38 +108,46 @@ def time_steps_graph(torch, step, warmup, steps, period):
 
 # ------------------------------------------------------------------ lm_head
 
-def setup_lm_head(torch, Q, synth):
+def setup_lm_head(torch, Q, synth, fmt="q8g64"):
+    """The LM-head GEMV in Q8G64 (headline) or Q8G128 (one scale per 128)."""
     _, _, N, K = synth.LM_HEAD
-    rng = synth.rng_for(synth.WORKLOAD_IDS["lm_head"], 0)
-    q, s = synth.q8g64_weights(rng, N, K)
+    name = "lm_head" if fmt == "q8g64" else "lm_head_q8g128"
+    rng = synth.rng_for(synth.WORKLOAD_IDS[name], 0)
+    if fmt == "q8g64":
+        q, s = synth.q8g64_weights(rng, N, K)
+        packed, weight_bytes = Q.qpack_q8g64(q, s), synth.bytes_q8g64(N, K)
+        bind, fmt_id = Q.bound_q8g64, Q.FMT_Q8G64
+    else:
+        q, s = synth.q8g128_weights(rng, N, K)
+        packed, weight_bytes = Q.qpack_q8g128(q, s), synth.bytes_q8g128(N, K)
+        bind, fmt_id = Q.bound_q8g128, Q.FMT_Q8G128
     x = synth.activations(rng, 1, K)
-    packed = Q.qpack_q8g64(q, s)
     copies = max(2, -(-2 * LLC_BYTES // packed.nbytes))
     w = [dev(torch, packed) for _ in range(copies)]
     del packed
     xd = dev(torch, x)
     y = torch.empty((1, N), dtype=torch.float32, device="cuda")
-    weight_bytes = synth.bytes_q8g64(N, K)
     alg_bytes = weight_bytes + 2 * K + 4 * N
 
     # Each bound call holds its device buffers, so they live as long as step.
-    calls = [Q.bound_q8g64(wc, xd, y, N, K) for wc in w]
+    calls = [bind(wc, xd, y, N, K) for wc in w]
 
     def step(i):
         calls[i % copies]()
 
-    info = {"workload": "lm_head Q8G64 GEMV m=1, N=151936 x K=2560 (Qwen3-4B vocabulary)",
-            "format": "q8g64", "m": 1, "N": N, "K": K, "weight_copies": copies, "period": copies,
-            "kernel": Q.variant_name(Q.FMT_Q8G64, 1, N, K)}
-    cpu = {"q": q, "s": s, "x": x}
+    info = {"workload": "lm_head %s GEMV m=1, N=151936 x K=2560 (Qwen3-4B vocabulary)" % fmt.upper(),
+            "format": fmt, "m": 1, "N": N, "K": K, "weight_copies": copies, "period": copies,
+            "kernel": Q.variant_name(fmt_id, 1, N, K)}
+    cpu = {"fmt": fmt, "q": q, "s": s, "x": x}
     return step, alg_bytes, weight_bytes, 1, info, cpu
 
 
 def cpu_lm_head(oracle, cpu, threads, reps):
+    fn = oracle.q8g64 if cpu["fmt"] == "q8g64" else oracle.q8g128
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        oracle.q8g64(cpu["q"], cpu["s"], cpu["x"], threads=threads)
+        fn(cpu["q"], cpu["s"], cpu["x"], threads=threads)
         times.append(time.perf_counter() - t0)
     return float(np.median(times)), "one full lm_head call (151936 x 2560, m=1), median of %d" % reps
 
@@ -143,7 +155,8 @@ def cpu_lm_head(oracle, cpu, threads, reps):
 # ------------------------------------------------------ small dense configs
 
 def setup_dense(torch, Q, synth, name, m=1):
-    """q8_small (1 GEMV), qwen3_0.6b (7 GEMVs) or q4_k2560 (3 GEMVs) per step."""
+    """q8_small (1 GEMV), qwen3_0.6b (7 GEMVs), q4_k2560 (3 GEMVs) or
+    w8a16_qwen3_14b_tp4 (5 GEMVs) per step."""
     wid = synth.WORKLOAD_IDS[name]
     if name == "q8_small":
         mats = [("w", "q8g64", 1024, 1024)]
@@ -151,6 +164,10 @@ def setup_dense(torch, Q, synth, name, m=1):
     elif name == "qwen3_0.6b":
         mats = synth.QWEN3_06B_LAYER
         desc = "Qwen3-0.6B-shaped decode layer, Q8G64 m=1: q, k, v, o, gate, up, down"
+    elif name == "w8a16_qwen3_14b_tp4":
+        mats = synth.W8A16_QWEN3_14B_TP4
+        desc = ("Qwen3-14B TP4 rank-local decode layer, per-output-channel W8A16 m=%d: "
+                "qkv 5120->1792, o 1280->5120, gate/up 5120->8704, down 4352->5120" % m)
     else:
         mats = synth.Q4_K2560
         desc = "Q4G32 K=2560 family m=%d: gate/up 2560->9216, down 9216->2560" % m
@@ -160,6 +177,9 @@ def setup_dense(torch, Q, synth, name, m=1):
         if fmt == "q8g64":
             packed = Q.qpack_q8g64(*synth.q8g64_weights(rng, N, K))
             wbytes += synth.bytes_q8g64(N, K)
+        elif fmt == "q8pc":
+            packed = Q.qpack_q8pc(*synth.q8pc_weights(rng, N, K))
+            wbytes += synth.bytes_q8pc(N, K)
         else:
             packed = Q.qpack_q4g32(*synth.q4g32_weights(rng, N, K))
             wbytes += synth.bytes_q4g32(N, K)
@@ -171,7 +191,9 @@ def setup_dense(torch, Q, synth, name, m=1):
     copies = max(1, -(-2 * LLC_BYTES // set_bytes))
     dev_sets = [[dev(torch, l[3]) for l in layer] for _ in range(copies)]
 
-    calls = [[(Q.bound_q8g64 if fmt == "q8g64" else Q.bound_q4g32)(w, x, y, N, K, m=m)
+    binders = {"q8g64": (Q.bound_q8g64, Q.FMT_Q8G64), "q4g32": (Q.bound_q4g32, Q.FMT_Q4G32),
+               "q8pc": (Q.bound_q8pc, Q.FMT_Q8PC)}
+    calls = [[binders[fmt][0](w, x, y, N, K, m=m)
               for (fmt, N, K, _, x, y), w in zip(layer, ws)] for ws in dev_sets]
 
     def step(i):
@@ -180,8 +202,7 @@ def setup_dense(torch, Q, synth, name, m=1):
 
     info = {"workload": desc, "format": mats[0][1], "m": m, "weight_copies": copies,
             "period": copies,
-            "kernel": sorted({Q.variant_name(0 if f == "q8g64" else 1, m, N, K)
-                              for (_, f, N, K) in mats})}
+            "kernel": sorted({Q.variant_name(binders[f][1], m, N, K) for (_, f, N, K) in mats})}
     return step, wbytes + io, wbytes, len(mats), info, None
 
 
@@ -311,9 +332,10 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="lm_head",
-                    choices=["lm_head", "moe_experts", "moe_experts_merged", "q8_small", "qwen3_0.6b",
-                             "q4_k2560"])
-    ap.add_argument("--m", type=int, default=1, help="activation rows (q4_k2560 only)")
+                    choices=["lm_head", "lm_head_q8g128", "moe_experts", "moe_experts_merged",
+                             "q8_small", "qwen3_0.6b", "q4_k2560", "w8a16_qwen3_14b_tp4"])
+    ap.add_argument("--m", type=int, default=1,
+                    help="activation rows (q4_k2560 and w8a16_qwen3_14b_tp4)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the timed steps from a captured HIP graph (no host launch cost)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -347,8 +369,9 @@ def main():
 
     def measure(name):
         t0 = time.time()
-        if name == "lm_head":
-            step, alg, wbytes, launches, info, cpu = setup_lm_head(torch, Q, synth)
+        if name in ("lm_head", "lm_head_q8g128"):
+            step, alg, wbytes, launches, info, cpu = setup_lm_head(
+                torch, Q, synth, "q8g64" if name == "lm_head" else "q8g128")
         elif name == "moe_experts":
             step, alg, wbytes, launches, info, cpu = setup_moe(torch, Q, synth)
         elif name == "moe_experts_merged":
@@ -382,7 +405,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded; int8/4-bit codes, fp16 scales and mins, N(0,1) bf16 x)",
+        "data": "synthetic (seeded; int8/4-bit codes, fp16 group scales and mins or fp32 row "
+                "scales, N(0,1) bf16 x)",
         "launch": "hip_graph" if args.graph else "eager",
         "config": dict(head["info"], algorithmic_bytes_per_step=head["alg"]),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
@@ -395,7 +419,7 @@ def main():
     if not args.no_cpu and head["cpu"] is not None:
         import oracle
         threads = max(1, min(16, len(os.sched_getaffinity(0))))
-        if args.workload == "lm_head":
+        if args.workload in ("lm_head", "lm_head_q8g128"):
             t, sample = cpu_lm_head(oracle, head["cpu"], threads, args.cpu_reps)
         else:
             t, sample = cpu_moe(oracle, head["cpu"], threads, args.cpu_reps, synth)

@@ -20,11 +20,16 @@
  *     dequantized inside the GEMV's registers.
  *
  * Formats (canonical, row-major, one output row n per weight row):
- *   Q8G64: q[N][K] int8; scale[N][K/64] fp16 bit patterns;
- *          w[n][k] = q[n][k] * scale[n][k/64]
- *   Q4G32: codes[N][K/2] bytes, element k in the low nibble of byte k/2 when
- *          k is even, the high nibble when k is odd; scale[N][K/32] and
- *          min[N][K/32] fp16 bit patterns; w[n][k] = code * scale + min
+ *   Q8G64:  q[N][K] int8; scale[N][K/64] fp16 bit patterns;
+ *           w[n][k] = q[n][k] * scale[n][k/64]
+ *   Q8G128: as Q8G64 with one scale per 128 K (scale[N][K/128]); the
+ *           LM-head format of the zLLM post's per-operator format map
+ *   Q8PC:   q[N][K] int8, one fp32 scale per output row (scale[N]);
+ *           w[n][k] = q[n][k] * scale[n]; the per-output-channel W8A16
+ *           format of the MetaInfer-cpp README (K a multiple of 16 here)
+ *   Q4G32:  codes[N][K/2] bytes, element k in the low nibble of byte k/2 when
+ *           k is even, the high nibble when k is odd; scale[N][K/32] and
+ *           min[N][K/32] fp16 bit patterns; w[n][k] = code * scale + min
  * The GEMV computes, for activation rows i < m,
  *          y[i*ldy + n] = sum_k w[n][k] * x[i*ldx + k]
  * with x in bf16 bit patterns and y in fp32.  Accumulation is fp32 in an
@@ -67,8 +72,8 @@ int qg_abi_version(void);
  * qpack_* re-tile canonical weights, once per matrix, into the layout the
  * kernels stream with 16-byte loads per lane.  Row order and the grouping
  * along K are kept; the packed buffer is opaque and its size depends only
- * on (N, K).  Both formats need K to be a whole number of groups (64 for
- * Q8G64, 32 for Q4G32) and 1 <= N, K < 2^31.
+ * on (N, K).  K must be a whole number of groups (64 for Q8G64, 128 for
+ * Q8G128, 32 for Q4G32, 16 for Q8PC) and 1 <= N, K < 2^31.
  *
  * *_size returns the packed size in bytes (a multiple of 256), or 0 for an
  * invalid shape.  The device copy of a packed buffer must be 256-byte
@@ -80,6 +85,18 @@ qg_status qpack_q8g64(const int8_t *q, const uint16_t *scales_f16,
                       int64_t N, int64_t K, void *out, size_t out_bytes);
 qg_status qunpack_q8g64(const void *packed, size_t packed_bytes, int64_t N, int64_t K,
                         int8_t *q, uint16_t *scales_f16);
+
+size_t    qpack_q8g128_size(int64_t N, int64_t K);              /* K % 128 == 0 */
+qg_status qpack_q8g128(const int8_t *q, const uint16_t *scales_f16,
+                       int64_t N, int64_t K, void *out, size_t out_bytes);
+qg_status qunpack_q8g128(const void *packed, size_t packed_bytes, int64_t N, int64_t K,
+                         int8_t *q, uint16_t *scales_f16);
+
+size_t    qpack_q8pc_size(int64_t N, int64_t K);                /* K % 16 == 0 */
+qg_status qpack_q8pc(const int8_t *q, const float *scales_f32,
+                     int64_t N, int64_t K, void *out, size_t out_bytes);
+qg_status qunpack_q8pc(const void *packed, size_t packed_bytes, int64_t N, int64_t K,
+                       int8_t *q, float *scales_f32);
 
 size_t    qpack_q4g32_size(int64_t N, int64_t K);
 qg_status qpack_q4g32(const uint8_t *codes, const uint16_t *scales_f16,
@@ -107,6 +124,14 @@ qg_status qgemv_q8g64(const void *w_packed, const uint16_t *x_bf16, float *y,
 qg_status qgemv_q4g32(const void *w_packed, const uint16_t *x_bf16, float *y,
                       int64_t m, int64_t N, int64_t K, int64_t ldx, int64_t ldy,
                       void *hip_stream);
+/* Same contract for the two further 8-bit formats (packed by qpack_q8g128 /
+ * qpack_q8pc with the same N and K). */
+qg_status qgemv_q8g128(const void *w_packed, const uint16_t *x_bf16, float *y,
+                       int64_t m, int64_t N, int64_t K, int64_t ldx, int64_t ldy,
+                       void *hip_stream);
+qg_status qgemv_q8pc(const void *w_packed, const uint16_t *x_bf16, float *y,
+                     int64_t m, int64_t N, int64_t K, int64_t ldx, int64_t ldy,
+                     void *hip_stream);
 
 /* Routed-expert decode (one token, several experts), Q4G32:
  *   for each slot j < n_slots, with e = expert_ids_dev[j]:
@@ -134,13 +159,15 @@ qg_status qgemv_grouped_q4g32(const void *w_experts_packed, int64_t expert_strid
 
 /* ------------------------------------------------------------- test hooks
  * Every successful qgemv_* call bumps the counter of the kernel variant it
- * launched.  Variant names: "<fmt>[_grouped]_m<m>_g<G>_r<R>", e.g.
- * "q8g64_m1_g32_r2".  qg_route_count returns 0 for unknown names. */
+ * launched.  Variant names: "<fmt>[_grouped]_m<m>_g<G>_r<R>" with fmt one of
+ * q8g64, q4g32, q8g128, q8pc, e.g. "q8g64_m1_g32_r2".  qg_route_count
+ * returns 0 for unknown names. */
 void     qg_route_counts_reset(void);
 uint64_t qg_route_count(const char *variant);
 /* Writes the name of the variant qgemv_* would launch for (fmt, m, N, K)
- * into buf (fmt 0 = Q8G64, 1 = Q4G32, 2 = grouped Q4G32).  Returns QG_OK or
- * the status the call itself would return for that shape. */
+ * into buf (fmt 0 = Q8G64, 1 = Q4G32, 2 = grouped Q4G32, 3 = Q8G128,
+ * 4 = Q8PC).  Returns QG_OK or the status the call itself would return for
+ * that shape. */
 qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char *buf, size_t buf_len);
 
 #ifdef __cplusplus

@@ -157,7 +157,11 @@ def q8g128(q: np.ndarray, scale: np.ndarray, x: np.ndarray, threads: int = 1):
 
 
 def q8pc(q: np.ndarray, scale_f32: np.ndarray, x: np.ndarray, threads: int = 1):
-    """Q8 per output channel: q [N][K] int8, scale [N] fp32 bit patterns (uint32)."""
+    """Q8 per output channel: q [N][K] int8, scale [N] fp32 bit patterns (uint32)
+    or float32 values (taken bit for bit, never converted)."""
+    scale_f32 = np.asarray(scale_f32)
+    if scale_f32.dtype == np.float32:
+        scale_f32 = scale_f32.view(np.uint32)
     return _q8_generic("oracle_q8pc", q, scale_f32, x, threads, np.uint32, lambda N, K: (N,))
 
 

@@ -61,6 +61,28 @@ def test_q8_pack_roundtrip(N, K):
     assert np.array_equal(packed, Q.qpack_q8g64(q, s))      # deterministic
 
 
+@pytest.mark.parametrize("N,K", [(1, 128), (7, 384), (129, 128), (3, 2560), (33, 5120)])
+def test_q8g128_pack_roundtrip(N, K):
+    rng = synth.rng_for(9, N, K)
+    q = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+    s = rng.integers(0, 65536, size=(N, K // 128), dtype=np.uint16)
+    packed = Q.qpack_q8g128(q, s)
+    assert packed.nbytes == Q.qpack_q8g128_size(N, K)
+    q2, s2 = Q.qunpack_q8g128(packed, N, K)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+@pytest.mark.parametrize("N,K", [(1, 16), (7, 48), (129, 16), (5, 4352), (33, 1280), (2, 5120)])
+def test_q8pc_pack_roundtrip(N, K):
+    rng = synth.rng_for(10, N, K)
+    q = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+    s = rng.integers(0, 2**32, size=N, dtype=np.uint64).astype(np.uint32)
+    packed = Q.qpack_q8pc(q, s)
+    assert packed.nbytes == Q.qpack_q8pc_size(N, K)
+    q2, s2 = Q.qunpack_q8pc(packed, N, K)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
 @pytest.mark.parametrize("N,K", [(1, 32), (7, 96), (129, 32), (5, 1536), (9, 9216), (33, 2560)])
 def test_q4_pack_roundtrip(N, K):
     rng = synth.rng_for(8, N, K)
@@ -81,6 +103,9 @@ def test_packed_size_is_algorithmic_bytes_plus_tail_padding():
         assert Q.qpack_q4g32_size(N, K) == synth.bytes_q4g32(N, K)
     for (N, K) in [(2048, 1024), (1024, 2048), (3072, 1024), (1024, 3072)]:
         assert Q.qpack_q8g64_size(N, K) == synth.bytes_q8g64(N, K)
+    assert Q.qpack_q8g128_size(151936, 2560) == synth.bytes_q8g128(151936, 2560)
+    for (_, _, N, K) in synth.W8A16_QWEN3_14B_TP4:
+        assert Q.qpack_q8pc_size(N, K) == synth.bytes_q8pc(N, K)
     # ragged N: at most one partial tile of padding, rounded to 256 bytes
     for N in (1, 7, 129, 1000):
         per_row = synth.bytes_q8g64(1, 1024)
@@ -95,6 +120,8 @@ def test_invalid_shapes_have_no_packed_size():
     assert Q.qpack_q4g32_size(4, 48) == 0      # not a whole 32-group
     assert Q.qpack_q4g32_size(-1, 32) == 0
     assert Q.qpack_q4g32_size(1 << 31, 32) == 0
+    assert Q.qpack_q8g128_size(4, 64) == 0    # not a whole 128-group
+    assert Q.qpack_q8pc_size(4, 24) == 0      # not a multiple of 16
 
 
 def test_qpack_rejects_short_output_and_nulls():
@@ -113,10 +140,16 @@ def test_qpack_rejects_short_output_and_nulls():
 W, X, Y, IDS = 1 << 20, 1 << 21, 1 << 22, 1 << 23
 
 
-@pytest.mark.parametrize("fn", ["qgemv_q8g64", "qgemv_q4g32"])
-def test_dense_validation(fn):
+# (entry point, K granularity).  Every call below must fail validation: a
+# call that passed would launch a kernel on the fake addresses.
+DENSE = [("qgemv_q8g64", 64), ("qgemv_q4g32", 32), ("qgemv_q8g128", 128), ("qgemv_q8pc", 16)]
+
+
+@pytest.mark.parametrize("fn,group", DENSE)
+def test_dense_validation(fn, group):
     f = getattr(Q.lib(), fn)
     K = 128
+    ragged = K + group // 2                    # not a whole number of groups
     assert f(None, X, Y, 1, 16, K, K, 16, None) == Q.QG_ERR_INVALID_ARG
     assert f(W, None, Y, 1, 16, K, K, 16, None) == Q.QG_ERR_INVALID_ARG
     assert f(W, X, None, 1, 16, K, K, 16, None) == Q.QG_ERR_INVALID_ARG
@@ -124,7 +157,7 @@ def test_dense_validation(fn):
     assert f(W, X, Y, -1, 16, K, K, 16, None) == Q.QG_ERR_UNSUPPORTED
     assert f(W, X, Y, 1, 0, K, K, 16, None) == Q.QG_ERR_INVALID_ARG           # N < 1
     assert f(W, X, Y, 1, 16, 0, K, 16, None) == Q.QG_ERR_INVALID_ARG
-    assert f(W, X, Y, 1, 16, K + 16, K + 16, 16, None) == Q.QG_ERR_INVALID_ARG  # ragged group
+    assert f(W, X, Y, 1, 16, ragged, ragged, 16, None) == Q.QG_ERR_INVALID_ARG
     assert f(W, X, Y, 2, 16, K, K - 2, 16, None) == Q.QG_ERR_INVALID_ARG      # ldx < K
     assert f(W, X, Y, 2, 16, K, K, 15, None) == Q.QG_ERR_INVALID_ARG          # ldy < N
     assert f(W + 16, X, Y, 1, 16, K, K, 16, None) == Q.QG_ERR_ALIGNMENT
@@ -169,6 +202,11 @@ def test_variant_names_follow_layout():
     assert Q.variant_name(2, 1, 1536, 4096) == "q4g32_grouped_m1_g64_r2"
     assert Q.variant_name(2, 1, 4096, 1536) == "q4g32_grouped_m1_g16_r2"
     assert Q.variant_name(1, 1, 8, 96) == "q4g32_m1_g1_r2"     # 3 units: G = 1
+    assert Q.variant_name(3, 1, 151936, 2560) == "q8g128_m1_g32_r2"
+    assert Q.variant_name(3, 2, 7, 128) == "q8g128_m2_g8_r2"  # one group: G = 8
+    assert Q.variant_name(4, 1, 1792, 5120) == "q8pc_m1_g64_r2"
+    assert Q.variant_name(4, 4, 5120, 4352) == "q8pc_m4_g16_r2"
+    assert Q.variant_name(4, 1, 3, 48) == "q8pc_m1_g1_r2"
     with pytest.raises(Q.QGError):
         Q.variant_name(0, 5, 16, 64)
     assert Q.route_count("no_such_variant") == 0

@@ -30,18 +30,29 @@ def _run(cmd):
     subprocess.check_call(cmd)
 
 
+HIP_SOURCES = ["kern_q8g64.hip", "kern_q4g32.hip", "kern_q8g128.hip", "kern_q8pc.hip",
+               "launch.hip", "abi.cpp"]
+HOST_SOURCES = ["qpack.cpp"]
+
+
 def build(verbose: bool = True) -> str:
+    """Compiles every source (the per-format kernel units in parallel) and
+    links libqgemv.so."""
+    from concurrent.futures import ThreadPoolExecutor
+
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
-    kern_o = os.path.join(BUILD, "kernels.o")
-    _run([HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, "kernels.hip"), "-o", kern_o])
-    objs.append(kern_o)
-    abi_o = os.path.join(BUILD, "abi.o")
-    _run([HIPCC] + HIP_FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, "abi.cpp"), "-o", abi_o])
-    objs.append(abi_o)
-    qpack_o = os.path.join(BUILD, "qpack.o")
-    _run(["g++"] + HOST_FLAGS + ["-c", os.path.join(CSRC, "qpack.cpp"), "-o", qpack_o])
-    objs.append(qpack_o)
+    jobs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        lang = ["-x", "hip"] if src.endswith(".cpp") else []
+        jobs.append((obj, [HIPCC] + HIP_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]))
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        jobs.append((obj, ["g++"] + HOST_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]))
+    workers = max(1, min(len(jobs), len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda job: _run(job[1]), jobs))
+    objs = [obj for obj, _ in jobs]
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)
     os.replace(tmp, LIB)

@@ -18,8 +18,8 @@
 namespace {
 
 // Route counters: one per (kind, m, log2 G).  kind 0 Q8G64, 1 Q4G32,
-// 2 grouped Q4G32.
-constexpr int kKinds = 3, kMs = 4, kGs = 7;
+// 2 grouped Q4G32, 3 Q8G128, 4 Q8PC.
+constexpr int kKinds = 5, kMs = 4, kGs = 7;
 std::atomic<uint64_t> g_route[kKinds][kMs][kGs];
 
 int log2i(int v)
@@ -31,7 +31,24 @@ int log2i(int v)
 
 const char* kind_name(int kind)
 {
-    return kind == 0 ? "q8g64" : kind == 1 ? "q4g32" : "q4g32_grouped";
+    switch (kind) {
+    case 0: return "q8g64";
+    case 1: return "q4g32";
+    case 2: return "q4g32_grouped";
+    case 3: return "q8g128";
+    default: return "q8pc";
+    }
+}
+
+// Route-counter kind of a dense format.
+int kind_of(int fmt)
+{
+    switch (fmt) {
+    case qg::FMT_Q8G64: return 0;
+    case qg::FMT_Q4G32: return 1;
+    case qg::FMT_Q8G128: return 3;
+    default: return 4;
+    }
 }
 
 void format_variant(int kind, int m, int G, char* buf, size_t len)
@@ -79,7 +96,7 @@ qg_status run_dense(int fmt, const void* w_packed, const uint16_t* x, float* y, 
     a.stream = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // clear a stale error so the check below is ours
     if (qg::launch(a) != hipSuccess) return QG_ERR_HIP;
-    g_route[fmt][m - 1][log2i(L.G)].fetch_add(1, std::memory_order_relaxed);
+    g_route[kind_of(fmt)][m - 1][log2i(L.G)].fetch_add(1, std::memory_order_relaxed);
     return QG_OK;
 }
 
@@ -111,6 +128,18 @@ qg_status qgemv_q4g32(const void* w_packed, const uint16_t* x_bf16, float* y, in
                       int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* hip_stream)
 {
     return run_dense(qg::FMT_Q4G32, w_packed, x_bf16, y, m, N, K, ldx, ldy, hip_stream);
+}
+
+qg_status qgemv_q8g128(const void* w_packed, const uint16_t* x_bf16, float* y, int64_t m,
+                       int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* hip_stream)
+{
+    return run_dense(qg::FMT_Q8G128, w_packed, x_bf16, y, m, N, K, ldx, ldy, hip_stream);
+}
+
+qg_status qgemv_q8pc(const void* w_packed, const uint16_t* x_bf16, float* y, int64_t m,
+                     int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* hip_stream)
+{
+    return run_dense(qg::FMT_Q8PC, w_packed, x_bf16, y, m, N, K, ldx, ldy, hip_stream);
 }
 
 qg_status qgemv_grouped_q4g32(const void* w_experts_packed, int64_t expert_stride_bytes,
@@ -176,10 +205,12 @@ uint64_t qg_route_count(const char* variant)
 qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char* buf, size_t buf_len)
 {
     if (!buf || buf_len == 0) return QG_ERR_INVALID_ARG;
-    if (fmt < 0 || fmt > 2) return QG_ERR_INVALID_ARG;
+    static const int kind_format[kKinds] = {qg::FMT_Q8G64, qg::FMT_Q4G32, qg::FMT_Q4G32,
+                                            qg::FMT_Q8G128, qg::FMT_Q8PC};
+    if (fmt < 0 || fmt >= kKinds) return QG_ERR_INVALID_ARG;
     if (fmt == 2 && m != 1) return QG_ERR_UNSUPPORTED;
     qg::Layout L;
-    const qg_status st = check_shape(fmt == 0 ? qg::FMT_Q8G64 : qg::FMT_Q4G32, m, N, K, &L);
+    const qg_status st = check_shape(kind_format[fmt], m, N, K, &L);
     if (st != QG_OK) return st;
     format_variant(fmt, int(m), L.G, buf, buf_len);
     return QG_OK;

@@ -1,0 +1,13 @@
+// Q8PC kernels: the instantiations of kernel_body.h for this format
+// (one translation unit per format so they compile in parallel).
+#include "kernel_body.h"
+
+namespace qg {
+
+hipError_t launch_q8pc(int m, bool grouped, int G, int shape, const KernelParams& kp, int64_t waves,
+                       int slots, size_t lds, hipStream_t s)
+{
+    return launch_format<FMT_Q8PC>(m, grouped, G, shape, kp, waves, slots, lds, s);
+}
+
+}  // namespace qg

@@ -26,6 +26,7 @@
 //    the lane group at the end of the tile.  No atomics: the result is the
 //    same bits on every run.
 // MFMA is not used: at m <= 4 there is no matrix to feed it.
+#pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -39,14 +40,6 @@ namespace {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Launch shapes (waves per work-group, ring depth) are template parameters;
-// launch() picks one per matrix shape.  Wave counts are per compute unit:
-// a dense sweep runs one 4-wave work-group per CU (every CU streams the same
-// bytes and the launch reads one window of about CUs*4 tiles at a time),
-// routed-expert launches two.  Both were measured best on MI355X; uneven
-// work-groups per CU (some CUs holding two) measured up to 25% slower.
-constexpr int64_t kWavesPerCuDense = 4;
-constexpr int64_t kWavesPerCuGrouped = 8;
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // (1.0, 1.0)
 constexpr uint32_t kMagicBf16x2 = 0x43004300u;  // (128.0, 128.0)
 
@@ -134,7 +127,7 @@ __device__ __forceinline__ void q4_pairs(const u32x4& c, uint32_t (&pr)[16])
 // memory loads complete in issue order.
 template <int FMT, int M, int THREADS>
 struct XStage {
-    static constexpr int UD = FMT == FMT_Q8G64 ? 8 : 16;   // dwords per unit
+    static constexpr int UD = FMT == FMT_Q4G32 ? 16 : 8;   // dwords per unit
     uint32_t v[UD];
     int first;                                             // flattened unit index
 
@@ -192,18 +185,19 @@ struct XStage {
 
 // One work item = one step of one tile: R 16-byte units per lane plus the
 // lane's meta word(s).  Items of a matrix are laid out back to back, so item
-// i's blocks start at i * R KiB and its meta at code_bytes + i * meta_step.
+// i of tile t has its blocks at i * R KiB and its meta at
+// code_bytes + i * meta_step + t * meta_tile (layout.h).
 template <int R, int META_BYTES>
 struct Item {
     u32x4 c[R];
     Meta<META_BYTES> m;
     __device__ __forceinline__ void load(const uint8_t* code_lane, const uint8_t* meta_lane,
-                                         int64_t item, int64_t meta_step)
+                                         int64_t item, int64_t tile, const KernelParams& p)
     {
         const uint8_t* cp = code_lane + item * (R * 1024);
 #pragma unroll
         for (int r = 0; r < R; ++r) c[r] = load_stream16(cp + r * 1024);
-        m.load(meta_lane + item * meta_step);
+        m.load(meta_lane + item * p.meta_step_bytes + tile * p.meta_tile_bytes);
     }
 };
 
@@ -212,7 +206,7 @@ __device__ __forceinline__ void consume(const Item<R, META_BYTES>& it, const uin
                                         const float* xsum, int KD, int U, int u,
                                         float (&acc)[R][M])
 {
-    constexpr int UD = FMT == FMT_Q8G64 ? 8 : 16;
+    constexpr int UD = FMT == FMT_Q4G32 ? 16 : 8;
     uint32_t xd[M][UD];
     float X[M];
 #pragma unroll
@@ -228,8 +222,11 @@ __device__ __forceinline__ void consume(const Item<R, META_BYTES>& it, const uin
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        if (FMT == FMT_Q8G64) {
-            const float s = (r & 1) ? half_hi(it.m.w[r >> 1]) : half_lo(it.m.w[r >> 1]);
+        if (FMT != FMT_Q4G32) {
+            // Q8G64/Q8G128: fp16 scale of the unit's group; Q8PC: fp32 row scale.
+            float s;
+            if constexpr (FMT == FMT_Q8PC) s = __uint_as_float(it.m.w[r]);
+            else s = (r & 1) ? half_hi(it.m.w[r >> 1]) : half_lo(it.m.w[r >> 1]);
             uint32_t pr[8];
             q8_pairs(it.c[r], pr);
 #pragma unroll
@@ -385,11 +382,14 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     constexpr int kWaves = WAVES;
     constexpr int kThreads = 64 * WAVES;
     extern __shared__ __align__(16) uint32_t lds[];
-    constexpr int META_BYTES = FMT == FMT_Q8G64 ? 2 * R : 4 * R;
+    // Meta bytes a lane reads per item: R fp16 scales (Q8G64, Q8G128), R
+    // scale|min dwords (Q4G32) or R fp32 row scales (Q8PC).
+    constexpr int META_BYTES = (FMT == FMT_Q8G64 || FMT == FMT_Q8G128) ? 2 * R : 4 * R;
     constexpr int RPS = 64 / G;
     constexpr int TR = R * RPS;
     static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "G must be a power of two <= 64");
-    static_assert(FMT != FMT_Q8G64 || G >= 4, "Q8 lane groups span whole 64-code groups");
+    static_assert(FMT != FMT_Q8G64 || G >= 4, "Q8G64 lane groups span whole 64-code groups");
+    static_assert(FMT != FMT_Q8G128 || G >= 8, "Q8G128 lane groups span whole 128-code groups");
 
     const int lane = threadIdx.x & 63;
     // The wave index is the same in every lane; say so, so that all item
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     const int g = lane & (G - 1);
     const int rho = lane / G;
     const int KD = p.K >> 1;
-    const int U = p.K / (FMT == FMT_Q8G64 ? 16 : 32);
+    const int U = p.K / (FMT == FMT_Q4G32 ? 32 : 16);
     uint32_t* xs = lds;
     float* xsum = reinterpret_cast<float*>(lds + M * KD);
 
@@ -445,6 +445,8 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     const uint8_t* code_lane = w + lane * 16;
     int lane_meta;
     if (FMT == FMT_Q8G64) lane_meta = ((rho * (G / 4) + (g >> 2)) * R) * 2;
+    else if (FMT == FMT_Q8G128) lane_meta = ((rho * (G / 8) + (g >> 3)) * R) * 2;
+    else if (FMT == FMT_Q8PC) lane_meta = rho * R * 4;
     else lane_meta = lane * R * 4;
     const uint8_t* meta_lane = w + p.code_bytes + lane_meta;
 
@@ -453,7 +455,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     Item<R, META_BYTES> ring[DEPTH];
 #define QG_LOAD_NEXT(slot_)                                                                   \
     do {                                                                                      \
-        ring[slot_].load(code_lane, meta_lane, ld_tile * p.J + ld_j, p.meta_step_bytes);     \
+        ring[slot_].load(code_lane, meta_lane, ld_tile * p.J + ld_j, ld_tile, p);            \
         if (++ld_j == p.J) { ld_j = 0; ld_tile += tstep; }                                   \
     } while (0)
 
@@ -467,7 +469,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
             if (d < n_items) {                                                                \
                 QG_LOAD_NEXT(d);                                                              \
             } else {                                                                          \
-                ring[d].load(code_lane, meta_lane, 0, p.meta_step_bytes);                     \
+                ring[d].load(code_lane, meta_lane, 0, 0, p);                                  \
             }                                                                                 \
         }                                                                                     \
     } while (0)
@@ -539,10 +541,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
 #undef QG_ADVANCE
 }
 
-// Launch shape: ring depth 2 when a tile has at most 3 steps (a deeper
-// ring would prefetch into the wave's next tile, far away in memory, and
-// measured slower), else 4.  Work-groups are 4 waves.
-enum Shape { SHAPE_D2_W4 = 0, SHAPE_D4_W4 = 1 };
+// Launch shape (launch.h): ring depth 2 or 4; work-groups are 4 waves.
 
 template <int FMT, int M, int G, int DEPTH, int WAVES, bool GROUPED>
 hipError_t launch_variant(const KernelParams& kp, int64_t waves, int slots, size_t lds_bytes,
@@ -578,10 +577,12 @@ hipError_t launch_g(int G, int shape, const KernelParams& kp, int64_t waves, int
     case 32: return launch_shape<FMT, M, 32, GROUPED>(shape, kp, waves, slots, lds, s);
     case 16: return launch_shape<FMT, M, 16, GROUPED>(shape, kp, waves, slots, lds, s);
     case 8: return launch_shape<FMT, M, 8, GROUPED>(shape, kp, waves, slots, lds, s);
-    case 4: return launch_shape<FMT, M, 4, GROUPED>(shape, kp, waves, slots, lds, s);
     default: break;
     }
-    if constexpr (FMT == FMT_Q4G32) {
+    if constexpr (FMT != FMT_Q8G128) {
+        if (G == 4) return launch_shape<FMT, M, 4, GROUPED>(shape, kp, waves, slots, lds, s);
+    }
+    if constexpr (FMT == FMT_Q4G32 || FMT == FMT_Q8PC) {
         switch (G) {
         case 2: return launch_shape<FMT, M, 2, GROUPED>(shape, kp, waves, slots, lds, s);
         case 1: return launch_shape<FMT, M, 1, GROUPED>(shape, kp, waves, slots, lds, s);
@@ -593,104 +594,23 @@ hipError_t launch_g(int G, int shape, const KernelParams& kp, int64_t waves, int
 
 }  // namespace
 
-// Compute units of the current device, looked up once per device.
-static int64_t compute_units()
+// Launches the kernel of format FMT for m activation rows (one instantiation
+// per format, each in its own translation unit).
+template <int FMT>
+hipError_t launch_format(int m, bool grouped, int G, int shape, const KernelParams& kp, int64_t waves,
+                         int slots, size_t lds, hipStream_t s)
 {
-    static int64_t cached[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
-size_t lds_bytes_for(const Layout& L, int m)
-{
-    return size_t(m) * size_t(L.K / 2 + L.U) * 4;
-}
-
-hipError_t launch(const LaunchArgs& a)
-{
-    const Layout& L = a.layout;
-    KernelParams kp;
-    kp.w = static_cast<const uint8_t*>(a.w);
-    kp.expert_stride = a.expert_stride;
-    kp.ids = a.ids;
-    kp.n_experts = a.n_experts;
-    kp.x = a.x;
-    kp.ldx = a.ldx;
-    kp.x_slot_stride = a.x_slot_stride;
-    kp.y = a.y;
-    kp.ldy = a.ldy;
-    kp.y_slot_stride = a.y_slot_stride;
-    kp.N = int32_t(L.N);
-    kp.K = int32_t(L.K);
-    kp.J = L.J;
-    kp.tiles = L.tiles;
-    kp.code_bytes = L.code_bytes;
-    kp.meta_step_bytes = L.meta_step_bytes;
-    const int slots = a.grouped ? a.n_slots : 1;
-    // About target_waves waves in total (QG_TARGET_WAVES overrides it, for
-    // tuning sweeps), never more waves than tiles; k tiles per wave, then the
-    // fewest waves that cover the tiles with k each, so all waves get k tiles
-    // (a few k-1), never k for some and k/2 for others.
-    static const int64_t env_waves = [] {
-        const char* e = getenv("QG_TARGET_WAVES");
-        const long v = e ? strtol(e, nullptr, 10) : 0;
-        return v > 0 ? int64_t(v) : int64_t(0);
-    }();
-    const int64_t cus = compute_units();
-    const int64_t target_waves =
-        env_waves ? env_waves : cus * (a.grouped ? kWavesPerCuGrouped : kWavesPerCuDense);
-    int64_t cap = target_waves / slots;
-    if (cap < 1) cap = 1;
-    // Up to twice the cap, a dense launch is latency-bound rather than
-    // stream-bound: one tile per wave gives it the most parallelism.
-    const int64_t k = (!a.grouped && L.tiles <= 2 * cap) ? 1 : (L.tiles + cap - 1) / cap;
-    const int64_t waves_per_slot = (L.tiles + k - 1) / k;
-    // A ring of 2 only when the wave streams several shallow tiles; with a
-    // single tile per wave the whole tile goes in flight at once.
-    int shape = (L.J <= 3 && k >= 2) ? SHAPE_D2_W4 : SHAPE_D4_W4;
-    // Routed-expert launches give each wave a contiguous run of k tiles (the
-    // whole 31.5 MB call is in flight at once anyway, so a common window
-    // buys nothing, and adjacent tiles measured ~3% faster); dense sweeps
-    // keep the grid-stride window.  QG_CONTIG=0/1 overrides (tuning sweeps).
-    static const int env_contig = [] {
-        const char* e = getenv("QG_CONTIG");
-        return e ? int(strtol(e, nullptr, 10)) : -1;
-    }();
-    const bool contig = env_contig >= 0 ? env_contig != 0 : a.grouped;
-    kp.contig_k = contig ? k : 0;
-    static const int env_shape = [] {
-        const char* e = getenv("QG_SHAPE");   // tuning sweeps only
-        return e ? int(strtol(e, nullptr, 10)) : -1;
-    }();
-    if (env_shape == SHAPE_D2_W4 || env_shape == SHAPE_D4_W4) shape = env_shape;
-    const size_t lds = lds_bytes_for(L, a.m);
-    const hipStream_t s = a.stream;
-    const int64_t w = waves_per_slot;
-    if (a.grouped) {
-        if (L.fmt != FMT_Q4G32 || a.m != 1) return hipErrorInvalidValue;
-        return launch_g<FMT_Q4G32, 1, true>(L.G, shape, kp, w, slots, lds, s);
-    }
-    if (L.fmt == FMT_Q8G64) {
-        switch (a.m) {
-        case 1: return launch_g<FMT_Q8G64, 1, false>(L.G, shape, kp, w, slots, lds, s);
-        case 2: return launch_g<FMT_Q8G64, 2, false>(L.G, shape, kp, w, slots, lds, s);
-        case 3: return launch_g<FMT_Q8G64, 3, false>(L.G, shape, kp, w, slots, lds, s);
-        case 4: return launch_g<FMT_Q8G64, 4, false>(L.G, shape, kp, w, slots, lds, s);
-        default: return hipErrorInvalidValue;
+    if (grouped) {
+        if constexpr (FMT == FMT_Q4G32) {
+            if (m == 1) return launch_g<FMT, 1, true>(G, shape, kp, waves, slots, lds, s);
         }
+        return hipErrorInvalidValue;
     }
-    switch (a.m) {
-    case 1: return launch_g<FMT_Q4G32, 1, false>(L.G, shape, kp, w, slots, lds, s);
-    case 2: return launch_g<FMT_Q4G32, 2, false>(L.G, shape, kp, w, slots, lds, s);
-    case 3: return launch_g<FMT_Q4G32, 3, false>(L.G, shape, kp, w, slots, lds, s);
-    case 4: return launch_g<FMT_Q4G32, 4, false>(L.G, shape, kp, w, slots, lds, s);
+    switch (m) {
+    case 1: return launch_g<FMT, 1, false>(G, shape, kp, waves, slots, lds, s);
+    case 2: return launch_g<FMT, 2, false>(G, shape, kp, waves, slots, lds, s);
+    case 3: return launch_g<FMT, 3, false>(G, shape, kp, waves, slots, lds, s);
+    case 4: return launch_g<FMT, 4, false>(G, shape, kp, waves, slots, lds, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -1,5 +1,5 @@
 // Internal interface between the C ABI (abi.cpp) and the kernels
-// (kernels.hip).  Not installed; callers use include/qgemv.h.
+// (kern_*.hip).  Not installed; callers use include/qgemv.h.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -30,8 +30,12 @@ struct KernelParams {
     int64_t tiles;
     int64_t code_bytes;        // offset of the meta blocks
     int64_t meta_step_bytes;
+    int64_t meta_tile_bytes;   // per-tile meta after the steps' meta (Q8PC row scales)
     int64_t contig_k;          // > 0: each wave streams contig_k consecutive tiles
 };
+
+// Launch shape: ring depth 2 or 4 items; work-groups are 4 waves.
+enum Shape { SHAPE_D2_W4 = 0, SHAPE_D4_W4 = 1 };
 
 struct LaunchArgs {
     Layout layout;
@@ -56,5 +60,16 @@ size_t lds_bytes_for(const Layout& L, int m);
 
 // Enqueues the kernel; returns the HIP status of the launch.
 hipError_t launch(const LaunchArgs& a);
+
+// Per-format kernel launchers (kern_<format>.hip): m activation rows, lane
+// group G, launch shape, waves per slot, slots (grid y), dynamic LDS bytes.
+#define QG_DECLARE_LAUNCHER(name)                                                            \
+    hipError_t name(int m, bool grouped, int G, int shape, const KernelParams& kp,            \
+                    int64_t waves, int slots, size_t lds, hipStream_t s)
+QG_DECLARE_LAUNCHER(launch_q8g64);
+QG_DECLARE_LAUNCHER(launch_q4g32);
+QG_DECLARE_LAUNCHER(launch_q8g128);
+QG_DECLARE_LAUNCHER(launch_q8pc);
+#undef QG_DECLARE_LAUNCHER
 
 }  // namespace qg

@@ -1,0 +1,111 @@
+// Host side of the launch: picks the wave count, ring depth and tile mapping
+// for a matrix and calls the format's kernel (kern_*.hip).  No device code.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "launch.h"
+
+namespace qg {
+
+namespace {
+// Wave counts are per compute unit: a dense sweep runs one 4-wave
+// work-group per CU (every CU streams the same bytes and the launch reads
+// one window of about CUs*4 tiles at a time), routed-expert launches two.
+// Both were measured best on MI355X; uneven work-groups per CU (some CUs
+// holding two) measured up to 25% slower.
+constexpr int64_t kWavesPerCuDense = 4;
+constexpr int64_t kWavesPerCuGrouped = 8;
+}  // namespace
+
+// Compute units of the current device, looked up once per device.
+static int64_t compute_units()
+{
+    static int64_t cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+size_t lds_bytes_for(const Layout& L, int m)
+{
+    return size_t(m) * size_t(L.K / 2 + L.U) * 4;
+}
+
+hipError_t launch(const LaunchArgs& a)
+{
+    const Layout& L = a.layout;
+    KernelParams kp;
+    kp.w = static_cast<const uint8_t*>(a.w);
+    kp.expert_stride = a.expert_stride;
+    kp.ids = a.ids;
+    kp.n_experts = a.n_experts;
+    kp.x = a.x;
+    kp.ldx = a.ldx;
+    kp.x_slot_stride = a.x_slot_stride;
+    kp.y = a.y;
+    kp.ldy = a.ldy;
+    kp.y_slot_stride = a.y_slot_stride;
+    kp.N = int32_t(L.N);
+    kp.K = int32_t(L.K);
+    kp.J = L.J;
+    kp.tiles = L.tiles;
+    kp.code_bytes = L.code_bytes;
+    kp.meta_step_bytes = L.meta_step_bytes;
+    kp.meta_tile_bytes = L.meta_tile_bytes;
+    const int slots = a.grouped ? a.n_slots : 1;
+    // About target_waves waves in total (QG_TARGET_WAVES overrides it, for
+    // tuning sweeps), never more waves than tiles; k tiles per wave, then the
+    // fewest waves that cover the tiles with k each, so all waves get k tiles
+    // (a few k-1), never k for some and k/2 for others.
+    static const int64_t env_waves = [] {
+        const char* e = getenv("QG_TARGET_WAVES");
+        const long v = e ? strtol(e, nullptr, 10) : 0;
+        return v > 0 ? int64_t(v) : int64_t(0);
+    }();
+    const int64_t cus = compute_units();
+    const int64_t target_waves =
+        env_waves ? env_waves : cus * (a.grouped ? kWavesPerCuGrouped : kWavesPerCuDense);
+    int64_t cap = target_waves / slots;
+    if (cap < 1) cap = 1;
+    // Up to twice the cap, a dense launch is latency-bound rather than
+    // stream-bound: one tile per wave gives it the most parallelism.
+    const int64_t k = (!a.grouped && L.tiles <= 2 * cap) ? 1 : (L.tiles + cap - 1) / cap;
+    const int64_t waves_per_slot = (L.tiles + k - 1) / k;
+    // A ring of 2 only when the wave streams several shallow tiles; with a
+    // single tile per wave the whole tile goes in flight at once.
+    int shape = (L.J <= 3 && k >= 2) ? SHAPE_D2_W4 : SHAPE_D4_W4;
+    // Routed-expert launches give each wave a contiguous run of k tiles (the
+    // whole 31.5 MB call is in flight at once anyway, so a common window
+    // buys nothing, and adjacent tiles measured ~3% faster); dense sweeps
+    // keep the grid-stride window.  QG_CONTIG=0/1 overrides (tuning sweeps).
+    static const int env_contig = [] {
+        const char* e = getenv("QG_CONTIG");
+        return e ? int(strtol(e, nullptr, 10)) : -1;
+    }();
+    const bool contig = env_contig >= 0 ? env_contig != 0 : a.grouped;
+    kp.contig_k = contig ? k : 0;
+    static const int env_shape = [] {
+        const char* e = getenv("QG_SHAPE");   // tuning sweeps only
+        return e ? int(strtol(e, nullptr, 10)) : -1;
+    }();
+    if (env_shape == SHAPE_D2_W4 || env_shape == SHAPE_D4_W4) shape = env_shape;
+    const size_t lds = lds_bytes_for(L, a.m);
+    const hipStream_t s = a.stream;
+    const int64_t w = waves_per_slot;
+    switch (L.fmt) {
+    case FMT_Q8G64: return launch_q8g64(a.m, a.grouped, L.G, shape, kp, w, slots, lds, s);
+    case FMT_Q4G32: return launch_q4g32(a.m, a.grouped, L.G, shape, kp, w, slots, lds, s);
+    case FMT_Q8G128: return launch_q8g128(a.m, a.grouped, L.G, shape, kp, w, slots, lds, s);
+    case FMT_Q8PC: return launch_q8pc(a.m, a.grouped, L.G, shape, kp, w, slots, lds, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qg

@@ -61,15 +61,100 @@ inline int64_t code_off(const qg::Layout& L, int64_t t, int64_t j, int r, int la
     return ((t * L.J + j) * L.R + r) * 1024 + int64_t(lane) * 16;
 }
 
-inline int64_t meta_off_q8(const qg::Layout& L, int64_t t, int64_t j, int r, int rho, int a)
+// Start of the meta of (tile t, step j).
+inline int64_t meta_base(const qg::Layout& L, int64_t t, int64_t j)
 {
-    return L.code_bytes + (t * L.J + j) * L.meta_step_bytes +
-           ((int64_t(rho) * (L.G / 4) + a) * L.R + r) * 2;
+    return L.code_bytes + t * (L.J * L.meta_step_bytes + L.meta_tile_bytes) + j * L.meta_step_bytes;
+}
+
+// Grouped 8-bit formats: lanes_per_group lanes (4 for Q8G64, 8 for Q8G128)
+// share one fp16 scale per row slot.
+inline int64_t meta_off_q8(const qg::Layout& L, int64_t t, int64_t j, int r, int rho, int a,
+                           int lanes_per_group)
+{
+    return meta_base(L, t, j) + ((int64_t(rho) * (L.G / lanes_per_group) + a) * L.R + r) * 2;
 }
 
 inline int64_t meta_off_q4(const qg::Layout& L, int64_t t, int64_t j, int r, int lane)
 {
-    return L.code_bytes + (t * L.J + j) * L.meta_step_bytes + (int64_t(lane) * L.R + r) * 4;
+    return meta_base(L, t, j) + (int64_t(lane) * L.R + r) * 4;
+}
+
+// Q8PC: the tile's row scales follow its steps' (empty) meta, ordered [rho][r].
+inline int64_t meta_off_pc(const qg::Layout& L, int64_t t, int r, int rho)
+{
+    return meta_base(L, t, L.J) + (int64_t(rho) * L.R + r) * 4;
+}
+
+// Packs any 8-bit-code format: codes biased to q+128, then the format's scales.
+// scales: fp16 [N][K/group] for the grouped formats, fp32 bit patterns [N] for Q8PC.
+qg_status pack_q8(int fmt, const int8_t* q, const void* scales, int64_t N, int64_t K, void* out,
+                  size_t out_bytes)
+{
+    qg::Layout L;
+    if (!q || !scales || !out) return QG_ERR_INVALID_ARG;
+    if (!qg::make_layout(fmt, N, K, &L)) return QG_ERR_INVALID_ARG;
+    if (out_bytes < size_t(L.total_bytes)) return QG_ERR_INVALID_ARG;
+    uint8_t* o = static_cast<uint8_t*>(out);
+    // Padding rows: code byte 0x80 (q = 0 after the +128 bias), scale 0.
+    memset(o, 0x80, size_t(L.code_bytes));
+    memset(o + L.code_bytes, 0, size_t(L.total_bytes - L.code_bytes));
+    const int lanes_per_group = fmt == qg::FMT_Q8G128 ? 8 : 4;
+    const int64_t groups = K / L.group;
+    const uint16_t* s16 = static_cast<const uint16_t*>(scales);
+    const uint32_t* s32 = static_cast<const uint32_t*>(scales);
+    for (int64_t t = 0; t < L.tiles; ++t)
+        for (int64_t j = 0; j < L.J; ++j)
+            for (int r = 0; r < L.R; ++r)
+                for (int lane = 0; lane < 64; ++lane) {
+                    const int g = lane % L.G, rho = lane / L.G;
+                    const int64_t n = row_of(L, t, r, rho);
+                    if (n >= N) continue;
+                    const int64_t u = j * L.G + g;
+                    const int8_t* src = q + n * K + u * 16;
+                    uint8_t* dst = o + code_off(L, t, j, r, lane);
+                    for (int b = 0; b < 16; ++b) dst[b] = uint8_t(int(src[b]) + 128);
+                    if (fmt == qg::FMT_Q8PC) {
+                        if (j == 0 && g == 0) memcpy(o + meta_off_pc(L, t, r, rho), &s32[n], 4);
+                    } else if (g % lanes_per_group == 0) {
+                        const uint16_t sv = s16[n * groups + (u * 16) / L.group];
+                        memcpy(o + meta_off_q8(L, t, j, r, rho, g / lanes_per_group, lanes_per_group),
+                               &sv, 2);
+                    }
+                }
+    return QG_OK;
+}
+
+qg_status unpack_q8(int fmt, const void* packed, size_t packed_bytes, int64_t N, int64_t K, int8_t* q,
+                    void* scales)
+{
+    qg::Layout L;
+    if (!packed || !q || !scales) return QG_ERR_INVALID_ARG;
+    if (!qg::make_layout(fmt, N, K, &L)) return QG_ERR_INVALID_ARG;
+    if (packed_bytes < size_t(L.total_bytes)) return QG_ERR_INVALID_ARG;
+    const uint8_t* p = static_cast<const uint8_t*>(packed);
+    const int lanes_per_group = fmt == qg::FMT_Q8G128 ? 8 : 4;
+    const int64_t groups = K / L.group;
+    uint16_t* s16 = static_cast<uint16_t*>(scales);
+    uint32_t* s32 = static_cast<uint32_t*>(scales);
+    for (int64_t t = 0; t < L.tiles; ++t)
+        for (int64_t j = 0; j < L.J; ++j)
+            for (int r = 0; r < L.R; ++r)
+                for (int lane = 0; lane < 64; ++lane) {
+                    const int g = lane % L.G, rho = lane / L.G;
+                    const int64_t n = row_of(L, t, r, rho);
+                    if (n >= N) continue;
+                    const int64_t u = j * L.G + g;
+                    const uint8_t* src = p + code_off(L, t, j, r, lane);
+                    for (int b = 0; b < 16; ++b) q[n * K + u * 16 + b] = int8_t(int(src[b]) - 128);
+                    if (fmt == qg::FMT_Q8PC) {
+                        if (j == 0 && g == 0) memcpy(&s32[n], p + meta_off_pc(L, t, r, rho), 4);
+                    } else if (g % lanes_per_group == 0) {
+                        memcpy(&s16[n * groups + (u * 16) / L.group],
+                               p + meta_off_q8(L, t, j, r, rho, g / lanes_per_group, lanes_per_group), 2);
+                    }
+                }
+    return QG_OK;
 }
 
 }  // namespace
@@ -91,57 +176,49 @@ size_t qpack_q4g32_size(int64_t N, int64_t K)
 qg_status qpack_q8g64(const int8_t* q, const uint16_t* scales_f16, int64_t N, int64_t K,
                       void* out, size_t out_bytes)
 {
-    qg::Layout L;
-    if (!q || !scales_f16 || !out) return QG_ERR_INVALID_ARG;
-    if (!qg::make_layout(qg::FMT_Q8G64, N, K, &L)) return QG_ERR_INVALID_ARG;
-    if (out_bytes < size_t(L.total_bytes)) return QG_ERR_INVALID_ARG;
-    uint8_t* o = static_cast<uint8_t*>(out);
-    // Padding rows: code byte 0x80 (q = 0 after the +128 bias), scale 0.
-    memset(o, 0x80, size_t(L.code_bytes));
-    memset(o + L.code_bytes, 0, size_t(L.total_bytes - L.code_bytes));
-    const int64_t groups = K / 64;
-    for (int64_t t = 0; t < L.tiles; ++t)
-        for (int64_t j = 0; j < L.J; ++j)
-            for (int r = 0; r < L.R; ++r)
-                for (int lane = 0; lane < 64; ++lane) {
-                    const int g = lane % L.G, rho = lane / L.G;
-                    const int64_t n = row_of(L, t, r, rho);
-                    if (n >= N) continue;
-                    const int64_t u = j * L.G + g;
-                    const int8_t* src = q + n * K + u * 16;
-                    uint8_t* dst = o + code_off(L, t, j, r, lane);
-                    for (int b = 0; b < 16; ++b) dst[b] = uint8_t(int(src[b]) + 128);
-                    if (g % 4 == 0) {
-                        const uint16_t s = scales_f16[n * groups + u / 4];
-                        memcpy(o + meta_off_q8(L, t, j, r, rho, g / 4), &s, 2);
-                    }
-                }
-    return QG_OK;
+    return pack_q8(qg::FMT_Q8G64, q, scales_f16, N, K, out, out_bytes);
 }
 
 qg_status qunpack_q8g64(const void* packed, size_t packed_bytes, int64_t N, int64_t K,
                         int8_t* q, uint16_t* scales_f16)
 {
+    return unpack_q8(qg::FMT_Q8G64, packed, packed_bytes, N, K, q, scales_f16);
+}
+
+size_t qpack_q8g128_size(int64_t N, int64_t K)
+{
     qg::Layout L;
-    if (!packed || !q || !scales_f16) return QG_ERR_INVALID_ARG;
-    if (!qg::make_layout(qg::FMT_Q8G64, N, K, &L)) return QG_ERR_INVALID_ARG;
-    if (packed_bytes < size_t(L.total_bytes)) return QG_ERR_INVALID_ARG;
-    const uint8_t* p = static_cast<const uint8_t*>(packed);
-    const int64_t groups = K / 64;
-    for (int64_t t = 0; t < L.tiles; ++t)
-        for (int64_t j = 0; j < L.J; ++j)
-            for (int r = 0; r < L.R; ++r)
-                for (int lane = 0; lane < 64; ++lane) {
-                    const int g = lane % L.G, rho = lane / L.G;
-                    const int64_t n = row_of(L, t, r, rho);
-                    if (n >= N) continue;
-                    const int64_t u = j * L.G + g;
-                    const uint8_t* src = p + code_off(L, t, j, r, lane);
-                    for (int b = 0; b < 16; ++b) q[n * K + u * 16 + b] = int8_t(int(src[b]) - 128);
-                    if (g % 4 == 0)
-                        memcpy(&scales_f16[n * groups + u / 4], p + meta_off_q8(L, t, j, r, rho, g / 4), 2);
-                }
-    return QG_OK;
+    return qg::make_layout(qg::FMT_Q8G128, N, K, &L) ? size_t(L.total_bytes) : 0;
+}
+
+qg_status qpack_q8g128(const int8_t* q, const uint16_t* scales_f16, int64_t N, int64_t K,
+                       void* out, size_t out_bytes)
+{
+    return pack_q8(qg::FMT_Q8G128, q, scales_f16, N, K, out, out_bytes);
+}
+
+qg_status qunpack_q8g128(const void* packed, size_t packed_bytes, int64_t N, int64_t K,
+                         int8_t* q, uint16_t* scales_f16)
+{
+    return unpack_q8(qg::FMT_Q8G128, packed, packed_bytes, N, K, q, scales_f16);
+}
+
+size_t qpack_q8pc_size(int64_t N, int64_t K)
+{
+    qg::Layout L;
+    return qg::make_layout(qg::FMT_Q8PC, N, K, &L) ? size_t(L.total_bytes) : 0;
+}
+
+qg_status qpack_q8pc(const int8_t* q, const float* scales_f32, int64_t N, int64_t K, void* out,
+                     size_t out_bytes)
+{
+    return pack_q8(qg::FMT_Q8PC, q, scales_f32, N, K, out, out_bytes);
+}
+
+qg_status qunpack_q8pc(const void* packed, size_t packed_bytes, int64_t N, int64_t K, int8_t* q,
+                       float* scales_f32)
+{
+    return unpack_q8(qg::FMT_Q8PC, packed, packed_bytes, N, K, q, scales_f32);
 }
 
 qg_status qpack_q4g32(const uint8_t* codes, const uint16_t* scales_f16, const uint16_t* mins_f16,

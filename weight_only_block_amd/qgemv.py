@@ -24,6 +24,8 @@ QG_ERR_HIP = 4
 FMT_Q8G64 = 0
 FMT_Q4G32 = 1
 FMT_GROUPED_Q4G32 = 2
+FMT_Q8G128 = 3
+FMT_Q8PC = 4
 
 _lib = None
 
@@ -50,6 +52,14 @@ def lib() -> ctypes.CDLL:
             "qpack_q8g64_size": ([i64, i64], sz),
             "qpack_q8g64": ([p, p, i64, i64, p, sz], st),
             "qunpack_q8g64": ([p, sz, i64, i64, p, p], st),
+            "qpack_q8g128_size": ([i64, i64], sz),
+            "qpack_q8g128": ([p, p, i64, i64, p, sz], st),
+            "qunpack_q8g128": ([p, sz, i64, i64, p, p], st),
+            "qpack_q8pc_size": ([i64, i64], sz),
+            "qpack_q8pc": ([p, p, i64, i64, p, sz], st),
+            "qunpack_q8pc": ([p, sz, i64, i64, p, p], st),
+            "qgemv_q8g128": ([p, p, p, i64, i64, i64, i64, i64, p], st),
+            "qgemv_q8pc": ([p, p, p, i64, i64, i64, i64, i64, p], st),
             "qpack_q4g32_size": ([i64, i64], sz),
             "qpack_q4g32": ([p, p, p, i64, i64, p, sz], st),
             "qunpack_q4g32": ([p, sz, i64, i64, p, p, p], st),
@@ -123,6 +133,62 @@ def qunpack_q8g64(packed: np.ndarray, N: int, K: int):
     return q, s
 
 
+def qpack_q8g128_size(N: int, K: int) -> int:
+    return int(lib().qpack_q8g128_size(N, K))
+
+
+def qpack_q8pc_size(N: int, K: int) -> int:
+    return int(lib().qpack_q8pc_size(N, K))
+
+
+def qpack_q8g128(q: np.ndarray, scales_f16: np.ndarray) -> np.ndarray:
+    """Canonical q [N][K] int8 and scales [N][K/128] fp16 bits -> packed uint8 buffer."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s = np.ascontiguousarray(scales_f16, dtype=np.uint16)
+    N, K = q.shape
+    size = qpack_q8g128_size(N, K)
+    if size == 0 or s.shape != (N, K // 128):
+        raise QGError(QG_ERR_INVALID_ARG, "qpack_q8g128")
+    out = np.empty(size, np.uint8)
+    _check(lib().qpack_q8g128(_np_ptr(q), _np_ptr(s), N, K, _np_ptr(out), size), "qpack_q8g128")
+    return out
+
+
+def qunpack_q8g128(packed: np.ndarray, N: int, K: int):
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    q = np.empty((N, K), np.int8)
+    s = np.empty((N, K // 128), np.uint16)
+    _check(lib().qunpack_q8g128(_np_ptr(packed), packed.nbytes, N, K, _np_ptr(q), _np_ptr(s)),
+           "qunpack_q8g128")
+    return q, s
+
+
+def qpack_q8pc(q: np.ndarray, scales_f32: np.ndarray) -> np.ndarray:
+    """Canonical q [N][K] int8 and one fp32 scale per row (float32 [N], or its
+    bit patterns as uint32) -> packed uint8 buffer."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s = np.ascontiguousarray(scales_f32)
+    if s.dtype != np.uint32:
+        s = np.ascontiguousarray(s, dtype=np.float32)
+    N, K = q.shape
+    size = qpack_q8pc_size(N, K)
+    if size == 0 or s.shape != (N,):
+        raise QGError(QG_ERR_INVALID_ARG, "qpack_q8pc")
+    out = np.empty(size, np.uint8)
+    _check(lib().qpack_q8pc(_np_ptr(q), _np_ptr(s), N, K, _np_ptr(out), size), "qpack_q8pc")
+    return out
+
+
+def qunpack_q8pc(packed: np.ndarray, N: int, K: int):
+    """-> (q [N][K] int8, scales as fp32 bit patterns uint32 [N])."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    q = np.empty((N, K), np.int8)
+    s = np.empty(N, np.uint32)
+    _check(lib().qunpack_q8pc(_np_ptr(packed), packed.nbytes, N, K, _np_ptr(q), _np_ptr(s)),
+           "qunpack_q8pc")
+    return q, s
+
+
 def qpack_q4g32(codes: np.ndarray, scales_f16: np.ndarray, mins_f16: np.ndarray) -> np.ndarray:
     """Canonical codes [N][K/2] (even k in the low nibble), scales and mins
     [N][K/32] fp16 bits -> packed uint8 buffer."""
@@ -183,6 +249,18 @@ def qgemv_q4g32(w_packed, x, y, N: int, K: int, m=None, ldx=None, ldy=None, stre
     return _dense("qgemv_q4g32", w_packed, x, y, N, K, m, ldx, ldy, stream, check)
 
 
+def qgemv_q8g128(w_packed, x, y, N: int, K: int, m=None, ldx=None, ldy=None, stream=None,
+                 check=True):
+    """As qgemv_q8g64 for Q8G128 weights packed by qpack_q8g128."""
+    return _dense("qgemv_q8g128", w_packed, x, y, N, K, m, ldx, ldy, stream, check)
+
+
+def qgemv_q8pc(w_packed, x, y, N: int, K: int, m=None, ldx=None, ldy=None, stream=None,
+               check=True):
+    """As qgemv_q8g64 for per-output-channel Q8 weights packed by qpack_q8pc."""
+    return _dense("qgemv_q8pc", w_packed, x, y, N, K, m, ldx, ldy, stream, check)
+
+
 def qgemv_grouped_q4g32(w_experts, expert_stride_bytes: int, n_experts: int, expert_ids, x,
                         x_slot_stride: int, y, y_slot_stride: int, N: int, K: int,
                         n_slots=None, stream=None, check=True):
@@ -233,6 +311,16 @@ def bound_q8g64(w_packed, x, y, N: int, K: int, m: int = 1, ldx=None, ldy=None, 
 def bound_q4g32(w_packed, x, y, N: int, K: int, m: int = 1, ldx=None, ldy=None, stream=None):
     """As bound_q8g64 for qgemv_q4g32."""
     return _bind("qgemv_q4g32", w_packed, x, y, N, K, m, ldx, ldy, stream)
+
+
+def bound_q8g128(w_packed, x, y, N: int, K: int, m: int = 1, ldx=None, ldy=None, stream=None):
+    """As bound_q8g64 for qgemv_q8g128."""
+    return _bind("qgemv_q8g128", w_packed, x, y, N, K, m, ldx, ldy, stream)
+
+
+def bound_q8pc(w_packed, x, y, N: int, K: int, m: int = 1, ldx=None, ldy=None, stream=None):
+    """As bound_q8g64 for qgemv_q8pc."""
+    return _bind("qgemv_q8pc", w_packed, x, y, N, K, m, ldx, ldy, stream)
 
 
 def _bind(fn_name, w_packed, x, y, N, K, m, ldx, ldy, stream):

@@ -14,6 +14,9 @@ Workload shapes (decode, one token, weights stored row-major [N][K]):
   lm_head       Q8G64 K=2560, N=151936 (vocabulary rows)
   moe_experts   Q4G32, 128 experts, gate/up 4096->1536, down 1536->4096,
                 8 distinct expert ids per token
+  lm_head_q8g128  the lm_head in Q8G128
+  w8a16_qwen3_14b_tp4  per-output-channel int8 (fp32 row scale) at Qwen3-14B
+                TP4 rank-local shapes
 Value distributions: int8 codes uniform in [-127, 127]; 4-bit codes uniform
 in 0..15; scales uniform in [1e-3, 2e-2] then fp16; Q4 mins uniform in
 [-0.1, 0] then fp16; activations N(0, 1) float32 then bf16.
@@ -57,6 +60,22 @@ def q8g64_weights(rng: np.random.Generator, N: int, K: int):
     return q, s
 
 
+def q8g128_weights(rng: np.random.Generator, N: int, K: int):
+    """(q [N][K] int8 in [-127,127], scale [N][K/128] fp16 bits)."""
+    q = rng.integers(-127, 128, size=(N, K), dtype=np.int8)
+    s = to_fp16_bits(rng.uniform(1e-3, 2e-2, size=(N, K // 128)))
+    return q, s
+
+
+def q8pc_weights(rng: np.random.Generator, N: int, K: int):
+    """(q [N][K] int8 in [-127,127], scale [N] as fp32 bit patterns).  A
+    per-output-channel symmetric scale spans the row's whole range, so it is
+    drawn from the same interval as the group scales."""
+    q = rng.integers(-127, 128, size=(N, K), dtype=np.int8)
+    s = rng.uniform(1e-3, 2e-2, size=N).astype(np.float32).view(np.uint32)
+    return q, s
+
+
 def q4g32_weights(rng: np.random.Generator, N: int, K: int):
     """(codes [N][K/2] packed, scale [N][K/32] fp16 bits, min [N][K/32] fp16 bits)."""
     c = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
@@ -93,15 +112,35 @@ Q4_K2560 = [
     ("down", "q4g32", 2560, 9216),
 ]
 LM_HEAD = ("lm_head", "q8g64", 151936, 2560)
+# Per-output-channel W8A16 at Qwen3-14B TP4 rank-local decode shapes:
+# QKV 5120->1792, O 1280->5120, gate/up 5120->8704, down 4352->5120.
+W8A16_QWEN3_14B_TP4 = [
+    ("qkv", "q8pc", 1792, 5120),
+    ("o", "q8pc", 5120, 1280),
+    ("gate", "q8pc", 8704, 5120),
+    ("up", "q8pc", 8704, 5120),
+    ("down", "q8pc", 5120, 4352),
+]
 MOE = {"n_experts": 128, "n_slots": 8,
        "gate": (1536, 4096), "up": (1536, 4096), "down": (4096, 1536)}
 
-WORKLOAD_IDS = {"q8_small": 0, "qwen3_0.6b": 1, "q4_k2560": 2, "lm_head": 3, "moe_experts": 4}
+WORKLOAD_IDS = {"q8_small": 0, "qwen3_0.6b": 1, "q4_k2560": 2, "lm_head": 3, "moe_experts": 4,
+                "lm_head_q8g128": 5, "w8a16_qwen3_14b_tp4": 6}
 
 
 def bytes_q8g64(N: int, K: int) -> int:
     """Algorithmic weight bytes: int8 codes plus one fp16 scale per 64."""
     return N * K + 2 * N * (K // Q8_GROUP)
+
+
+def bytes_q8g128(N: int, K: int) -> int:
+    """Algorithmic weight bytes: int8 codes plus one fp16 scale per 128."""
+    return N * K + 2 * N * (K // 128)
+
+
+def bytes_q8pc(N: int, K: int) -> int:
+    """Algorithmic weight bytes: int8 codes plus one fp32 scale per row."""
+    return N * K + 4 * N
 
 
 def bytes_q4g32(N: int, K: int) -> int:
