@@ -41,7 +41,7 @@ TRAFFIC = {
 
 
 KERNEL_SOURCES = ("kernel_body.h", "kern_q8g64.hip", "kern_q4g32.hip", "kern_q8g128.hip",
-                  "kern_q8pc.hip", "launch.hip", "layout.h", "launch.h")
+                  "kern_q8pc.hip", "kern_q4g32_swiglu.hip", "launch.hip", "layout.h", "launch.h")
 
 
 def kernel_source_digest():
@@ -304,6 +304,48 @@ def setup_moe_merged(torch, Q, synth, id_sets=256):
     return step, weight_bytes + io_bytes, weight_bytes, 2, info, None
 
 
+def setup_moe_swiglu(torch, Q, synth, id_sets=256):
+    """Routed experts as a decode step runs them with the fused epilogue: one
+    grouped call over gate/up pair buffers that writes bf16 silu(g) * u,
+    then the grouped down call reading that activation."""
+    n_exp, n_slots = synth.MOE["n_experts"], synth.MOE["n_slots"]
+    wid = synth.WORKLOAD_IDS["moe_experts"]
+    Ng, Kg = synth.MOE["gate"]
+    Nd, Kd = synth.MOE["down"]
+    s_gu, s_dn = Q.gate_up_expert_stride(Ng, Kg), Q.expert_stride(Nd, Kd)
+    buf_gu = torch.empty(n_exp * s_gu, dtype=torch.uint8, device="cuda")
+    buf_dn = torch.empty(n_exp * s_dn, dtype=torch.uint8, device="cuda")
+    for e in range(n_exp):
+        g = synth.q4g32_weights(synth.rng_for(wid, 0, e), Ng, Kg)
+        u = synth.q4g32_weights(synth.rng_for(wid, 1, e), Ng, Kg)
+        buf_gu[e * s_gu:(e + 1) * s_gu].copy_(torch.from_numpy(Q.qpack_q4g32_gate_up(g, u)))
+        d = synth.q4g32_weights(synth.rng_for(wid, 2, e), Nd, Kd)
+        buf_dn[e * s_dn:(e + 1) * s_dn].copy_(torch.from_numpy(Q.qpack_q4g32(*d)))
+    ids = np.stack([synth.expert_ids(synth.rng_for(wid, 1000, t), n_exp, n_slots)
+                    for t in range(id_sets)])
+    ids_d = dev(torch, ids)
+    x_tok = dev(torch, synth.activations(synth.rng_for(wid, 2000), 1, Kg))
+    act = torch.empty((n_slots, Ng), dtype=torch.int16, device="cuda")
+    y_dn = torch.empty((n_slots, Nd), dtype=torch.float32, device="cuda")
+    calls = [(Q.bound_grouped_q4g32_swiglu(buf_gu, s_gu, n_exp, ids_d[t], x_tok, 0, act, Ng, Ng, Kg),
+              Q.bound_grouped_q4g32(buf_dn, s_dn, n_exp, ids_d[t], act, Kd, y_dn, Nd, Nd, Kd))
+             for t in range(id_sets)]
+
+    def step(i):
+        a, b = calls[i % id_sets]
+        a()
+        b()
+
+    weight_bytes = n_slots * (2 * synth.bytes_q4g32(Ng, Kg) + synth.bytes_q4g32(Nd, Kd))
+    io_bytes = (2 * Kg + 2 * n_slots * Ng) + (2 * n_slots * Kd + 4 * n_slots * Nd)
+    info = {"workload": "routed-expert decode, Q4G32, 128 experts, 8 per token: gate/up "
+                        "4096->2x1536 with fused SwiGLU (bf16 out), then down 1536->4096",
+            "format": "q4g32", "m": 1, "experts": n_exp, "slots": n_slots, "period": id_sets,
+            "kernel": [Q.variant_name(Q.FMT_GROUPED_Q4G32_SWIGLU, 1, Ng, Kg),
+                       Q.variant_name(Q.FMT_GROUPED_Q4G32, 1, Nd, Kd)]}
+    return step, weight_bytes + io_bytes, weight_bytes, 2, info, None
+
+
 def cpu_moe(oracle, cpu, threads, reps, synth):
     # The oracle on one token's eight routed experts (gate, up, down).
     ex = cpu["experts"]
@@ -333,7 +375,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="lm_head",
                     choices=["lm_head", "lm_head_q8g128", "moe_experts", "moe_experts_merged",
-                             "q8_small", "qwen3_0.6b", "q4_k2560", "w8a16_qwen3_14b_tp4"])
+                             "moe_experts_swiglu", "q8_small", "qwen3_0.6b", "q4_k2560", "w8a16_qwen3_14b_tp4"])
     ap.add_argument("--m", type=int, default=1,
                     help="activation rows (q4_k2560 and w8a16_qwen3_14b_tp4)")
     ap.add_argument("--graph", action="store_true",
@@ -376,6 +418,8 @@ def main():
             step, alg, wbytes, launches, info, cpu = setup_moe(torch, Q, synth)
         elif name == "moe_experts_merged":
             step, alg, wbytes, launches, info, cpu = setup_moe_merged(torch, Q, synth)
+        elif name == "moe_experts_swiglu":
+            step, alg, wbytes, launches, info, cpu = setup_moe_swiglu(torch, Q, synth)
         else:
             step, alg, wbytes, launches, info, cpu = setup_dense(torch, Q, synth, name, args.m)
         log("setup %s: %.1f s" % (name, time.time() - t0))

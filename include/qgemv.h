@@ -105,6 +105,24 @@ qg_status qpack_q4g32(const uint8_t *codes, const uint16_t *scales_f16,
 qg_status qunpack_q4g32(const void *packed, size_t packed_bytes, int64_t N, int64_t K,
                         uint8_t *codes, uint16_t *scales_f16, uint16_t *mins_f16);
 
+/* Gate/up pair packing for qgemv_grouped_q4g32_swiglu: the gate and up
+ * projections of one expert (each N x K, Q4G32, canonical as above) in one
+ * buffer whose tiles hold matching gate and up rows side by side, so the
+ * kernel that ends a tile holds both halves of each output.  This is the
+ * row-stacked gate+up matrix of the merged gate_up GEMM in the commit log of
+ * vllm.cpp pull request #1936 (rows are independent, so stacking them keeps
+ * every row's result), interleaved in blocks of rows instead of appended.
+ * Size rules as qpack_q4g32 (K % 32 == 0). */
+size_t    qpack_q4g32_gate_up_size(int64_t N, int64_t K);
+qg_status qpack_q4g32_gate_up(const uint8_t *gate_codes, const uint16_t *gate_scales_f16,
+                              const uint16_t *gate_mins_f16, const uint8_t *up_codes,
+                              const uint16_t *up_scales_f16, const uint16_t *up_mins_f16,
+                              int64_t N, int64_t K, void *out, size_t out_bytes);
+qg_status qunpack_q4g32_gate_up(const void *packed, size_t packed_bytes, int64_t N, int64_t K,
+                                uint8_t *gate_codes, uint16_t *gate_scales_f16,
+                                uint16_t *gate_mins_f16, uint8_t *up_codes,
+                                uint16_t *up_scales_f16, uint16_t *up_mins_f16);
+
 /* ------------------------------------------------------------------- GEMV
  * y[i*ldy + n] = sum_k W[n][k] * x[i*ldx + k] for 0 <= i < m, 0 <= n < N.
  *   w_packed  device, qpack_*_size(N, K) bytes from qpack_*, 256-B aligned
@@ -157,17 +175,45 @@ qg_status qgemv_grouped_q4g32(const void *w_experts_packed, int64_t expert_strid
                               float *y, int64_t y_slot_stride, int64_t N, int64_t K,
                               void *hip_stream);
 
+/* Routed-expert gate+up projection with the SwiGLU activation fused into
+ * its epilogue (one token, several experts), Q4G32:
+ *   for each slot j < n_slots, with e = expert_ids_dev[j] and x_j the slot's
+ *   activation,
+ *     g = Gate_e x_j,  u = Up_e x_j  (fp32, computed as qgemv_grouped_q4g32)
+ *     act[j*act_slot_stride + n] = bf16( silu(g[n]) * u[n] ),
+ *     silu(z) = z / (1 + exp(-z)),  rounded to nearest even
+ *   for 0 <= n < N.  act is laid out as the activation input of the down
+ *   projection's grouped call (x_slot_stride = act_slot_stride).  The
+ *   "packed Gate/Up GEMM, then one kernel computes SwiGLU and writes the
+ *   down projection's input" step is from the Qwen3 C++ Reference Runtime
+ *   (MetaInfer-cpp) README, milestone M6.5-D; here the GEMV and the
+ *   activation are one kernel and g, u never reach memory.
+ *   w_gate_up_packed  device, n_experts buffers from qpack_q4g32_gate_up
+ *                     (this N, K), buffer e at byte offset
+ *                     e * expert_stride_bytes; 256-B aligned
+ *   expert_stride_bytes  multiple of 256, >= qpack_q4g32_gate_up_size(N, K)
+ *   expert_ids_dev    as qgemv_grouped_q4g32; a slot with an id outside
+ *                     [0, n_experts) reads no weights and gets NaN (0x7FC0)
+ *   act_bf16          device bf16, 2-byte aligned; act_slot_stride >= N
+ *   n_slots, x_bf16, x_slot_stride, K: as qgemv_grouped_q4g32. */
+qg_status qgemv_grouped_q4g32_swiglu(const void *w_gate_up_packed, int64_t expert_stride_bytes,
+                                     int32_t n_experts, const int32_t *expert_ids_dev,
+                                     int32_t n_slots, const uint16_t *x_bf16,
+                                     int64_t x_slot_stride, uint16_t *act_bf16,
+                                     int64_t act_slot_stride, int64_t N, int64_t K,
+                                     void *hip_stream);
+
 /* ------------------------------------------------------------- test hooks
  * Every successful qgemv_* call bumps the counter of the kernel variant it
- * launched.  Variant names: "<fmt>[_grouped]_m<m>_g<G>_r<R>" with fmt one of
- * q8g64, q4g32, q8g128, q8pc, e.g. "q8g64_m1_g32_r2".  qg_route_count
+ * launched.  Variant names: "<fmt>[_grouped[_swiglu]]_m<m>_g<G>_r<R>" with fmt
+ * one of q8g64, q4g32, q8g128, q8pc, e.g. "q8g64_m1_g32_r2".  qg_route_count
  * returns 0 for unknown names. */
 void     qg_route_counts_reset(void);
 uint64_t qg_route_count(const char *variant);
 /* Writes the name of the variant qgemv_* would launch for (fmt, m, N, K)
  * into buf (fmt 0 = Q8G64, 1 = Q4G32, 2 = grouped Q4G32, 3 = Q8G128,
- * 4 = Q8PC).  Returns QG_OK or the status the call itself would return for
- * that shape. */
+ * 4 = Q8PC, 5 = grouped Q4G32 with SwiGLU, N = gate rows).  Returns QG_OK or
+ * the status the call itself would return for that shape. */
 qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char *buf, size_t buf_len);
 
 #ifdef __cplusplus

@@ -4,11 +4,13 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
 its Python binding) never imports it, and it imports nothing from the product.
 
-The arithmetic lives in ``oracle.c`` (plain C, fp64 decode and fp64
-accumulation in ascending k).  This module only marshals numpy arrays into
-it, splits output rows across threads when asked (each thread runs the same
-plain loop on its own rows, so the result does not depend on the split), and
-loops over expert slots for the routed-expert case.
+The GEMV arithmetic lives in ``oracle.c`` (plain C, fp64 decode and fp64
+accumulation in ascending k).  This module marshals numpy arrays into it,
+splits output rows across threads when asked (each thread runs the same
+plain loop on its own rows, so the result does not depend on the split),
+loops over expert slots for the routed-expert case, and applies the SwiGLU
+activation (elementwise fp64 numpy, ``silu`` / ``swiglu`` below) to the
+GEMV results for the fused gate+up call.
 
 Every function is pinned by ``tests/test_oracle_pins.py``.
 """
@@ -222,3 +224,73 @@ def within_tolerance(y_test, y_ref, a_ref, rel: float = 2e-3):
     evaluated in fp64; y must be finite.  Returns a boolean mask."""
     y_test = np.asarray(y_test, np.float64)
     return np.isfinite(y_test) & (np.abs(y_test - y_ref) <= rel * a_ref)
+
+
+# ------------------------------------------------------------------ SwiGLU
+#
+# The merged gate+up projection of a routed expert is followed by SwiGLU,
+# act = silu(gate) * up, which becomes the down projection's input (Qwen3
+# C++ Reference Runtime (MetaInfer-cpp) README, milestone M6.5-D; the
+# SiluAndMul step after the merged gate_up GEMM in the commit log of
+# vllm.cpp pull request #1936).  Neither page spells out SiLU; the reading
+# taken is the standard one, silu(z) = z * sigmoid(z) = z / (1 + e^-z).
+
+# Upper bound of |silu'(z)| over all real z.  silu'(z) = s (1 + z (1 - s))
+# with s = sigmoid(z) peaks at z ~= 2.3994 with value ~= 1.09984.
+SILU_SLOPE_BOUND = 1.0999
+
+
+def silu(z):
+    """silu(z) = z / (1 + exp(-z)) in fp64, written so that exp never
+    overflows: for z < 0 it is z e^z / (1 + e^z)."""
+    z = np.asarray(z, np.float64)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = z[pos] / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = z[~pos] * ez / (1.0 + ez)
+    return out
+
+
+def swiglu(gate, up):
+    """act = silu(gate) * up, elementwise, fp64."""
+    return silu(gate) * np.asarray(up, np.float64)
+
+
+def grouped_q4g32_swiglu(gate_experts, up_experts, ids, x_slots, threads: int = 1):
+    """Routed-expert gate+up with SwiGLU: for slot j with e = ids[j],
+    g = Gate_e x_j and u = Up_e x_j (the Q4G32 GEMV above), act = swiglu(g, u).
+
+    Returns (act, g, u, a_g, a_u), each float64 [n_slots][N]; a_g and a_u are
+    the sum_k |w x| of the two GEMVs (their tolerance scale)."""
+    g, a_g = grouped_q4g32(gate_experts, ids, x_slots, threads=threads)
+    u, a_u = grouped_q4g32(up_experts, ids, x_slots, threads=threads)
+    return swiglu(g, u), g, u, a_g, a_u
+
+
+def swiglu_propagated_bound(g, u, a_g, a_u, rel: float = 2e-3):
+    """How far silu(g') u' can move from silu(g) u when the fp32 gate/up sums
+    each meet the GEMV bar (|g' - g| <= rel a_g, |u' - u| <= rel a_u).
+
+    By the mean value theorem, with dg = rel a_g and du = rel a_u,
+      |silu(g')u' - silu(g)u| <= B |u'| dg + |silu(g)| du
+                               <= B dg (|u| + du) + |silu(g)| du =: E
+    with B = SILU_SLOPE_BOUND."""
+    dg = rel * np.asarray(a_g, np.float64)
+    du = rel * np.asarray(a_u, np.float64)
+    return SILU_SLOPE_BOUND * dg * (np.abs(u) + du) + np.abs(silu(g)) * du
+
+
+def swiglu_tolerance(act_ref, g, u, a_g, a_u, rel: float = 2e-3):
+    """Per-output bound on |act_test - act_ref| for a bf16 SwiGLU output built
+    from fp32 gate/up sums that each meet the GEMV bar.
+
+    The kernel forms t = silu(g') u' in fp32 (relative error below 2^-20 for
+    the exp, add, divide and multiply) and rounds t to bf16 (8 significant
+    bits: relative error up to 2^-8).  With E the propagated bound above,
+      |act - act_ref| <= E + 2^-20 |a'| + 2^-8 |t|
+                      <= (1 + 2^-7) E + (2^-8 + 2^-19) |act_ref|.
+    Results below the smallest normal bf16 may come out as zero (an fp32 exp
+    that overflows for very negative g), so 2^-126 is added."""
+    E = swiglu_propagated_bound(g, u, a_g, a_u, rel)
+    return (1.0 + 2.0 ** -7) * E + (2.0 ** -8 + 2.0 ** -19) * np.abs(act_ref) + 2.0 ** -126

@@ -18,8 +18,8 @@
 namespace {
 
 // Route counters: one per (kind, m, log2 G).  kind 0 Q8G64, 1 Q4G32,
-// 2 grouped Q4G32, 3 Q8G128, 4 Q8PC.
-constexpr int kKinds = 5, kMs = 4, kGs = 7;
+// 2 grouped Q4G32, 3 Q8G128, 4 Q8PC, 5 grouped Q4G32 with SwiGLU.
+constexpr int kKinds = 6, kMs = 4, kGs = 7;
 std::atomic<uint64_t> g_route[kKinds][kMs][kGs];
 
 int log2i(int v)
@@ -36,7 +36,8 @@ const char* kind_name(int kind)
     case 1: return "q4g32";
     case 2: return "q4g32_grouped";
     case 3: return "q8g128";
-    default: return "q8pc";
+    case 4: return "q8pc";
+    default: return "q4g32_grouped_swiglu";
     }
 }
 
@@ -67,6 +68,15 @@ qg_status check_shape(int fmt, int64_t m, int64_t N, int64_t K, qg::Layout* L)
     return QG_OK;
 }
 
+// Gate/up pair layout for N gate rows (same m = 1 LDS rule as the GEMV).
+qg_status check_gate_up(int64_t N, int64_t K, qg::Layout* L)
+{
+    int64_t rps;
+    if (!qg::make_gate_up_layout(N, K, L, &rps)) return QG_ERR_INVALID_ARG;
+    if (qg::lds_bytes_for(*L, 1) > qg::kMaxLdsBytes) return QG_ERR_UNSUPPORTED;
+    return QG_OK;
+}
+
 qg_status run_dense(int fmt, const void* w_packed, const uint16_t* x, float* y, int64_t m,
                     int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* stream)
 {
@@ -93,6 +103,10 @@ qg_status run_dense(int fmt, const void* w_packed, const uint16_t* x, float* y, 
     a.y = y;
     a.ldy = ldy;
     a.y_slot_stride = 0;
+    a.swiglu = false;
+    a.act = nullptr;
+    a.act_slot_stride = 0;
+    a.n_out = N;
     a.stream = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // clear a stale error so the check below is ours
     if (qg::launch(a) != hipSuccess) return QG_ERR_HIP;
@@ -175,10 +189,60 @@ qg_status qgemv_grouped_q4g32(const void* w_experts_packed, int64_t expert_strid
     a.y = y;
     a.ldy = N;
     a.y_slot_stride = y_slot_stride;
+    a.swiglu = false;
+    a.act = nullptr;
+    a.act_slot_stride = 0;
+    a.n_out = N;
     a.stream = static_cast<hipStream_t>(hip_stream);
     (void)hipGetLastError();
     if (qg::launch(a) != hipSuccess) return QG_ERR_HIP;
     g_route[2][0][log2i(L.G)].fetch_add(1, std::memory_order_relaxed);
+    return QG_OK;
+}
+
+qg_status qgemv_grouped_q4g32_swiglu(const void* w_gate_up_packed, int64_t expert_stride_bytes,
+                                     int32_t n_experts, const int32_t* expert_ids_dev,
+                                     int32_t n_slots, const uint16_t* x_bf16,
+                                     int64_t x_slot_stride, uint16_t* act_bf16,
+                                     int64_t act_slot_stride, int64_t N, int64_t K,
+                                     void* hip_stream)
+{
+    if (!w_gate_up_packed || !expert_ids_dev || !x_bf16 || !act_bf16) return QG_ERR_INVALID_ARG;
+    if (n_slots == 0) return QG_OK;
+    if (n_slots < 0 || n_slots > 64) return QG_ERR_UNSUPPORTED;
+    if (n_experts < 1) return QG_ERR_INVALID_ARG;
+    qg::Layout L;
+    const qg_status st = check_gate_up(N, K, &L);
+    if (st != QG_OK) return st;
+    if (expert_stride_bytes < L.total_bytes || x_slot_stride < 0 || act_slot_stride < N)
+        return QG_ERR_INVALID_ARG;
+    if (expert_stride_bytes % 256 != 0 || x_slot_stride % 2 != 0) return QG_ERR_ALIGNMENT;
+    if (!aligned(w_gate_up_packed, 256) || !aligned(x_bf16, 4) || !aligned(act_bf16, 2) ||
+        !aligned(expert_ids_dev, 4))
+        return QG_ERR_ALIGNMENT;
+    qg::LaunchArgs a;
+    a.layout = L;
+    a.grouped = true;
+    a.m = 1;
+    a.w = w_gate_up_packed;
+    a.expert_stride = expert_stride_bytes;
+    a.ids = expert_ids_dev;
+    a.n_experts = n_experts;
+    a.n_slots = n_slots;
+    a.x = x_bf16;
+    a.ldx = K;
+    a.x_slot_stride = x_slot_stride;
+    a.y = nullptr;
+    a.ldy = L.N;
+    a.y_slot_stride = 0;
+    a.swiglu = true;
+    a.act = act_bf16;
+    a.act_slot_stride = act_slot_stride;
+    a.n_out = N;
+    a.stream = static_cast<hipStream_t>(hip_stream);
+    (void)hipGetLastError();
+    if (qg::launch(a) != hipSuccess) return QG_ERR_HIP;
+    g_route[5][0][log2i(L.G)].fetch_add(1, std::memory_order_relaxed);
     return QG_OK;
 }
 
@@ -206,11 +270,11 @@ qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char* buf, s
 {
     if (!buf || buf_len == 0) return QG_ERR_INVALID_ARG;
     static const int kind_format[kKinds] = {qg::FMT_Q8G64, qg::FMT_Q4G32, qg::FMT_Q4G32,
-                                            qg::FMT_Q8G128, qg::FMT_Q8PC};
+                                            qg::FMT_Q8G128, qg::FMT_Q8PC, qg::FMT_Q4G32};
     if (fmt < 0 || fmt >= kKinds) return QG_ERR_INVALID_ARG;
-    if (fmt == 2 && m != 1) return QG_ERR_UNSUPPORTED;
+    if ((fmt == 2 || fmt == 5) && m != 1) return QG_ERR_UNSUPPORTED;
     qg::Layout L;
-    const qg_status st = check_shape(kind_format[fmt], m, N, K, &L);
+    const qg_status st = fmt == 5 ? check_gate_up(N, K, &L) : check_shape(kind_format[fmt], m, N, K, &L);
     if (st != QG_OK) return st;
     format_variant(fmt, int(m), L.G, buf, buf_len);
     return QG_OK;

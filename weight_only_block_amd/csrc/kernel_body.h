@@ -299,26 +299,47 @@ __device__ __forceinline__ float bit_add(float v)
 }
 
 // End of a tile: sum each of the V = R*M accumulators over the G lanes of its
-// row group (lane bits 0 .. log2 G - 1), then store.  With G >= 32 the top
-// lane bits are summed as a transpose: one swap + one add folds two
-// accumulators at once, after which lanes differ in which accumulator they
-// hold (bit 5 / bit 4 of the lane picks it).  The remaining bits are plain
-// butterflies (DPP inside a 16-lane row, swaps across rows).  Each sum is
-// then stored by the lanes whose untransposed group bits are zero.
+// row group (lane bits 0 .. log2 G - 1).  With G >= 32 the top lane bits are
+// summed as a transpose: one swap + one add folds two accumulators at once,
+// after which lanes differ in which accumulator they hold (bit 5 / bit 4 of
+// the lane picks it).  The remaining bits are plain butterflies (DPP inside
+// a 16-lane row, swaps across rows).  Each sum is then held by the lanes
+// whose untransposed group bits are zero.
 template <int M, int G, int R>
-__device__ __forceinline__ void finish_tile(float (&acc)[R][M], const KernelParams& p, float* y,
-                                            int64_t tile, int g, int rho, int lane)
-{
-    constexpr int RPS = 64 / G;
-    constexpr int TR = R * RPS;
-    constexpr int V = R * M;
-    constexpr int LOGG = G >= 64 ? 6 : G >= 32 ? 5 : G >= 16 ? 4 : G >= 8 ? 3 : G >= 4 ? 2 : G >= 2 ? 1 : 0;
-    constexpr bool T5 = LOGG == 6 && V % 2 == 0;                  // transpose on lane bit 5
-    constexpr int V1 = T5 ? V / 2 : V;
-    constexpr bool T4 = LOGG >= 5 && V1 % 2 == 0;                 // transpose on lane bit 4
-    constexpr int V2 = T4 ? V1 / 2 : V1;
+struct TileSums {
+    static constexpr int V = R * M;
+    static constexpr int LOGG = G >= 64 ? 6 : G >= 32 ? 5 : G >= 16 ? 4 : G >= 8 ? 3 : G >= 4 ? 2 : G >= 2 ? 1 : 0;
+    static constexpr bool T5 = LOGG == 6 && V % 2 == 0;        // transpose on lane bit 5
+    static constexpr int V1 = T5 ? V / 2 : V;
+    static constexpr bool T4 = LOGG >= 5 && V1 % 2 == 0;       // transpose on lane bit 4
+    static constexpr int V2 = T4 ? V1 / 2 : V1;
+    float v[V2];
 
-    float v0[V];
+    // Accumulator index (r * M + i) whose sum this lane holds in v[k].
+    __device__ __forceinline__ static int which(int k, int lane)
+    {
+        const int b5 = (lane >> 5) & 1, b4 = (lane >> 4) & 1;
+        if constexpr (T5 && T4) return 4 * k + 2 * b4 + b5;
+        else if constexpr (T5) return 2 * k + b5;
+        else if constexpr (T4) return 2 * k + b4;
+        else return k;
+    }
+
+    // Lanes that hold complete sums (one per row group and accumulator).
+    __device__ __forceinline__ static bool holder(int g)
+    {
+        int transposed_mask = 0;
+        if constexpr (T5) transposed_mask |= 32;
+        if constexpr (T4) transposed_mask |= 16;
+        return (g & ~transposed_mask) == 0;
+    }
+};
+
+template <int M, int G, int R>
+__device__ __forceinline__ void reduce_tile(float (&acc)[R][M], TileSums<M, G, R>& out)
+{
+    using TS = TileSums<M, G, R>;
+    float v0[TS::V];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -326,45 +347,93 @@ __device__ __forceinline__ void finish_tile(float (&acc)[R][M], const KernelPara
             v0[r * M + i] = acc[r][i];
             acc[r][i] = 0.0f;
         }
-    float v1[V1];
-    if constexpr (T5) {
+    float v1[TS::V1];
+    if constexpr (TS::T5) {
 #pragma unroll
-        for (int k = 0; k < V1; ++k) v1[k] = swap_add<5>(v0[2 * k], v0[2 * k + 1]);
+        for (int k = 0; k < TS::V1; ++k) v1[k] = swap_add<5>(v0[2 * k], v0[2 * k + 1]);
     } else {
 #pragma unroll
-        for (int k = 0; k < V1; ++k) v1[k] = LOGG == 6 ? bit_add<5>(v0[k]) : v0[k];
+        for (int k = 0; k < TS::V1; ++k) v1[k] = TS::LOGG == 6 ? bit_add<5>(v0[k]) : v0[k];
     }
-    float v2[V2];
-    if constexpr (T4) {
+    if constexpr (TS::T4) {
 #pragma unroll
-        for (int k = 0; k < V2; ++k) v2[k] = swap_add<4>(v1[2 * k], v1[2 * k + 1]);
+        for (int k = 0; k < TS::V2; ++k) out.v[k] = swap_add<4>(v1[2 * k], v1[2 * k + 1]);
     } else {
 #pragma unroll
-        for (int k = 0; k < V2; ++k) v2[k] = LOGG >= 5 ? bit_add<4>(v1[k]) : v1[k];
+        for (int k = 0; k < TS::V2; ++k) out.v[k] = TS::LOGG >= 5 ? bit_add<4>(v1[k]) : v1[k];
     }
 #pragma unroll
-    for (int k = 0; k < V2; ++k) {
-        if constexpr (LOGG >= 4) v2[k] = bit_add<3>(v2[k]);
-        if constexpr (LOGG >= 3) v2[k] = bit_add<2>(v2[k]);
-        if constexpr (LOGG >= 2) v2[k] = bit_add<1>(v2[k]);
-        if constexpr (LOGG >= 1) v2[k] = bit_add<0>(v2[k]);
+    for (int k = 0; k < TS::V2; ++k) {
+        if constexpr (TS::LOGG >= 4) out.v[k] = bit_add<3>(out.v[k]);
+        if constexpr (TS::LOGG >= 3) out.v[k] = bit_add<2>(out.v[k]);
+        if constexpr (TS::LOGG >= 2) out.v[k] = bit_add<1>(out.v[k]);
+        if constexpr (TS::LOGG >= 1) out.v[k] = bit_add<0>(out.v[k]);
     }
-    // Which accumulator this lane holds for slot k, and whether it stores.
-    const int b5 = (lane >> 5) & 1, b4 = (lane >> 4) & 1;
-    int transposed_mask = 0;
-    if constexpr (T5) transposed_mask |= 32;
-    if constexpr (T4) transposed_mask |= 16;
-    const bool storer = (g & ~transposed_mask) == 0;
+}
+
+// Reduces the tile and stores its fp32 sums.
+template <int M, int G, int R>
+__device__ __forceinline__ void finish_tile(float (&acc)[R][M], const KernelParams& p, float* y,
+                                            int64_t tile, int g, int rho, int lane)
+{
+    constexpr int RPS = 64 / G;
+    constexpr int TR = R * RPS;
+    TileSums<M, G, R> ts;
+    reduce_tile<M, G, R>(acc, ts);
+    const bool holder = TileSums<M, G, R>::holder(g);
 #pragma unroll
-    for (int k = 0; k < V2; ++k) {
-        int o;
-        if constexpr (T5 && T4) o = 4 * k + 2 * b4 + b5;
-        else if constexpr (T5) o = 2 * k + b5;
-        else if constexpr (T4) o = 2 * k + b4;
-        else o = k;
+    for (int k = 0; k < TileSums<M, G, R>::V2; ++k) {
+        const int o = TileSums<M, G, R>::which(k, lane);
         const int r = o / M, i = o - (o / M) * M;
         const int64_t row = tile * TR + r * RPS + rho;
-        if (storer && row < p.N) y[int64_t(i) * p.ldy + row] = v2[k];
+        if (holder && row < p.N) y[int64_t(i) * p.ldy + row] = ts.v[k];
+    }
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t to_bf16(float v)
+{
+    const uint32_t b = __float_as_uint(v);
+    if ((b & 0x7fffffffu) > 0x7f800000u) return uint16_t(0x7fc0);
+    return uint16_t((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
+}
+
+// Gate/up pair layout (layout.h): row slot 0 of a tile holds gate rows and
+// slot 1 the up rows with the same output indices.  After the reduction the
+// lane holding a gate sum fetches the matching up sum (from the lane that
+// differs in the transposed bit, or from its own second register when
+// nothing was transposed) and writes bf16(silu(g) * u).
+template <int G, int R>
+__device__ __forceinline__ void finish_tile_swiglu(float (&acc)[R][1], const KernelParams& p,
+                                                   uint16_t* act, int64_t tile, int g, int rho, int lane)
+{
+    static_assert(R == 2, "gate and up occupy the two row slots");
+    using TS = TileSums<1, G, R>;
+    constexpr int RPS = 64 / G;
+    TS ts;
+    reduce_tile<1, G, R>(acc, ts);
+    float gate, up;
+    bool writer = TS::holder(g);
+    if constexpr (TS::V2 == 1) {
+        // One transposed bit separates the gate lane (bit clear) from the up lane.
+        constexpr int BIT = TS::T5 ? 32 : 16;
+        const float other = __shfl_xor(ts.v[0], BIT, 64);
+        const bool is_up = (lane & BIT) != 0;
+        gate = is_up ? other : ts.v[0];
+        up = is_up ? ts.v[0] : other;
+        writer = writer && !is_up;
+    } else {
+        gate = ts.v[0];
+        up = ts.v[1];
+    }
+    const int64_t n = tile * RPS + rho;
+    if (writer && n < p.n_out) {
+        // sigmoid(g) from e = exp(-|g|) <= 1, so exp never overflows: for a
+        // very negative gate silu(g) = g e^g / (1 + e^g) stays a tiny
+        // nonzero number instead of g / inf.
+        const float e = expf(-fabsf(gate));
+        const float sig = (gate >= 0.0f ? 1.0f : e) / (1.0f + e);
+        act[n] = to_bf16(gate * sig * up);
     }
 }
 
@@ -376,7 +445,9 @@ __device__ __forceinline__ void finish_tile(float (&acc)[R][M], const KernelPara
 // matrix and measurably loses bandwidth.  Every wave gets the same number of
 // tiles up to one.  The work-group stages x once for its waves, and a ring of
 // DEPTH items in registers keeps up to DEPTH*R KiB of loads in flight per wave.
-template <int FMT, int M, int G, int R, int DEPTH, int WAVES, bool GROUPED>
+// EPI 0 stores fp32 sums; EPI 1 is the SwiGLU epilogue over gate/up pairs
+// (grouped Q4G32, m = 1 only).
+template <int FMT, int M, int G, int R, int DEPTH, int WAVES, bool GROUPED, int EPI>
 __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
 {
     constexpr int kWaves = WAVES;
@@ -418,7 +489,10 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
         my_tiles = gw < p.tiles ? (p.tiles - 1 - gw) / W + 1 : 0;
     }
     const int64_t n_items = my_tiles * p.J;
+    static_assert(EPI == 0 || (FMT == FMT_Q4G32 && M == 1 && GROUPED && R == 2),
+                  "the SwiGLU epilogue is built for grouped Q4G32 gate/up pairs");
     float* y = p.y + int64_t(slot) * p.y_slot_stride;
+    uint16_t* act = p.act + int64_t(slot) * p.act_slot_stride;
     const uint16_t* x = p.x + int64_t(slot) * p.x_slot_stride;
 
     // Activations first (see XStage), then the expert id, then the weights.
@@ -432,11 +506,19 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
             // Out-of-range expert id: read no weights, report NaN outputs.
             // The whole work-group takes this branch (e is per work-group),
             // so no barrier below is skipped by part of it.
-            for (int64_t n = 0, t = t0; n < my_tiles; ++n, t += tstep)
-                for (int idx = lane; idx < TR; idx += 64) {
-                    const int64_t row = t * TR + idx;
-                    if (row < p.N) y[row] = __builtin_nanf("");
+            for (int64_t n = 0, t = t0; n < my_tiles; ++n, t += tstep) {
+                if constexpr (EPI == 1) {
+                    for (int idx = lane; idx < RPS; idx += 64) {
+                        const int64_t row = t * RPS + idx;
+                        if (row < p.n_out) act[row] = uint16_t(0x7fc0);
+                    }
+                } else {
+                    for (int idx = lane; idx < TR; idx += 64) {
+                        const int64_t row = t * TR + idx;
+                        if (row < p.N) y[row] = __builtin_nanf("");
+                    }
                 }
+            }
             return;
         }
         w += int64_t(e) * p.expert_stride;
@@ -503,7 +585,8 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
 #define QG_ADVANCE()                                                                          \
     do {                                                                                      \
         if (++j == p.J) {                                                                     \
-            finish_tile<M, G, R>(acc, p, y, tile, g, rho, lane);                                    \
+            if constexpr (EPI == 1) finish_tile_swiglu<G, R>(acc, p, act, tile, g, rho, lane);      \
+            else finish_tile<M, G, R>(acc, p, y, tile, g, rho, lane);                               \
             tile += tstep;                                                                    \
             j = 0;                                                                            \
         }                                                                                     \
@@ -543,11 +626,11 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
 
 // Launch shape (launch.h): ring depth 2 or 4; work-groups are 4 waves.
 
-template <int FMT, int M, int G, int DEPTH, int WAVES, bool GROUPED>
+template <int FMT, int M, int G, int DEPTH, int WAVES, bool GROUPED, int EPI>
 hipError_t launch_variant(const KernelParams& kp, int64_t waves, int slots, size_t lds_bytes,
                           hipStream_t stream)
 {
-    auto kern = qgemv_stream<FMT, M, G, kRowSlots, DEPTH, WAVES, GROUPED>;
+    auto kern = qgemv_stream<FMT, M, G, kRowSlots, DEPTH, WAVES, GROUPED, EPI>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
         int(kMaxLdsBytes));
@@ -557,35 +640,35 @@ hipError_t launch_variant(const KernelParams& kp, int64_t waves, int slots, size
     return hipGetLastError();
 }
 
-template <int FMT, int M, int G, bool GROUPED>
+template <int FMT, int M, int G, bool GROUPED, int EPI>
 hipError_t launch_shape(int shape, const KernelParams& kp, int64_t waves, int slots, size_t lds,
                         hipStream_t s)
 {
     switch (shape) {
-    case SHAPE_D2_W4: return launch_variant<FMT, M, G, 2, 4, GROUPED>(kp, waves, slots, lds, s);
-    case SHAPE_D4_W4: return launch_variant<FMT, M, G, 4, 4, GROUPED>(kp, waves, slots, lds, s);
+    case SHAPE_D2_W4: return launch_variant<FMT, M, G, 2, 4, GROUPED, EPI>(kp, waves, slots, lds, s);
+    case SHAPE_D4_W4: return launch_variant<FMT, M, G, 4, 4, GROUPED, EPI>(kp, waves, slots, lds, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <int FMT, int M, bool GROUPED>
+template <int FMT, int M, bool GROUPED, int EPI>
 hipError_t launch_g(int G, int shape, const KernelParams& kp, int64_t waves, int slots, size_t lds,
                     hipStream_t s)
 {
     switch (G) {
-    case 64: return launch_shape<FMT, M, 64, GROUPED>(shape, kp, waves, slots, lds, s);
-    case 32: return launch_shape<FMT, M, 32, GROUPED>(shape, kp, waves, slots, lds, s);
-    case 16: return launch_shape<FMT, M, 16, GROUPED>(shape, kp, waves, slots, lds, s);
-    case 8: return launch_shape<FMT, M, 8, GROUPED>(shape, kp, waves, slots, lds, s);
+    case 64: return launch_shape<FMT, M, 64, GROUPED, EPI>(shape, kp, waves, slots, lds, s);
+    case 32: return launch_shape<FMT, M, 32, GROUPED, EPI>(shape, kp, waves, slots, lds, s);
+    case 16: return launch_shape<FMT, M, 16, GROUPED, EPI>(shape, kp, waves, slots, lds, s);
+    case 8: return launch_shape<FMT, M, 8, GROUPED, EPI>(shape, kp, waves, slots, lds, s);
     default: break;
     }
     if constexpr (FMT != FMT_Q8G128) {
-        if (G == 4) return launch_shape<FMT, M, 4, GROUPED>(shape, kp, waves, slots, lds, s);
+        if (G == 4) return launch_shape<FMT, M, 4, GROUPED, EPI>(shape, kp, waves, slots, lds, s);
     }
     if constexpr (FMT == FMT_Q4G32 || FMT == FMT_Q8PC) {
         switch (G) {
-        case 2: return launch_shape<FMT, M, 2, GROUPED>(shape, kp, waves, slots, lds, s);
-        case 1: return launch_shape<FMT, M, 1, GROUPED>(shape, kp, waves, slots, lds, s);
+        case 2: return launch_shape<FMT, M, 2, GROUPED, EPI>(shape, kp, waves, slots, lds, s);
+        case 1: return launch_shape<FMT, M, 1, GROUPED, EPI>(shape, kp, waves, slots, lds, s);
         default: break;
         }
     }
@@ -602,17 +685,24 @@ hipError_t launch_format(int m, bool grouped, int G, int shape, const KernelPara
 {
     if (grouped) {
         if constexpr (FMT == FMT_Q4G32) {
-            if (m == 1) return launch_g<FMT, 1, true>(G, shape, kp, waves, slots, lds, s);
+            if (m == 1) return launch_g<FMT, 1, true, 0>(G, shape, kp, waves, slots, lds, s);
         }
         return hipErrorInvalidValue;
     }
     switch (m) {
-    case 1: return launch_g<FMT, 1, false>(G, shape, kp, waves, slots, lds, s);
-    case 2: return launch_g<FMT, 2, false>(G, shape, kp, waves, slots, lds, s);
-    case 3: return launch_g<FMT, 3, false>(G, shape, kp, waves, slots, lds, s);
-    case 4: return launch_g<FMT, 4, false>(G, shape, kp, waves, slots, lds, s);
+    case 1: return launch_g<FMT, 1, false, 0>(G, shape, kp, waves, slots, lds, s);
+    case 2: return launch_g<FMT, 2, false, 0>(G, shape, kp, waves, slots, lds, s);
+    case 3: return launch_g<FMT, 3, false, 0>(G, shape, kp, waves, slots, lds, s);
+    case 4: return launch_g<FMT, 4, false, 0>(G, shape, kp, waves, slots, lds, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+// Grouped Q4G32 gate/up pairs with the SwiGLU epilogue (m = 1).
+inline hipError_t launch_swiglu(int G, int shape, const KernelParams& kp, int64_t waves, int slots,
+                                size_t lds, hipStream_t s)
+{
+    return launch_g<FMT_Q4G32, 1, true, 1>(G, shape, kp, waves, slots, lds, s);
 }
 
 }  // namespace qg

@@ -32,6 +32,9 @@ struct KernelParams {
     int64_t meta_step_bytes;
     int64_t meta_tile_bytes;   // per-tile meta after the steps' meta (Q8PC row scales)
     int64_t contig_k;          // > 0: each wave streams contig_k consecutive tiles
+    uint16_t* act;             // SwiGLU epilogue: bf16 output per slot
+    int64_t act_slot_stride;   // elements between slot outputs (SwiGLU)
+    int32_t n_out;             // outputs per slot (SwiGLU: gate rows)
 };
 
 // Launch shape: ring depth 2 or 4 items; work-groups are 4 waves.
@@ -52,6 +55,10 @@ struct LaunchArgs {
     float* y;
     int64_t ldy;
     int64_t y_slot_stride;
+    bool swiglu;               // gate/up pair layout with the SwiGLU epilogue
+    uint16_t* act;
+    int64_t act_slot_stride;
+    int64_t n_out;
     hipStream_t stream;
 };
 
@@ -71,5 +78,8 @@ QG_DECLARE_LAUNCHER(launch_q4g32);
 QG_DECLARE_LAUNCHER(launch_q8g128);
 QG_DECLARE_LAUNCHER(launch_q8pc);
 #undef QG_DECLARE_LAUNCHER
+// Grouped Q4G32 with the SwiGLU epilogue (kern_q4g32_swiglu.hip), m = 1.
+hipError_t launch_q4g32_swiglu(int G, int shape, const KernelParams& kp, int64_t waves, int slots,
+                               size_t lds, hipStream_t s);
 
 }  // namespace qg

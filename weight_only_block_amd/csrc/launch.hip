@@ -59,6 +59,9 @@ hipError_t launch(const LaunchArgs& a)
     kp.code_bytes = L.code_bytes;
     kp.meta_step_bytes = L.meta_step_bytes;
     kp.meta_tile_bytes = L.meta_tile_bytes;
+    kp.act = a.act;
+    kp.act_slot_stride = a.act_slot_stride;
+    kp.n_out = int32_t(a.n_out);
     const int slots = a.grouped ? a.n_slots : 1;
     // About target_waves waves in total (QG_TARGET_WAVES overrides it, for
     // tuning sweeps), never more waves than tiles; k tiles per wave, then the
@@ -99,6 +102,7 @@ hipError_t launch(const LaunchArgs& a)
     const size_t lds = lds_bytes_for(L, a.m);
     const hipStream_t s = a.stream;
     const int64_t w = waves_per_slot;
+    if (a.swiglu) return launch_q4g32_swiglu(L.G, shape, kp, w, slots, lds, s);
     switch (L.fmt) {
     case FMT_Q8G64: return launch_q8g64(a.m, a.grouped, L.G, shape, kp, w, slots, lds, s);
     case FMT_Q4G32: return launch_q4g32(a.m, a.grouped, L.G, shape, kp, w, slots, lds, s);

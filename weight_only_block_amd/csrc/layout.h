@@ -98,4 +98,24 @@ static inline bool make_layout(int fmt, int64_t N, int64_t K, Layout* L)
     return true;
 }
 
+// Gate/up pair layout (Q4G32 only), for a fused SwiGLU epilogue: the packed
+// matrix is an ordinary Q4G32 layout of Nv = 2 * ceil(N / RPS) * RPS rows
+// (RPS = 64 / G rows per row slot) in which tile t holds gate rows
+// t*RPS .. t*RPS + RPS - 1 in row slot 0 and the up rows with the same
+// indices in row slot 1, so one lane group ends a tile with both halves of
+// each output.  Rows past N are zero padding.  G depends on K alone, so the
+// N-row and Nv-row layouts share it.
+static_assert(kRowSlots == 2, "gate/up pairs occupy the two row slots of a tile");
+
+static inline bool make_gate_up_layout(int64_t N, int64_t K, Layout* L, int64_t* rows_per_slot)
+{
+    Layout l0;
+    if (!make_layout(FMT_Q4G32, N, K, &l0)) return false;
+    const int64_t rps = 64 / l0.G;
+    const int64_t Nv = 2 * ((N + rps - 1) / rps) * rps;
+    if (!make_layout(FMT_Q4G32, Nv, K, L) || L->G != l0.G) return false;
+    *rows_per_slot = rps;
+    return true;
+}
+
 }  // namespace qg

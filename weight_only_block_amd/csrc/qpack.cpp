@@ -157,6 +157,74 @@ qg_status unpack_q8(int fmt, const void* packed, size_t packed_bytes, int64_t N,
     return QG_OK;
 }
 
+// A canonical Q4G32 matrix (codes [N][K/2], scale and min [N][K/32]).  The
+// pointers are writable only for unpacking.
+struct Q4Rows {
+    const uint8_t* codes;
+    const uint16_t* scales;
+    const uint16_t* mins;
+};
+
+// Packs the rows of layout L; source(n, &row) names the canonical matrix and
+// row that packed row n comes from, or returns null for a padding row (code
+// 0, scale 0, min 0).
+template <class Source>
+void pack_q4(const qg::Layout& L, int64_t K, Source source, void* out)
+{
+    uint8_t* o = static_cast<uint8_t*>(out);
+    memset(o, 0, size_t(L.total_bytes));
+    const int64_t groups = K / 32;
+    for (int64_t t = 0; t < L.tiles; ++t)
+        for (int64_t j = 0; j < L.J; ++j)
+            for (int r = 0; r < L.R; ++r)
+                for (int lane = 0; lane < 64; ++lane) {
+                    const int g = lane % L.G, rho = lane / L.G;
+                    int64_t n;
+                    const Q4Rows* m = source(row_of(L, t, r, rho), &n);
+                    if (!m) continue;
+                    const int64_t u = j * L.G + g;
+                    q4_unit_pack(m->codes + n * (K / 2) + u * 16, o + code_off(L, t, j, r, lane));
+                    const uint32_t meta = uint32_t(m->scales[n * groups + u]) |
+                                          (uint32_t(m->mins[n * groups + u]) << 16);
+                    memcpy(o + meta_off_q4(L, t, j, r, lane), &meta, 4);
+                }
+}
+
+template <class Source>
+void unpack_q4(const qg::Layout& L, int64_t K, Source source, const void* packed)
+{
+    const uint8_t* p = static_cast<const uint8_t*>(packed);
+    const int64_t groups = K / 32;
+    for (int64_t t = 0; t < L.tiles; ++t)
+        for (int64_t j = 0; j < L.J; ++j)
+            for (int r = 0; r < L.R; ++r)
+                for (int lane = 0; lane < 64; ++lane) {
+                    const int g = lane % L.G, rho = lane / L.G;
+                    int64_t n;
+                    const Q4Rows* m = source(row_of(L, t, r, rho), &n);
+                    if (!m) continue;
+                    const int64_t u = j * L.G + g;
+                    q4_unit_unpack(p + code_off(L, t, j, r, lane),
+                                   const_cast<uint8_t*>(m->codes) + n * (K / 2) + u * 16);
+                    uint32_t meta;
+                    memcpy(&meta, p + meta_off_q4(L, t, j, r, lane), 4);
+                    const_cast<uint16_t*>(m->scales)[n * groups + u] = uint16_t(meta & 0xffff);
+                    const_cast<uint16_t*>(m->mins)[n * groups + u] = uint16_t(meta >> 16);
+                }
+}
+
+// Gate/up pair layout (layout.h): packed row v of tile t = v / (2 rps) is
+// gate row t*rps + (v mod rps) in the first rps rows of the tile and the up
+// row with that index in the next rps.
+inline const Q4Rows* gate_up_source(int64_t v, int64_t N, int64_t rps, const Q4Rows& gate,
+                                    const Q4Rows& up, int64_t* row)
+{
+    const int64_t t = v / (2 * rps), w = v % (2 * rps);
+    *row = t * rps + w % rps;
+    if (*row >= N) return nullptr;
+    return w < rps ? &gate : &up;
+}
+
 }  // namespace
 
 extern "C" {
@@ -228,22 +296,8 @@ qg_status qpack_q4g32(const uint8_t* codes, const uint16_t* scales_f16, const ui
     if (!codes || !scales_f16 || !mins_f16 || !out) return QG_ERR_INVALID_ARG;
     if (!qg::make_layout(qg::FMT_Q4G32, N, K, &L)) return QG_ERR_INVALID_ARG;
     if (out_bytes < size_t(L.total_bytes)) return QG_ERR_INVALID_ARG;
-    uint8_t* o = static_cast<uint8_t*>(out);
-    memset(o, 0, size_t(L.total_bytes));  // padding: code 0, scale 0, min 0
-    const int64_t groups = K / 32;
-    for (int64_t t = 0; t < L.tiles; ++t)
-        for (int64_t j = 0; j < L.J; ++j)
-            for (int r = 0; r < L.R; ++r)
-                for (int lane = 0; lane < 64; ++lane) {
-                    const int g = lane % L.G, rho = lane / L.G;
-                    const int64_t n = row_of(L, t, r, rho);
-                    if (n >= N) continue;
-                    const int64_t u = j * L.G + g;
-                    q4_unit_pack(codes + n * (K / 2) + u * 16, o + code_off(L, t, j, r, lane));
-                    const uint32_t meta = uint32_t(scales_f16[n * groups + u]) |
-                                          (uint32_t(mins_f16[n * groups + u]) << 16);
-                    memcpy(o + meta_off_q4(L, t, j, r, lane), &meta, 4);
-                }
+    const Q4Rows m{codes, scales_f16, mins_f16};
+    pack_q4(L, K, [&](int64_t n, int64_t* row) { *row = n; return n < N ? &m : nullptr; }, out);
     return QG_OK;
 }
 
@@ -254,22 +308,53 @@ qg_status qunpack_q4g32(const void* packed, size_t packed_bytes, int64_t N, int6
     if (!packed || !codes || !scales_f16 || !mins_f16) return QG_ERR_INVALID_ARG;
     if (!qg::make_layout(qg::FMT_Q4G32, N, K, &L)) return QG_ERR_INVALID_ARG;
     if (packed_bytes < size_t(L.total_bytes)) return QG_ERR_INVALID_ARG;
-    const uint8_t* p = static_cast<const uint8_t*>(packed);
-    const int64_t groups = K / 32;
-    for (int64_t t = 0; t < L.tiles; ++t)
-        for (int64_t j = 0; j < L.J; ++j)
-            for (int r = 0; r < L.R; ++r)
-                for (int lane = 0; lane < 64; ++lane) {
-                    const int g = lane % L.G, rho = lane / L.G;
-                    const int64_t n = row_of(L, t, r, rho);
-                    if (n >= N) continue;
-                    const int64_t u = j * L.G + g;
-                    q4_unit_unpack(p + code_off(L, t, j, r, lane), codes + n * (K / 2) + u * 16);
-                    uint32_t meta;
-                    memcpy(&meta, p + meta_off_q4(L, t, j, r, lane), 4);
-                    scales_f16[n * groups + u] = uint16_t(meta & 0xffff);
-                    mins_f16[n * groups + u] = uint16_t(meta >> 16);
-                }
+    const Q4Rows m{codes, scales_f16, mins_f16};
+    unpack_q4(L, K, [&](int64_t n, int64_t* row) { *row = n; return n < N ? &m : nullptr; }, packed);
+    return QG_OK;
+}
+
+size_t qpack_q4g32_gate_up_size(int64_t N, int64_t K)
+{
+    qg::Layout L;
+    int64_t rps;
+    return qg::make_gate_up_layout(N, K, &L, &rps) ? size_t(L.total_bytes) : 0;
+}
+
+qg_status qpack_q4g32_gate_up(const uint8_t* gate_codes, const uint16_t* gate_scales_f16,
+                              const uint16_t* gate_mins_f16, const uint8_t* up_codes,
+                              const uint16_t* up_scales_f16, const uint16_t* up_mins_f16,
+                              int64_t N, int64_t K, void* out, size_t out_bytes)
+{
+    qg::Layout L;
+    int64_t rps;
+    if (!gate_codes || !gate_scales_f16 || !gate_mins_f16 || !up_codes || !up_scales_f16 ||
+        !up_mins_f16 || !out)
+        return QG_ERR_INVALID_ARG;
+    if (!qg::make_gate_up_layout(N, K, &L, &rps)) return QG_ERR_INVALID_ARG;
+    if (out_bytes < size_t(L.total_bytes)) return QG_ERR_INVALID_ARG;
+    const Q4Rows gate{gate_codes, gate_scales_f16, gate_mins_f16};
+    const Q4Rows up{up_codes, up_scales_f16, up_mins_f16};
+    pack_q4(L, K, [&](int64_t v, int64_t* row) { return gate_up_source(v, N, rps, gate, up, row); },
+            out);
+    return QG_OK;
+}
+
+qg_status qunpack_q4g32_gate_up(const void* packed, size_t packed_bytes, int64_t N, int64_t K,
+                                uint8_t* gate_codes, uint16_t* gate_scales_f16,
+                                uint16_t* gate_mins_f16, uint8_t* up_codes,
+                                uint16_t* up_scales_f16, uint16_t* up_mins_f16)
+{
+    qg::Layout L;
+    int64_t rps;
+    if (!packed || !gate_codes || !gate_scales_f16 || !gate_mins_f16 || !up_codes ||
+        !up_scales_f16 || !up_mins_f16)
+        return QG_ERR_INVALID_ARG;
+    if (!qg::make_gate_up_layout(N, K, &L, &rps)) return QG_ERR_INVALID_ARG;
+    if (packed_bytes < size_t(L.total_bytes)) return QG_ERR_INVALID_ARG;
+    const Q4Rows gate{gate_codes, gate_scales_f16, gate_mins_f16};
+    const Q4Rows up{up_codes, up_scales_f16, up_mins_f16};
+    unpack_q4(L, K, [&](int64_t v, int64_t* row) { return gate_up_source(v, N, rps, gate, up, row); },
+              packed);
     return QG_OK;
 }
 

@@ -26,6 +26,7 @@ FMT_Q4G32 = 1
 FMT_GROUPED_Q4G32 = 2
 FMT_Q8G128 = 3
 FMT_Q8PC = 4
+FMT_GROUPED_Q4G32_SWIGLU = 5
 
 _lib = None
 
@@ -66,6 +67,10 @@ def lib() -> ctypes.CDLL:
             "qgemv_q8g64": ([p, p, p, i64, i64, i64, i64, i64, p], st),
             "qgemv_q4g32": ([p, p, p, i64, i64, i64, i64, i64, p], st),
             "qgemv_grouped_q4g32": ([p, i64, i32, p, i32, p, i64, p, i64, i64, i64, p], st),
+            "qpack_q4g32_gate_up_size": ([i64, i64], sz),
+            "qpack_q4g32_gate_up": ([p, p, p, p, p, p, i64, i64, p, sz], st),
+            "qunpack_q4g32_gate_up": ([p, sz, i64, i64, p, p, p, p, p, p], st),
+            "qgemv_grouped_q4g32_swiglu": ([p, i64, i32, p, i32, p, i64, p, i64, i64, i64, p], st),
             "qg_route_counts_reset": ([], None),
             "qg_route_count": ([ctypes.c_char_p], ctypes.c_uint64),
             "qg_variant_name": ([ctypes.c_int, i64, i64, i64, ctypes.c_char_p, sz], st),
@@ -216,6 +221,39 @@ def qunpack_q4g32(packed: np.ndarray, N: int, K: int):
     return codes, s, mn
 
 
+def qpack_q4g32_gate_up_size(N: int, K: int) -> int:
+    return int(lib().qpack_q4g32_gate_up_size(N, K))
+
+
+def qpack_q4g32_gate_up(gate, up) -> np.ndarray:
+    """gate and up: (codes [N][K/2], scales [N][K/32], mins [N][K/32]) of one
+    expert's two projections -> one packed gate/up pair buffer (uint8) for
+    qgemv_grouped_q4g32_swiglu."""
+    g = [np.ascontiguousarray(a, dtype=t) for a, t in zip(gate, (np.uint8, np.uint16, np.uint16))]
+    u = [np.ascontiguousarray(a, dtype=t) for a, t in zip(up, (np.uint8, np.uint16, np.uint16))]
+    N, half_k = g[0].shape
+    K = 2 * half_k
+    size = qpack_q4g32_gate_up_size(N, K)
+    shapes = [(N, half_k), (N, K // 32), (N, K // 32)]
+    if size == 0 or [a.shape for a in g] != shapes or [a.shape for a in u] != shapes:
+        raise QGError(QG_ERR_INVALID_ARG, "qpack_q4g32_gate_up")
+    out = np.empty(size, np.uint8)
+    _check(lib().qpack_q4g32_gate_up(*[_np_ptr(a) for a in g + u], N, K, _np_ptr(out), size),
+           "qpack_q4g32_gate_up")
+    return out
+
+
+def qunpack_q4g32_gate_up(packed: np.ndarray, N: int, K: int):
+    """-> (gate, up), each (codes, scales, mins) as qpack_q4g32_gate_up takes them."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    mats = [np.empty((N, K // 2), np.uint8), np.empty((N, K // 32), np.uint16),
+            np.empty((N, K // 32), np.uint16), np.empty((N, K // 2), np.uint8),
+            np.empty((N, K // 32), np.uint16), np.empty((N, K // 32), np.uint16)]
+    _check(lib().qunpack_q4g32_gate_up(_np_ptr(packed), packed.nbytes, N, K,
+                                       *[_np_ptr(a) for a in mats]), "qunpack_q4g32_gate_up")
+    return tuple(mats[:3]), tuple(mats[3:])
+
+
 # --------------------------------------------------------------------- GEMV
 
 def _dense(fn_name, w_packed, x, y, N, K, m=None, ldx=None, ldy=None, stream=None, check=True):
@@ -275,6 +313,26 @@ def qgemv_grouped_q4g32(w_experts, expert_stride_bytes: int, n_experts: int, exp
                                    y.data_ptr(), y_slot_stride, N, K, _stream_handle(stream))
     if check:
         _check(st, "qgemv_grouped_q4g32")
+    return st
+
+
+def qgemv_grouped_q4g32_swiglu(w_gate_up, expert_stride_bytes: int, n_experts: int, expert_ids,
+                               x, x_slot_stride: int, act, act_slot_stride: int, N: int, K: int,
+                               n_slots=None, stream=None, check=True):
+    """Routed-expert gate+up with the SwiGLU epilogue:
+    act[j*act_slot_stride + n] = bf16(silu(g[n]) * u[n]) with g, u the gate
+    and up projections of expert ids[j] applied to x[j*x_slot_stride:].
+
+    w_gate_up: device uint8 tensor of n_experts buffers from
+    qpack_q4g32_gate_up at expert_stride_bytes; act: device 16-bit tensor."""
+    if n_slots is None:
+        n_slots = expert_ids.numel()
+    st = lib().qgemv_grouped_q4g32_swiglu(w_gate_up.data_ptr(), expert_stride_bytes, n_experts,
+                                          expert_ids.data_ptr(), n_slots, x.data_ptr(),
+                                          x_slot_stride, act.data_ptr(), act_slot_stride, N, K,
+                                          _stream_handle(stream))
+    if check:
+        _check(st, "qgemv_grouped_q4g32_swiglu")
     return st
 
 
@@ -343,6 +401,19 @@ def bound_grouped_q4g32(w_experts, expert_stride_bytes: int, n_experts: int, exp
                      (w_experts, expert_ids, x, y))
 
 
+def bound_grouped_q4g32_swiglu(w_gate_up, expert_stride_bytes: int, n_experts: int, expert_ids,
+                               x, x_slot_stride: int, act, act_slot_stride: int, N: int, K: int,
+                               n_slots=None, stream=None):
+    """As bound_q8g64 for qgemv_grouped_q4g32_swiglu."""
+    if n_slots is None:
+        n_slots = expert_ids.numel()
+    args = (w_gate_up.data_ptr(), expert_stride_bytes, n_experts, expert_ids.data_ptr(), n_slots,
+            x.data_ptr(), x_slot_stride, act.data_ptr(), act_slot_stride, N, K,
+            _stream_handle(stream))
+    return BoundCall(lib().qgemv_grouped_q4g32_swiglu, args, "qgemv_grouped_q4g32_swiglu",
+                     (w_gate_up, expert_ids, x, act))
+
+
 # --------------------------------------------------------------- test hooks
 
 def route_counts_reset() -> None:
@@ -362,3 +433,8 @@ def variant_name(fmt: int, m: int, N: int, K: int) -> str:
 def expert_stride(N: int, K: int) -> int:
     """Smallest valid expert stride (packed size is already a multiple of 256)."""
     return qpack_q4g32_size(N, K)
+
+
+def gate_up_expert_stride(N: int, K: int) -> int:
+    """Smallest valid expert stride for gate/up pair buffers."""
+    return qpack_q4g32_gate_up_size(N, K)
