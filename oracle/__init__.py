@@ -10,7 +10,8 @@ splits output rows across threads when asked (each thread runs the same
 plain loop on its own rows, so the result does not depend on the split),
 loops over expert slots for the routed-expert case, and applies the SwiGLU
 activation (elementwise fp64 numpy, ``silu`` / ``swiglu`` below) to the
-GEMV results for the fused gate+up call.
+GEMV results for the fused gate+up call.  The greedy argmax over logits is a
+plain left-to-right scan in ``oracle.c``.
 
 Every function is pinned by ``tests/test_oracle_pins.py``.
 """
@@ -30,8 +31,10 @@ _lib = None
 
 
 def build(force: bool = False) -> str:
-    """Compile oracle.c into liboracle.so with gcc (no fast-math)."""
-    if force or not os.path.exists(_LIB):
+    """Compile oracle.c into liboracle.so with gcc (no fast-math); also when
+    the source is newer than the built library."""
+    stale = not os.path.exists(_LIB) or os.path.getmtime(_SRC) > os.path.getmtime(_LIB)
+    if force or stale:
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-std=c99",
                                "-fno-fast-math", "-o", tmp, _SRC, "-lm"])
@@ -59,6 +62,8 @@ def _load():
         lib.oracle_half_to_double.restype = ctypes.c_double
         lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_to_double.restype = ctypes.c_double
+        lib.oracle_argmax_f32.argtypes = [p, i64, i64, i64, p]
+        lib.oracle_argmax_f32.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -224,6 +229,26 @@ def within_tolerance(y_test, y_ref, a_ref, rel: float = 2e-3):
     evaluated in fp64; y must be finite.  Returns a boolean mask."""
     y_test = np.asarray(y_test, np.float64)
     return np.isfinite(y_test) & (np.abs(y_test - y_ref) <= rel * a_ref)
+
+
+# ------------------------------------------------------------------ argmax
+
+def argmax_f32(x) -> np.ndarray:
+    """Greedy choice per row of fp32 logits x [m][>=N] (float32 values or
+    their uint32 bit patterns; rows of length N = x.shape[1]): the index of
+    the largest value, the lowest index on ties, -0 == +0, and the first NaN
+    of a row if it has one.  Returns int64 [m]."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        x = x.view(np.uint32)
+    x = np.ascontiguousarray(x, dtype=np.uint32)
+    if x.ndim == 1:
+        x = x[None, :]
+    m, N = x.shape
+    out = np.zeros(m, np.int64)
+    if m and _load().oracle_argmax_f32(_ptr(x), m, N, N, _ptr(out)) != 0:
+        raise ValueError("bad argmax shape")
+    return out
 
 
 # ------------------------------------------------------------------ SwiGLU

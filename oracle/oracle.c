@@ -216,3 +216,33 @@ int oracle_q8pc(const int8_t *q, const uint32_t *scale, int64_t N, int64_t K,
     }
     return 0;
 }
+
+/* Greedy token choice over fp32 logits: for each row i < m, the index of the
+ * largest of x[i*ldx + 0 .. N-1], the lowest such index on ties.  This is
+ * the (value, lower index) rule of the split argmax in the commit log of
+ * vllm.cpp pull request #1936, which makes the choice independent of how a
+ * row is split.  Values are compared as the real numbers the fp32 bit
+ * patterns denote, so -0 and +0 tie.  A NaN counts as larger than every
+ * number, and the first NaN of a row wins (numpy.argmax does the same).
+ * A plain left-to-right scan, one row at a time. */
+int oracle_argmax_f32(const uint32_t *x, int64_t m, int64_t N, int64_t ldx, int64_t *out)
+{
+    if (m < 0 || N < 1 || ldx < N) return -1;
+    for (int64_t i = 0; i < m; ++i) {
+        int64_t best = 0;
+        double best_v = f32_bits_to_double(x[i * ldx]);
+        int best_nan = isnan(best_v);
+        for (int64_t n = 1; n < N && !best_nan; ++n) {
+            double v = f32_bits_to_double(x[i * ldx + n]);
+            if (isnan(v)) {
+                best = n;
+                best_nan = 1;
+            } else if (v > best_v) {
+                best = n;
+                best_v = v;
+            }
+        }
+        out[i] = best;
+    }
+    return 0;
+}

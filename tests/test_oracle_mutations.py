@@ -12,6 +12,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_argmax as argmax_pins
 from tests import test_oracle_pins as pins
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -37,6 +38,12 @@ MUTATIONS = {
                        "double s = f32_bits_to_double(scale[N - 1 - n]);"),
     "f32_exponent": ("expo - 150", "expo - 149"),
     "f32_implicit_one": ("(0x800000u + frac)", "(frac)"),
+    "argmax_last_on_ties": ("} else if (v > best_v) {", "} else if (v >= best_v) {"),
+    "argmax_ignores_nan": ("            if (isnan(v)) {", "            if (0) {"),
+    "argmax_scans_past_nan": ("for (int64_t n = 1; n < N && !best_nan; ++n)",
+                              "for (int64_t n = 1; n < N; ++n)"),
+    "argmax_row_stride": ("double v = f32_bits_to_double(x[i * ldx + n]);",
+                          "double v = f32_bits_to_double(x[n]);"),
 }
 
 PIN_TESTS = [
@@ -57,6 +64,9 @@ PIN_TESTS = [
     (pins.test_q8g128_equals_q8g64_with_duplicated_scales, False),
     (pins.test_q8pc_equals_q8g64_with_row_constant_scales, False),
     (pins.test_q8g128_one_hot_group_index, False),
+    (argmax_pins.test_argmax_hand_written_rows, False),
+    (lambda: argmax_pins.test_argmax_matches_numpy_on_random_rows(1000), False),
+    (argmax_pins.test_argmax_split_and_combine_gives_the_row_winner, False),
 ]
 
 
@@ -73,7 +83,8 @@ def test_pins_catch_planted_mistake(name, tmp_path, golden_dir):
     real = oracle._load()
     lib = ctypes.CDLL(str(so))
     for fn in ("oracle_q8g64", "oracle_q4g32", "oracle_q8g128", "oracle_q8pc",
-               "oracle_half_to_double", "oracle_bf16_to_double", "oracle_f32_to_double"):
+               "oracle_half_to_double", "oracle_bf16_to_double", "oracle_f32_to_double",
+               "oracle_argmax_f32"):
         getattr(lib, fn).argtypes = getattr(real, fn).argtypes
         getattr(lib, fn).restype = getattr(real, fn).restype
     caught = []
@@ -83,7 +94,7 @@ def test_pins_catch_planted_mistake(name, tmp_path, golden_dir):
             try:
                 fn(golden_dir) if wants_dir else fn()
             except AssertionError:
-                caught.append(fn.__name__)
+                caught.append(getattr(fn, "__name__", "pin"))
     finally:
         oracle._lib = real
     assert caught, "no pin caught mutation " + name

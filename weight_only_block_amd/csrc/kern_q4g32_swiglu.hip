@@ -8,7 +8,7 @@ namespace qg {
 hipError_t launch_q4g32_swiglu(int G, int shape, const KernelParams& kp, int64_t waves, int slots,
                                size_t lds, hipStream_t s)
 {
-    return launch_swiglu(G, shape, kp, waves, slots, lds, s);
+    return launch_swiglu<FMT_Q4G32>(G, shape, kp, waves, slots, lds, s);
 }
 
 }  // namespace qg

@@ -698,11 +698,14 @@ hipError_t launch_format(int m, bool grouped, int G, int shape, const KernelPara
     }
 }
 
-// Grouped Q4G32 gate/up pairs with the SwiGLU epilogue (m = 1).
-inline hipError_t launch_swiglu(int G, int shape, const KernelParams& kp, int64_t waves, int slots,
-                                size_t lds, hipStream_t s)
+// Grouped Q4G32 gate/up pairs with the SwiGLU epilogue (m = 1).  A template
+// so that only the translation unit that calls it instantiates the kernels.
+template <int FMT>
+hipError_t launch_swiglu(int G, int shape, const KernelParams& kp, int64_t waves, int slots,
+                         size_t lds, hipStream_t s)
 {
-    return launch_g<FMT_Q4G32, 1, true, 1>(G, shape, kp, waves, slots, lds, s);
+    static_assert(FMT == FMT_Q4G32, "the SwiGLU epilogue is built for Q4G32 gate/up pairs");
+    return launch_g<FMT, 1, true, 1>(G, shape, kp, waves, slots, lds, s);
 }
 
 }  // namespace qg
