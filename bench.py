@@ -41,7 +41,8 @@ TRAFFIC = {
 
 
 KERNEL_SOURCES = ("kernel_body.h", "kern_q8g64.hip", "kern_q4g32.hip", "kern_q8g128.hip",
-                  "kern_q8pc.hip", "kern_q4g32_swiglu.hip", "launch.hip", "layout.h", "launch.h")
+                  "kern_q8pc.hip", "kern_q4g32_swiglu.hip", "argmax.hip", "argmax.h", "launch.hip",
+                  "layout.h", "launch.h")
 
 
 def kernel_source_digest():
@@ -135,11 +136,31 @@ def setup_lm_head(torch, Q, synth, fmt="q8g64"):
     def step(i):
         calls[i % copies]()
 
+    step.logits = y
     info = {"workload": "lm_head %s GEMV m=1, N=151936 x K=2560 (Qwen3-4B vocabulary)" % fmt.upper(),
             "format": fmt, "m": 1, "N": N, "K": K, "weight_copies": copies, "period": copies,
             "kernel": Q.variant_name(fmt_id, 1, N, K)}
     cpu = {"fmt": fmt, "q": q, "s": s, "x": x}
     return step, alg_bytes, weight_bytes, 1, info, cpu
+
+
+def setup_lm_head_argmax(torch, Q, synth):
+    """The LM head followed by the greedy argmax over its logits: the GEMV
+    writes the fp32 logits, the argmax reads them and writes one index."""
+    step0, alg, weight_bytes, _, info, cpu = setup_lm_head(torch, Q, synth, "q8g64")
+    _, _, N, K = synth.LM_HEAD
+    y = step0.logits                  # the GEMV's output is the argmax's input
+    idx = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(Q.argmax_workspace_size(1), dtype=torch.uint8, device="cuda")
+    arg = Q.bound_argmax_f32(y, idx, ws, N)
+
+    def step(i):
+        step0(i)
+        arg()
+
+    info = dict(info, workload="lm_head Q8G64 GEMV m=1 (N=151936 x K=2560) + greedy argmax",
+                kernel=[info["kernel"], "argmax_rows"])
+    return step, alg + 4 * N + 4, weight_bytes, 2, info, cpu
 
 
 def cpu_lm_head(oracle, cpu, threads, reps):
@@ -374,7 +395,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="lm_head",
-                    choices=["lm_head", "lm_head_q8g128", "moe_experts", "moe_experts_merged",
+                    choices=["lm_head", "lm_head_q8g128", "lm_head_argmax", "moe_experts", "moe_experts_merged",
                              "moe_experts_swiglu", "q8_small", "qwen3_0.6b", "q4_k2560", "w8a16_qwen3_14b_tp4"])
     ap.add_argument("--m", type=int, default=1,
                     help="activation rows (q4_k2560 and w8a16_qwen3_14b_tp4)")
@@ -411,7 +432,9 @@ def main():
 
     def measure(name):
         t0 = time.time()
-        if name in ("lm_head", "lm_head_q8g128"):
+        if name == "lm_head_argmax":
+            step, alg, wbytes, launches, info, cpu = setup_lm_head_argmax(torch, Q, synth)
+        elif name in ("lm_head", "lm_head_q8g128"):
             step, alg, wbytes, launches, info, cpu = setup_lm_head(
                 torch, Q, synth, "q8g64" if name == "lm_head" else "q8g128")
         elif name == "moe_experts":

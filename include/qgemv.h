@@ -203,6 +203,28 @@ qg_status qgemv_grouped_q4g32_swiglu(const void *w_gate_up_packed, int64_t exper
                                      int64_t act_slot_stride, int64_t N, int64_t K,
                                      void *hip_stream);
 
+/* ------------------------------------------------------------ greedy tail
+ * Greedy token choice over fp32 logits (the LM head's output):
+ *   idx_out[i] = the n in [0, N) with the largest x[i*ldx + n], the lowest
+ *                such n on ties, for 0 <= i < m.
+ * Values compare as real numbers (-0 == +0; -inf lowest); a NaN counts as
+ * larger than every number, so the first NaN of a row wins.  Each row is
+ * split across work-groups with a (value, lower index) comparator, the
+ * split argmax of the commit log of vllm.cpp pull request #1936 (also the
+ * device-side greedy step after the LM head in the Qwen3 C++ Reference
+ * Runtime (MetaInfer-cpp) README, milestone M6.5-F); the index does not
+ * depend on the split or on timing.  One kernel launch.
+ *   x          device fp32, 4-byte aligned, m rows of N values, ldx >= N
+ *   idx_out    device int32[m], 4-byte aligned
+ *   workspace  device, >= qg_argmax_workspace_size(m) bytes, 8-byte
+ *              aligned, all zero before the first call.  Each completed
+ *              call leaves it all zero again.  Calls that share a workspace
+ *              must not overlap in time (same stream is enough).
+ *   1 <= N < 2^31; m = 0 is a no-op; m <= 65535. */
+size_t    qg_argmax_workspace_size(int64_t m);
+qg_status qg_argmax_f32(const float *x, int64_t m, int64_t N, int64_t ldx, int32_t *idx_out,
+                        void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* ------------------------------------------------------------- test hooks
  * Every successful qgemv_* call bumps the counter of the kernel variant it
  * launched.  Variant names: "<fmt>[_grouped[_swiglu]]_m<m>_g<G>_r<R>" with fmt

@@ -233,3 +233,71 @@ def test_bound_calls_keep_their_buffers_alive():
     del dense, grouped
     gc.collect()
     assert all(r() is None for r in refs)
+
+
+def test_argmax_validation_and_workspace_size():
+    f = Q.lib().qg_argmax_f32
+    ws_need = Q.argmax_workspace_size(4)
+    assert ws_need >= 12 * 4 and ws_need % 256 == 0
+    assert Q.argmax_workspace_size(0) == 0 and Q.argmax_workspace_size(-1) == 0
+    WS, OUT = W, Y
+    # Every call below must fail validation (no launch on fake addresses).
+    assert f(None, 4, 100, 100, OUT, WS, ws_need, None) == Q.QG_ERR_INVALID_ARG
+    assert f(X, 4, 100, 100, None, WS, ws_need, None) == Q.QG_ERR_INVALID_ARG
+    assert f(X, 4, 100, 100, OUT, None, ws_need, None) == Q.QG_ERR_INVALID_ARG
+    assert f(X, -1, 100, 100, OUT, WS, ws_need, None) == Q.QG_ERR_INVALID_ARG
+    assert f(X, 65536, 100, 100, OUT, WS, 1 << 30, None) == Q.QG_ERR_INVALID_ARG
+    assert f(X, 4, 0, 100, OUT, WS, ws_need, None) == Q.QG_ERR_INVALID_ARG
+    assert f(X, 4, 1 << 31, 1 << 31, OUT, WS, ws_need, None) == Q.QG_ERR_INVALID_ARG
+    assert f(X, 4, 100, 99, OUT, WS, ws_need, None) == Q.QG_ERR_INVALID_ARG
+    assert f(X, 4, 100, 100, OUT, WS, ws_need - 1, None) == Q.QG_ERR_INVALID_ARG
+    assert f(X + 2, 4, 100, 100, OUT, WS, ws_need, None) == Q.QG_ERR_ALIGNMENT
+    assert f(X, 4, 100, 100, OUT + 2, WS, ws_need, None) == Q.QG_ERR_ALIGNMENT
+    assert f(X, 4, 100, 100, OUT, WS + 4, ws_need, None) == Q.QG_ERR_ALIGNMENT
+    assert f(X, 0, 100, 100, OUT, WS, ws_need, None) == Q.QG_OK      # no rows
+
+
+def test_swiglu_validation():
+    f = Q.lib().qgemv_grouped_q4g32_swiglu
+    N, K = 64, 256
+    st = Q.gate_up_expert_stride(N, K)
+    assert st == Q.qpack_q4g32_gate_up_size(N, K) and st % 256 == 0
+    A = Y
+    # Every call below must fail validation (no launch on fake addresses).
+    assert f(None, st, 4, IDS, 2, X, 0, A, N, N, K, None) == Q.QG_ERR_INVALID_ARG
+    assert f(W, st, 4, None, 2, X, 0, A, N, N, K, None) == Q.QG_ERR_INVALID_ARG
+    assert f(W, st, 4, IDS, 2, X, 0, None, N, N, K, None) == Q.QG_ERR_INVALID_ARG
+    assert f(W, st, 4, IDS, 65, X, 0, A, N, N, K, None) == Q.QG_ERR_UNSUPPORTED
+    assert f(W, st, 0, IDS, 2, X, 0, A, N, N, K, None) == Q.QG_ERR_INVALID_ARG
+    assert f(W, st - 256, 4, IDS, 2, X, 0, A, N, N, K, None) == Q.QG_ERR_INVALID_ARG
+    assert f(W, st, 4, IDS, 2, X, 0, A, N - 1, N, K, None) == Q.QG_ERR_INVALID_ARG
+    assert f(W, st, 4, IDS, 2, X, 0, A, N, N, K + 16, None) == Q.QG_ERR_INVALID_ARG
+    assert f(W, st + 16, 4, IDS, 2, X, 0, A, N, N, K, None) == Q.QG_ERR_ALIGNMENT
+    assert f(W, st, 4, IDS, 2, X, 3, A, N, N, K, None) == Q.QG_ERR_ALIGNMENT
+    assert f(W, st, 4, IDS, 2, X, 0, A + 1, N, N, K, None) == Q.QG_ERR_ALIGNMENT
+    assert f(W + 64, st, 4, IDS, 2, X, 0, A, N, N, K, None) == Q.QG_ERR_ALIGNMENT
+    assert f(W, st, 4, IDS, 0, X, 0, A, N, N, K, None) == Q.QG_OK     # no slots
+
+
+def test_gate_up_pack_roundtrip_and_interleave():
+    for (N, K) in [(1, 32), (7, 96), (100, 2560), (1536, 4096), (129, 32)]:
+        rng = synth.rng_for(11, N, K)
+        g = synth.q4g32_weights(rng, N, K)
+        u = synth.q4g32_weights(rng, N, K)
+        buf = Q.qpack_q4g32_gate_up(g, u)
+        assert buf.nbytes == Q.qpack_q4g32_gate_up_size(N, K)
+        g2, u2 = Q.qunpack_q4g32_gate_up(buf, N, K)
+        assert all(np.array_equal(a, b) for a, b in zip(g + u, g2 + u2))
+        # The pair buffer is the plain packing of the rows interleaved in
+        # blocks of RPS = 64 / G: gate rows of a tile, then its up rows.
+        G = int(Q.variant_name(Q.FMT_GROUPED_Q4G32_SWIGLU, 1, N, K).split("_g")[-1].split("_")[0])
+        rps = 64 // G
+        Nv = 2 * (-(-N // rps)) * rps
+        mats = [np.zeros((Nv,) + a.shape[1:], a.dtype) for a in g]
+        for v in range(Nv):
+            t, w = divmod(v, 2 * rps)
+            n = t * rps + w % rps
+            if n < N:
+                for k in range(3):
+                    mats[k][v] = (g if w < rps else u)[k][n]
+        assert np.array_equal(Q.qpack_q4g32(*mats), buf)

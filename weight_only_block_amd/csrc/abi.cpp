@@ -13,6 +13,7 @@
 #include <atomic>
 
 #include "../../include/qgemv.h"
+#include "argmax.h"
 #include "launch.h"
 
 namespace {
@@ -243,6 +244,28 @@ qg_status qgemv_grouped_q4g32_swiglu(const void* w_gate_up_packed, int64_t exper
     (void)hipGetLastError();
     if (qg::launch(a) != hipSuccess) return QG_ERR_HIP;
     g_route[5][0][log2i(L.G)].fetch_add(1, std::memory_order_relaxed);
+    return QG_OK;
+}
+
+size_t qg_argmax_workspace_size(int64_t m)
+{
+    if (m < 0 || m > 65535) return 0;
+    return qg::argmax_workspace_bytes(m);
+}
+
+qg_status qg_argmax_f32(const float* x, int64_t m, int64_t N, int64_t ldx, int32_t* idx_out,
+                        void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    if (!x || !idx_out || !workspace) return QG_ERR_INVALID_ARG;
+    if (m == 0) return QG_OK;
+    if (m < 0 || m > 65535 || N < 1 || N > (int64_t(1) << 31) - 1 || ldx < N)
+        return QG_ERR_INVALID_ARG;
+    if (workspace_bytes < qg::argmax_workspace_bytes(m)) return QG_ERR_INVALID_ARG;
+    if (!aligned(x, 4) || !aligned(idx_out, 4) || !aligned(workspace, 8)) return QG_ERR_ALIGNMENT;
+    (void)hipGetLastError();
+    if (qg::launch_argmax(x, m, N, ldx, idx_out, workspace, static_cast<hipStream_t>(hip_stream)) !=
+        hipSuccess)
+        return QG_ERR_HIP;
     return QG_OK;
 }
 

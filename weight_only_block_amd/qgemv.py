@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
             "qpack_q4g32_gate_up": ([p, p, p, p, p, p, i64, i64, p, sz], st),
             "qunpack_q4g32_gate_up": ([p, sz, i64, i64, p, p, p, p, p, p], st),
             "qgemv_grouped_q4g32_swiglu": ([p, i64, i32, p, i32, p, i64, p, i64, i64, i64, p], st),
+            "qg_argmax_workspace_size": ([i64], sz),
+            "qg_argmax_f32": ([p, i64, i64, i64, p, p, sz, p], st),
             "qg_route_counts_reset": ([], None),
             "qg_route_count": ([ctypes.c_char_p], ctypes.c_uint64),
             "qg_variant_name": ([ctypes.c_int, i64, i64, i64, ctypes.c_char_p, sz], st),
@@ -336,6 +338,31 @@ def qgemv_grouped_q4g32_swiglu(w_gate_up, expert_stride_bytes: int, n_experts: i
     return st
 
 
+def argmax_workspace_size(m: int) -> int:
+    return int(lib().qg_argmax_workspace_size(m))
+
+
+def argmax_f32(x, idx_out, workspace, N=None, m=None, ldx=None, stream=None, check=True):
+    """Greedy choice per row of device fp32 logits x [m][>=N]: idx_out[i] =
+    index of the largest value (lowest on ties, first NaN wins).
+
+    idx_out: device int32 tensor [m]; workspace: device tensor of at least
+    argmax_workspace_size(m) bytes, zero before the first call and left zero
+    by every call."""
+    if m is None:
+        m = 1 if x.dim() == 1 else x.shape[0]
+    if N is None:
+        N = x.shape[-1]
+    if ldx is None:
+        ldx = x.stride(0) if x.dim() == 2 else N
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib().qg_argmax_f32(x.data_ptr(), m, N, ldx, idx_out.data_ptr(), workspace.data_ptr(),
+                             nbytes, _stream_handle(stream))
+    if check:
+        _check(st, "qg_argmax_f32")
+    return st
+
+
 # ------------------------------------------------------- prepared launches
 
 class BoundCall:
@@ -412,6 +439,15 @@ def bound_grouped_q4g32_swiglu(w_gate_up, expert_stride_bytes: int, n_experts: i
             _stream_handle(stream))
     return BoundCall(lib().qgemv_grouped_q4g32_swiglu, args, "qgemv_grouped_q4g32_swiglu",
                      (w_gate_up, expert_ids, x, act))
+
+
+def bound_argmax_f32(x, idx_out, workspace, N: int, m: int = 1, ldx=None, stream=None):
+    """As bound_q8g64 for qg_argmax_f32."""
+    ldx = N if ldx is None else ldx
+    nbytes = workspace.numel() * workspace.element_size()
+    args = (x.data_ptr(), m, N, ldx, idx_out.data_ptr(), workspace.data_ptr(), nbytes,
+            _stream_handle(stream))
+    return BoundCall(lib().qg_argmax_f32, args, "qg_argmax_f32", (x, idx_out, workspace))
 
 
 # --------------------------------------------------------------- test hooks
