@@ -41,8 +41,8 @@ TRAFFIC = {
 
 
 KERNEL_SOURCES = ("kernel_body.h", "kern_q8g64.hip", "kern_q4g32.hip", "kern_q8g128.hip",
-                  "kern_q8pc.hip", "kern_q4g32_swiglu.hip", "argmax.hip", "argmax.h", "launch.hip",
-                  "layout.h", "launch.h")
+                  "kern_q8pc.hip", "kern_q4g32_swiglu.hip", "kern_argmax_epi.hip", "argmax.hip",
+                  "argmax.h", "argmax_key.h", "launch.hip", "layout.h", "launch.h")
 
 
 def kernel_source_digest():
@@ -161,6 +161,33 @@ def setup_lm_head_argmax(torch, Q, synth):
     info = dict(info, workload="lm_head Q8G64 GEMV m=1 (N=151936 x K=2560) + greedy argmax",
                 kernel=[info["kernel"], "argmax_rows"])
     return step, alg + 4 * N + 4, weight_bytes, 2, info, cpu
+
+
+def setup_lm_head_argmax_fused(torch, Q, synth):
+    """The LM head with the greedy argmax in the same launch and no logits
+    written: what a greedy decode step needs from the LM head."""
+    _, _, N, K = synth.LM_HEAD
+    rng = synth.rng_for(synth.WORKLOAD_IDS["lm_head"], 0)
+    q, s = synth.q8g64_weights(rng, N, K)
+    x = synth.activations(rng, 1, K)
+    packed = Q.qpack_q8g64(q, s)
+    copies = max(2, -(-2 * LLC_BYTES // packed.nbytes))
+    w = [dev(torch, packed) for _ in range(copies)]
+    del packed
+    xd = dev(torch, x)
+    idx = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(Q.argmax_workspace_size(1), dtype=torch.uint8, device="cuda")
+    calls = [Q.bound_q8g64_argmax(wc, xd, None, idx, ws, N, K) for wc in w]
+
+    def step(i):
+        calls[i % copies]()
+
+    weight_bytes = synth.bytes_q8g64(N, K)
+    info = {"workload": "lm_head Q8G64 GEMV m=1 (N=151936 x K=2560) with the greedy argmax fused, "
+                        "no logits written",
+            "format": "q8g64", "m": 1, "N": N, "K": K, "weight_copies": copies, "period": copies,
+            "kernel": Q.variant_name(Q.FMT_Q8G64_ARGMAX, 1, N, K)}
+    return step, weight_bytes + 2 * K + 4, weight_bytes, 1, info, {"fmt": "q8g64", "q": q, "s": s, "x": x}
 
 
 def cpu_lm_head(oracle, cpu, threads, reps):
@@ -395,7 +422,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="lm_head",
-                    choices=["lm_head", "lm_head_q8g128", "lm_head_argmax", "moe_experts", "moe_experts_merged",
+                    choices=["lm_head", "lm_head_q8g128", "lm_head_argmax", "lm_head_argmax_fused",
+                             "moe_experts", "moe_experts_merged",
                              "moe_experts_swiglu", "q8_small", "qwen3_0.6b", "q4_k2560", "w8a16_qwen3_14b_tp4"])
     ap.add_argument("--m", type=int, default=1,
                     help="activation rows (q4_k2560 and w8a16_qwen3_14b_tp4)")
@@ -432,7 +460,9 @@ def main():
 
     def measure(name):
         t0 = time.time()
-        if name == "lm_head_argmax":
+        if name == "lm_head_argmax_fused":
+            step, alg, wbytes, launches, info, cpu = setup_lm_head_argmax_fused(torch, Q, synth)
+        elif name == "lm_head_argmax":
             step, alg, wbytes, launches, info, cpu = setup_lm_head_argmax(torch, Q, synth)
         elif name in ("lm_head", "lm_head_q8g128"):
             step, alg, wbytes, launches, info, cpu = setup_lm_head(

@@ -225,17 +225,41 @@ size_t    qg_argmax_workspace_size(int64_t m);
 qg_status qg_argmax_f32(const float *x, int64_t m, int64_t N, int64_t ldx, int32_t *idx_out,
                         void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* LM head with the greedy choice fused into the GEMV: as qgemv_q8g64 /
+ * qgemv_q8g128, and in the same launch idx_out[i] = the argmax of output
+ * row i under the rule of qg_argmax_f32.  The fused LM-head argmax candidate
+ * of the Qwen3 C++ Reference Runtime (MetaInfer-cpp) README, milestone
+ * M6.5-F (rejected there against a library GEMM plus argmax; here the GEMV
+ * is this library's own).  The index equals qg_argmax_f32 applied to the
+ * logits the same call writes.
+ *   logits     device fp32 m x N with row stride ldy, or NULL to skip
+ *              writing the logits (ldy is then ignored)
+ *   idx_out    device int32[m]
+ *   workspace  as qg_argmax_f32 (qg_argmax_workspace_size(m) bytes, zero
+ *              before the first call, left zero by every completed call;
+ *              calls sharing it must not overlap)
+ * Other arguments and errors as qgemv_q8g64. */
+qg_status qgemv_q8g64_argmax(const void *w_packed, const uint16_t *x_bf16, float *logits,
+                             int32_t *idx_out, int64_t m, int64_t N, int64_t K, int64_t ldx,
+                             int64_t ldy, void *workspace, size_t workspace_bytes,
+                             void *hip_stream);
+qg_status qgemv_q8g128_argmax(const void *w_packed, const uint16_t *x_bf16, float *logits,
+                              int32_t *idx_out, int64_t m, int64_t N, int64_t K, int64_t ldx,
+                              int64_t ldy, void *workspace, size_t workspace_bytes,
+                              void *hip_stream);
+
 /* ------------------------------------------------------------- test hooks
  * Every successful qgemv_* call bumps the counter of the kernel variant it
- * launched.  Variant names: "<fmt>[_grouped[_swiglu]]_m<m>_g<G>_r<R>" with fmt
- * one of q8g64, q4g32, q8g128, q8pc, e.g. "q8g64_m1_g32_r2".  qg_route_count
- * returns 0 for unknown names. */
+ * launched.  Variant names: "<fmt>[_grouped[_swiglu]|_argmax]_m<m>_g<G>_r<R>"
+ * with fmt one of q8g64, q4g32, q8g128, q8pc, e.g. "q8g64_m1_g32_r2".
+ * qg_route_count returns 0 for unknown names. */
 void     qg_route_counts_reset(void);
 uint64_t qg_route_count(const char *variant);
 /* Writes the name of the variant qgemv_* would launch for (fmt, m, N, K)
  * into buf (fmt 0 = Q8G64, 1 = Q4G32, 2 = grouped Q4G32, 3 = Q8G128,
- * 4 = Q8PC, 5 = grouped Q4G32 with SwiGLU, N = gate rows).  Returns QG_OK or
- * the status the call itself would return for that shape. */
+ * 4 = Q8PC, 5 = grouped Q4G32 with SwiGLU, N = gate rows, 6 = Q8G64 with
+ * the argmax epilogue, 7 = Q8G128 with the argmax epilogue).  Returns QG_OK
+ * or the status the call itself would return for that shape. */
 qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char *buf, size_t buf_len);
 
 #ifdef __cplusplus

@@ -301,3 +301,21 @@ def test_gate_up_pack_roundtrip_and_interleave():
                 for k in range(3):
                     mats[k][v] = (g if w < rps else u)[k][n]
         assert np.array_equal(Q.qpack_q4g32(*mats), buf)
+
+
+def test_fused_argmax_validation():
+    ws_need = Q.argmax_workspace_size(2)
+    for name in ("qgemv_q8g64_argmax", "qgemv_q8g128_argmax"):
+        f = getattr(Q.lib(), name)
+        K = 256
+        # Every call below must fail validation (no launch on fake addresses).
+        assert f(W, X, Y, None, 2, 16, K, K, 16, IDS, ws_need, None) == Q.QG_ERR_INVALID_ARG
+        assert f(W, X, Y, IDS, 2, 16, K, K, 16, None, ws_need, None) == Q.QG_ERR_INVALID_ARG
+        assert f(W, X, Y, IDS, 2, 16, K, K, 16, IDS, ws_need - 1, None) == Q.QG_ERR_INVALID_ARG
+        assert f(W, X, Y, IDS, 5, 16, K, K, 16, IDS, 1 << 20, None) == Q.QG_ERR_UNSUPPORTED
+        assert f(W, X, Y, IDS, 2, 16, K, K, 15, IDS, ws_need, None) == Q.QG_ERR_INVALID_ARG
+        assert f(W, X, Y, IDS + 2, 2, 16, K, K, 16, IDS, ws_need, None) == Q.QG_ERR_ALIGNMENT
+        assert f(W, X, Y, IDS, 2, 16, K, K, 16, IDS + 4, ws_need, None) == Q.QG_ERR_ALIGNMENT
+        assert f(W, X, Y, IDS, 0, 16, K, K, 16, IDS, ws_need, None) == Q.QG_OK   # empty batch
+    assert Q.variant_name(Q.FMT_Q8G64_ARGMAX, 1, 151936, 2560) == "q8g64_argmax_m1_g32_r2"
+    assert Q.variant_name(Q.FMT_Q8G128_ARGMAX, 3, 151936, 2560) == "q8g128_argmax_m3_g32_r2"

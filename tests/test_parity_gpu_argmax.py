@@ -145,3 +145,122 @@ def test_lm_head_then_argmax_picks_a_valid_token():
     for i in range(2):
         best = y_ref[i].max()
         assert y_ref[i, got[i]] >= best - 2e-3 * (a_ref[i, got[i]] + a_ref[i, y_ref[i].argmax()])
+
+
+# ------------------------------------------------ LM head with fused argmax
+
+FUSED = {"q8g64": (synth.q8g64_weights, Q.qpack_q8g64, Q.qgemv_q8g64, Q.qgemv_q8g64_argmax,
+                   oracle.q8g64, Q.FMT_Q8G64_ARGMAX),
+         "q8g128": (synth.q8g128_weights, Q.qpack_q8g128, Q.qgemv_q8g128, Q.qgemv_q8g128_argmax,
+                    oracle.q8g128, Q.FMT_Q8G128_ARGMAX)}
+
+
+@pytest.mark.parametrize("fmt", ["q8g64", "q8g128"])
+@pytest.mark.parametrize("m", [1, 4])
+def test_fused_lm_head_argmax_full_size(fmt, m):
+    # Same launch configuration as the plain GEMV: the fused call's logits
+    # must equal the plain call's bit for bit, its index must equal the
+    # argmax of those logits, and the logits must meet the GEMV bar.
+    gen, pack, plain, fused, ref, _ = FUSED[fmt]
+    _, _, N, K = synth.LM_HEAD
+    rng = synth.rng_for(91, m)
+    q, s = gen(rng, N, K)
+    x = synth.activations(rng, m, K)
+    w = torch.from_numpy(pack(q, s)).to("cuda")
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+    y_plain = torch.empty((m, N), dtype=torch.float32, device="cuda")
+    y_fused = torch.full((m, N), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.full((m,), -7, dtype=torch.int32, device="cuda")
+    ws = workspace(m)
+    plain(w, xd, y_plain, N, K)
+    fused(w, xd, y_fused, idx, ws, N, K)
+    torch.cuda.synchronize()
+    yp, yf = y_plain.cpu().numpy(), y_fused.cpu().numpy()
+    assert np.array_equal(yp.view(np.uint32), yf.view(np.uint32))
+    assert np.array_equal(idx.cpu().numpy().astype(np.int64), oracle.argmax_f32(yf))
+    y_ref, a_ref = ref(q, s, x, threads=16)
+    assert oracle.within_tolerance(yf, y_ref, a_ref).all()
+    assert not ws.any().item()
+
+
+@pytest.mark.parametrize("N,K", [(1, 64), (7, 128), (1000, 2560), (5003, 1024), (40000, 256)])
+def test_fused_argmax_ragged_shapes_without_logits(N, K):
+    # With logits=None nothing but the index is written.
+    gen, pack, plain, fused, _, _ = FUSED["q8g64"]
+    rng = synth.rng_for(92, N, K)
+    q, s = gen(rng, N, K)
+    x = synth.activations(rng, 3, K)
+    w = torch.from_numpy(pack(q, s)).to("cuda")
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+    y = torch.empty((3, N), dtype=torch.float32, device="cuda")
+    plain(w, xd, y, N, K)
+    idx = torch.full((3,), -7, dtype=torch.int32, device="cuda")
+    ws = workspace(3)
+    for _ in range(3):                       # the workspace is reused
+        fused(w, xd, None, idx, ws, N, K, m=3)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy().astype(np.int64), oracle.argmax_f32(y.cpu().numpy()))
+    assert not ws.any().item()
+
+
+def test_fused_argmax_ties_take_the_lowest_index():
+    # Four identical weight rows (codes of the sign of x, the largest scale)
+    # give four identical logits far above the rest: the first of them wins.
+    N, K = 3000, 512
+    rng = synth.rng_for(93, 0)
+    q, s = synth.q8g64_weights(rng, N, K)
+    x = synth.activations(rng, 1, K)
+    sign = np.where(x[0] & 0x8000, -1, 1)
+    for r in (17, 1500, 2000, 2999):
+        q[r] = (100 * sign).astype(np.int8)
+        s[r] = synth.to_fp16_bits(np.full(K // 64, 0.05))
+    w = torch.from_numpy(Q.qpack_q8g64(q, s)).to("cuda")
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+    y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    idx = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Q.qgemv_q8g64_argmax(w, xd, y, idx, workspace(1), N, K)
+    torch.cuda.synchronize()
+    yv = y.cpu().numpy()[0]
+    assert yv[17] == yv[1500] == yv[2000] == yv[2999] == yv.max()
+    assert idx.item() == 17
+
+
+def test_fused_argmax_graph_replays():
+    _, _, N, K = synth.LM_HEAD
+    rng = synth.rng_for(94, 0)
+    q, s = synth.q8g64_weights(rng, 20000, K)
+    w = torch.from_numpy(Q.qpack_q8g64(q, s)).to("cuda")
+    xd = torch.from_numpy(synth.activations(rng, 1, K).view(np.int16)).to("cuda")
+    y = torch.empty((1, 20000), dtype=torch.float32, device="cuda")
+    idx = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = workspace(1)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call = Q.bound_q8g64_argmax(w, xd, y, idx, ws, 20000, K)
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        call()
+    for r in range(4):
+        xd.copy_(torch.from_numpy(synth.activations(synth.rng_for(94, 10 + r), 1, K).view(np.int16)).to("cuda"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy().astype(np.int64), oracle.argmax_f32(y.cpu().numpy()))
+
+
+def test_fused_route_counter_and_variant_name():
+    Q.route_counts_reset()
+    N, K = 640, 1024
+    rng = synth.rng_for(95, 0)
+    q, s = synth.q8g128_weights(rng, N, K)
+    w = torch.from_numpy(Q.qpack_q8g128(q, s)).to("cuda")
+    xd = torch.from_numpy(synth.activations(rng, 2, K).view(np.int16)).to("cuda")
+    idx = torch.zeros(2, dtype=torch.int32, device="cuda")
+    Q.qgemv_q8g128_argmax(w, xd, None, idx, workspace(2), N, K)
+    torch.cuda.synchronize()
+    name = Q.variant_name(Q.FMT_Q8G128_ARGMAX, 2, N, K)
+    assert name.startswith("q8g128_argmax_m2_")
+    assert Q.route_count(name) == 1

@@ -19,8 +19,9 @@
 namespace {
 
 // Route counters: one per (kind, m, log2 G).  kind 0 Q8G64, 1 Q4G32,
-// 2 grouped Q4G32, 3 Q8G128, 4 Q8PC, 5 grouped Q4G32 with SwiGLU.
-constexpr int kKinds = 6, kMs = 4, kGs = 7;
+// 2 grouped Q4G32, 3 Q8G128, 4 Q8PC, 5 grouped Q4G32 with SwiGLU,
+// 6 Q8G64 with the argmax epilogue, 7 Q8G128 with the argmax epilogue.
+constexpr int kKinds = 8, kMs = 4, kGs = 7;
 std::atomic<uint64_t> g_route[kKinds][kMs][kGs];
 
 int log2i(int v)
@@ -38,7 +39,9 @@ const char* kind_name(int kind)
     case 2: return "q4g32_grouped";
     case 3: return "q8g128";
     case 4: return "q8pc";
-    default: return "q4g32_grouped_swiglu";
+    case 5: return "q4g32_grouped_swiglu";
+    case 6: return "q8g64_argmax";
+    default: return "q8g128_argmax";
     }
 }
 
@@ -65,7 +68,7 @@ qg_status check_shape(int fmt, int64_t m, int64_t N, int64_t K, qg::Layout* L)
 {
     if (m < 1 || m > 4) return QG_ERR_UNSUPPORTED;
     if (!qg::make_layout(fmt, N, K, L)) return QG_ERR_INVALID_ARG;
-    if (qg::lds_bytes_for(*L, int(m)) > qg::kMaxLdsBytes) return QG_ERR_UNSUPPORTED;
+    if (qg::lds_bytes_for(*L, int(m)) > qg::kMaxDynLdsBytes) return QG_ERR_UNSUPPORTED;
     return QG_OK;
 }
 
@@ -74,20 +77,26 @@ qg_status check_gate_up(int64_t N, int64_t K, qg::Layout* L)
 {
     int64_t rps;
     if (!qg::make_gate_up_layout(N, K, L, &rps)) return QG_ERR_INVALID_ARG;
-    if (qg::lds_bytes_for(*L, 1) > qg::kMaxLdsBytes) return QG_ERR_UNSUPPORTED;
+    if (qg::lds_bytes_for(*L, 1) > qg::kMaxDynLdsBytes) return QG_ERR_UNSUPPORTED;
     return QG_OK;
 }
 
+// Dense GEMV; with idx_out the argmax epilogue (y may then be null).
 qg_status run_dense(int fmt, const void* w_packed, const uint16_t* x, float* y, int64_t m,
-                    int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* stream)
+                    int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* stream,
+                    int32_t* idx_out = nullptr, void* workspace = nullptr, size_t workspace_bytes = 0)
 {
-    if (!w_packed || !x || !y) return QG_ERR_INVALID_ARG;
+    const bool argmax = idx_out != nullptr;
+    if (!w_packed || !x || (!y && !argmax)) return QG_ERR_INVALID_ARG;
+    if (argmax && !workspace) return QG_ERR_INVALID_ARG;
     if (m == 0) return QG_OK;  // an empty batch: nothing to compute
     qg::Layout L;
     const qg_status st = check_shape(fmt, m, N, K, &L);
     if (st != QG_OK) return st;
-    if (ldx < K || ldy < N) return QG_ERR_INVALID_ARG;
-    if (!aligned(w_packed, 256) || !aligned(x, 4) || !aligned(y, 4)) return QG_ERR_ALIGNMENT;
+    if (ldx < K || (y && ldy < N)) return QG_ERR_INVALID_ARG;
+    if (argmax && workspace_bytes < qg::argmax_workspace_bytes(m)) return QG_ERR_INVALID_ARG;
+    if (!aligned(w_packed, 256) || !aligned(x, 4) || (y && !aligned(y, 4))) return QG_ERR_ALIGNMENT;
+    if (argmax && (!aligned(idx_out, 4) || !aligned(workspace, 8))) return QG_ERR_ALIGNMENT;
     if (m > 1 && (ldx % 2) != 0) return QG_ERR_ALIGNMENT;
     qg::LaunchArgs a;
     a.layout = L;
@@ -108,10 +117,14 @@ qg_status run_dense(int fmt, const void* w_packed, const uint16_t* x, float* y, 
     a.act = nullptr;
     a.act_slot_stride = 0;
     a.n_out = N;
+    a.argmax = argmax;
+    a.idx_out = idx_out;
+    a.argmax_workspace = workspace;
     a.stream = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // clear a stale error so the check below is ours
     if (qg::launch(a) != hipSuccess) return QG_ERR_HIP;
-    g_route[kind_of(fmt)][m - 1][log2i(L.G)].fetch_add(1, std::memory_order_relaxed);
+    const int kind = argmax ? (fmt == qg::FMT_Q8G64 ? 6 : 7) : kind_of(fmt);
+    g_route[kind][m - 1][log2i(L.G)].fetch_add(1, std::memory_order_relaxed);
     return QG_OK;
 }
 
@@ -194,6 +207,9 @@ qg_status qgemv_grouped_q4g32(const void* w_experts_packed, int64_t expert_strid
     a.act = nullptr;
     a.act_slot_stride = 0;
     a.n_out = N;
+    a.argmax = false;
+    a.idx_out = nullptr;
+    a.argmax_workspace = nullptr;
     a.stream = static_cast<hipStream_t>(hip_stream);
     (void)hipGetLastError();
     if (qg::launch(a) != hipSuccess) return QG_ERR_HIP;
@@ -240,11 +256,32 @@ qg_status qgemv_grouped_q4g32_swiglu(const void* w_gate_up_packed, int64_t exper
     a.act = act_bf16;
     a.act_slot_stride = act_slot_stride;
     a.n_out = N;
+    a.argmax = false;
+    a.idx_out = nullptr;
+    a.argmax_workspace = nullptr;
     a.stream = static_cast<hipStream_t>(hip_stream);
     (void)hipGetLastError();
     if (qg::launch(a) != hipSuccess) return QG_ERR_HIP;
     g_route[5][0][log2i(L.G)].fetch_add(1, std::memory_order_relaxed);
     return QG_OK;
+}
+
+qg_status qgemv_q8g64_argmax(const void* w_packed, const uint16_t* x_bf16, float* logits,
+                             int32_t* idx_out, int64_t m, int64_t N, int64_t K, int64_t ldx,
+                             int64_t ldy, void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    if (!idx_out) return QG_ERR_INVALID_ARG;
+    return run_dense(qg::FMT_Q8G64, w_packed, x_bf16, logits, m, N, K, ldx, ldy, hip_stream, idx_out,
+                     workspace, workspace_bytes);
+}
+
+qg_status qgemv_q8g128_argmax(const void* w_packed, const uint16_t* x_bf16, float* logits,
+                              int32_t* idx_out, int64_t m, int64_t N, int64_t K, int64_t ldx,
+                              int64_t ldy, void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    if (!idx_out) return QG_ERR_INVALID_ARG;
+    return run_dense(qg::FMT_Q8G128, w_packed, x_bf16, logits, m, N, K, ldx, ldy, hip_stream,
+                     idx_out, workspace, workspace_bytes);
 }
 
 size_t qg_argmax_workspace_size(int64_t m)
@@ -293,7 +330,8 @@ qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char* buf, s
 {
     if (!buf || buf_len == 0) return QG_ERR_INVALID_ARG;
     static const int kind_format[kKinds] = {qg::FMT_Q8G64, qg::FMT_Q4G32, qg::FMT_Q4G32,
-                                            qg::FMT_Q8G128, qg::FMT_Q8PC, qg::FMT_Q4G32};
+                                            qg::FMT_Q8G128, qg::FMT_Q8PC, qg::FMT_Q4G32,
+                                            qg::FMT_Q8G64, qg::FMT_Q8G128};
     if (fmt < 0 || fmt >= kKinds) return QG_ERR_INVALID_ARG;
     if ((fmt == 2 || fmt == 5) && m != 1) return QG_ERR_UNSUPPORTED;
     qg::Layout L;

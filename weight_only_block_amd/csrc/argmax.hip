@@ -11,6 +11,7 @@
 #include <stdint.h>
 
 #include "argmax.h"
+#include "argmax_key.h"
 
 namespace qg {
 
@@ -19,25 +20,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPerThread = 8;                        // elements per thread per work-group
 constexpr int64_t kChunk = int64_t(kThreads) * kPerThread;
-
-// Orderable key: the value's total order in the high 32 bits (-inf lowest,
-// -0 folded onto +0, every NaN above +inf), the inverted index in the low 32
-// bits so that among equal values the lower index has the larger key.  No
-// value maps to key 0, which therefore starts every reduction.
-__device__ __forceinline__ uint64_t argmax_key(float v, uint32_t idx)
-{
-    uint32_t u = __float_as_uint(v);
-    uint32_t ord;
-    if ((u & 0x7fffffffu) > 0x7f800000u) {
-        ord = 0xffffffffu;
-    } else {
-        if (u == 0x80000000u) u = 0;
-        ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    }
-    return (uint64_t(ord) << 32) | uint64_t(~idx);
-}
-
-__device__ __forceinline__ uint64_t max_key(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
 __global__ __launch_bounds__(kThreads) void argmax_rows(const float* __restrict__ x, int64_t ldx,
                                                          int64_t N, int32_t* __restrict__ out,
@@ -79,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void argmax_rows(const float* __restrict_
             __threadfence();
             const unsigned long long fin = atomicExch(&keys[row], 0ull);
             atomicExch(&counts[row], 0u);
-            out[row] = int32_t(~uint32_t(fin & 0xffffffffu));
+            out[row] = key_index(fin);
         }
     }
 }

@@ -31,6 +31,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include "argmax_key.h"
 #include "launch.h"
 
 namespace qg {
@@ -437,6 +438,71 @@ __device__ __forceinline__ void finish_tile_swiglu(float (&acc)[R][1], const Ker
     }
 }
 
+// Argmax epilogue: reduces the tile like finish_tile, stores the logits if
+// the caller wants them, and folds each finished logit into the lane's
+// running key for its activation row.
+template <int M, int G, int R>
+__device__ __forceinline__ void finish_tile_argmax(float (&acc)[R][M], const KernelParams& p, float* y,
+                                                   int64_t tile, int g, int rho, int lane,
+                                                   uint64_t (&best)[M])
+{
+    constexpr int RPS = 64 / G;
+    constexpr int TR = R * RPS;
+    TileSums<M, G, R> ts;
+    reduce_tile<M, G, R>(acc, ts);
+    const bool holder = TileSums<M, G, R>::holder(g);
+#pragma unroll
+    for (int k = 0; k < TileSums<M, G, R>::V2; ++k) {
+        const int o = TileSums<M, G, R>::which(k, lane);
+        const int r = o / M, i = o - (o / M) * M;
+        const int64_t row = tile * TR + r * RPS + rho;
+        if (holder && row < p.N) {
+            if (y) y[int64_t(i) * p.ldy + row] = ts.v[k];
+            const uint64_t key = argmax_key(ts.v[k], uint32_t(row));
+#pragma unroll
+            for (int ii = 0; ii < M; ++ii)
+                if (ii == i) best[ii] = max_key(best[ii], key);
+        }
+    }
+}
+
+// End of an argmax-epilogue launch: the work-group's best key per row goes
+// into the row's global key with an atomic max (order-free, so the result
+// is the same whatever the timing); the last work-group to finish writes
+// the indices and zeroes the keys and the counter for the next call.
+template <int M>
+__device__ __forceinline__ void finish_argmax(uint64_t (&best)[M], const KernelParams& p, int lane, int wave)
+{
+    __shared__ uint64_t wave_best[4][M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const unsigned long long o = __shfl_xor((unsigned long long)best[i], off, 64);
+            best[i] = max_key(best[i], o);
+        }
+        if (lane == 0) wave_best[wave][i] = best[i];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            uint64_t k = wave_best[0][i];
+#pragma unroll
+            for (int w = 1; w < 4; ++w) k = max_key(k, wave_best[w][i]);
+            atomicMax(&p.keys[i], (unsigned long long)k);
+        }
+        __threadfence();
+        const unsigned int done = atomicAdd(p.counter, 1u);
+        if (done == gridDim.x - 1) {
+            __threadfence();
+#pragma unroll
+            for (int i = 0; i < M; ++i) p.idx_out[i] = key_index(atomicExch(&p.keys[i], 0ull));
+            atomicExch(p.counter, 0u);
+        }
+    }
+}
+
 // Waves sweep the matrix together: global wave gw of a slot streams tiles
 // gw, gw + W, gw + 2W, ... (W = waves per slot), so at any moment the whole
 // launch reads one contiguous window of the packed buffer.  That keeps the
@@ -446,7 +512,8 @@ __device__ __forceinline__ void finish_tile_swiglu(float (&acc)[R][1], const Ker
 // tiles up to one.  The work-group stages x once for its waves, and a ring of
 // DEPTH items in registers keeps up to DEPTH*R KiB of loads in flight per wave.
 // EPI 0 stores fp32 sums; EPI 1 is the SwiGLU epilogue over gate/up pairs
-// (grouped Q4G32, m = 1 only).
+// (grouped Q4G32, m = 1 only); EPI 2 is the greedy argmax epilogue (dense,
+// logits store optional).
 template <int FMT, int M, int G, int R, int DEPTH, int WAVES, bool GROUPED, int EPI>
 __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
 {
@@ -489,8 +556,9 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
         my_tiles = gw < p.tiles ? (p.tiles - 1 - gw) / W + 1 : 0;
     }
     const int64_t n_items = my_tiles * p.J;
-    static_assert(EPI == 0 || (FMT == FMT_Q4G32 && M == 1 && GROUPED && R == 2),
+    static_assert(EPI != 1 || (FMT == FMT_Q4G32 && M == 1 && GROUPED && R == 2),
                   "the SwiGLU epilogue is built for grouped Q4G32 gate/up pairs");
+    static_assert(EPI != 2 || (!GROUPED && WAVES == 4), "the argmax epilogue is for dense launches");
     float* y = p.y + int64_t(slot) * p.y_slot_stride;
     uint16_t* act = p.act + int64_t(slot) * p.act_slot_stride;
     const uint16_t* x = p.x + int64_t(slot) * p.x_slot_stride;
@@ -568,7 +636,11 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     }
 #undef QG_FILL_RING
     __syncthreads();
-    if (n_items == 0) return;
+    // (The argmax epilogue needs every wave at its closing barrier.)
+    if (EPI != 2 && n_items == 0) return;
+    uint64_t best[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) best[i] = 0;
 
     float acc[R][M];
 #pragma unroll
@@ -586,6 +658,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     do {                                                                                      \
         if (++j == p.J) {                                                                     \
             if constexpr (EPI == 1) finish_tile_swiglu<G, R>(acc, p, act, tile, g, rho, lane);      \
+            else if constexpr (EPI == 2) finish_tile_argmax<M, G, R>(acc, p, p.y, tile, g, rho, lane, best); \
             else finish_tile<M, G, R>(acc, p, y, tile, g, rho, lane);                               \
             tile += tstep;                                                                    \
             j = 0;                                                                            \
@@ -622,6 +695,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
 #undef QG_LOAD_NEXT
 #undef QG_CONSUME
 #undef QG_ADVANCE
+    if constexpr (EPI == 2) finish_argmax<M>(best, p, lane, wave);
 }
 
 // Launch shape (launch.h): ring depth 2 or 4; work-groups are 4 waves.
@@ -631,10 +705,17 @@ hipError_t launch_variant(const KernelParams& kp, int64_t waves, int slots, size
                           hipStream_t stream)
 {
     auto kern = qgemv_stream<FMT, M, G, kRowSlots, DEPTH, WAVES, GROUPED, EPI>;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-        int(kMaxLdsBytes));
-    (void)attr;
+    // Raise the dynamic-LDS limit once per kernel (static LDS is within the
+    // reserve).  A failure is not left behind as the launch's error; it only
+    // matters to launches that need more than the default 64 KiB.
+    static const hipError_t attr = [&] {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 int(kMaxDynLdsBytes));
+        if (e != hipSuccess) (void)hipGetLastError();
+        return e;
+    }();
+    if (attr != hipSuccess && lds_bytes > 64 * 1024) return attr;
     const dim3 grid(unsigned((waves + WAVES - 1) / WAVES), unsigned(slots));
     hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), lds_bytes, stream, kp);
     return hipGetLastError();
@@ -694,6 +775,21 @@ hipError_t launch_format(int m, bool grouped, int G, int shape, const KernelPara
     case 2: return launch_g<FMT, 2, false, 0>(G, shape, kp, waves, slots, lds, s);
     case 3: return launch_g<FMT, 3, false, 0>(G, shape, kp, waves, slots, lds, s);
     case 4: return launch_g<FMT, 4, false, 0>(G, shape, kp, waves, slots, lds, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Dense launches with the argmax epilogue (m = 1..4).  A template so that
+// only the translation unit that calls it instantiates the kernels.
+template <int FMT>
+hipError_t launch_argmax_format(int m, int G, int shape, const KernelParams& kp, int64_t waves,
+                                size_t lds, hipStream_t s)
+{
+    switch (m) {
+    case 1: return launch_g<FMT, 1, false, 2>(G, shape, kp, waves, 1, lds, s);
+    case 2: return launch_g<FMT, 2, false, 2>(G, shape, kp, waves, 1, lds, s);
+    case 3: return launch_g<FMT, 3, false, 2>(G, shape, kp, waves, 1, lds, s);
+    case 4: return launch_g<FMT, 4, false, 2>(G, shape, kp, waves, 1, lds, s);
     default: return hipErrorInvalidValue;
     }
 }

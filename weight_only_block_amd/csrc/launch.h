@@ -9,8 +9,11 @@
 
 namespace qg {
 
-// LDS a work-group may use on gfx950.
+// LDS a work-group may use on gfx950, and the part of it left for the
+// dynamic (activation) area once 1 KiB is set aside for the kernels' own
+// static LDS (the argmax epilogue's per-wave keys).
 constexpr size_t kMaxLdsBytes = 160 * 1024;
+constexpr size_t kMaxDynLdsBytes = kMaxLdsBytes - 1024;
 
 // Kernel arguments (passed by value).
 struct KernelParams {
@@ -35,6 +38,9 @@ struct KernelParams {
     uint16_t* act;             // SwiGLU epilogue: bf16 output per slot
     int64_t act_slot_stride;   // elements between slot outputs (SwiGLU)
     int32_t n_out;             // outputs per slot (SwiGLU: gate rows)
+    int32_t* idx_out;          // argmax epilogue: chosen index per activation row
+    unsigned long long* keys;  // argmax epilogue: one key per row (zero between calls)
+    unsigned int* counter;     // argmax epilogue: finished work-groups (zero between calls)
 };
 
 // Launch shape: ring depth 2 or 4 items; work-groups are 4 waves.
@@ -59,6 +65,9 @@ struct LaunchArgs {
     uint16_t* act;
     int64_t act_slot_stride;
     int64_t n_out;
+    bool argmax;               // argmax epilogue (dense Q8G64 / Q8G128)
+    int32_t* idx_out;
+    void* argmax_workspace;    // keys[m], then the counter
     hipStream_t stream;
 };
 
@@ -78,6 +87,9 @@ QG_DECLARE_LAUNCHER(launch_q4g32);
 QG_DECLARE_LAUNCHER(launch_q8g128);
 QG_DECLARE_LAUNCHER(launch_q8pc);
 #undef QG_DECLARE_LAUNCHER
+// Dense Q8G64 / Q8G128 with the argmax epilogue (kern_argmax_epi.hip).
+hipError_t launch_argmax_epilogue(int fmt, int m, int G, int shape, const KernelParams& kp,
+                                  int64_t waves, size_t lds, hipStream_t s);
 // Grouped Q4G32 with the SwiGLU epilogue (kern_q4g32_swiglu.hip), m = 1.
 hipError_t launch_q4g32_swiglu(int G, int shape, const KernelParams& kp, int64_t waves, int slots,
                                size_t lds, hipStream_t s);

@@ -62,6 +62,9 @@ hipError_t launch(const LaunchArgs& a)
     kp.act = a.act;
     kp.act_slot_stride = a.act_slot_stride;
     kp.n_out = int32_t(a.n_out);
+    kp.idx_out = a.idx_out;
+    kp.keys = static_cast<unsigned long long*>(a.argmax_workspace);
+    kp.counter = a.argmax_workspace ? reinterpret_cast<unsigned int*>(kp.keys + a.m) : nullptr;
     const int slots = a.grouped ? a.n_slots : 1;
     // About target_waves waves in total (QG_TARGET_WAVES overrides it, for
     // tuning sweeps), never more waves than tiles; k tiles per wave, then the
@@ -103,6 +106,7 @@ hipError_t launch(const LaunchArgs& a)
     const hipStream_t s = a.stream;
     const int64_t w = waves_per_slot;
     if (a.swiglu) return launch_q4g32_swiglu(L.G, shape, kp, w, slots, lds, s);
+    if (a.argmax) return launch_argmax_epilogue(L.fmt, a.m, L.G, shape, kp, w, lds, s);
     switch (L.fmt) {
     case FMT_Q8G64: return launch_q8g64(a.m, a.grouped, L.G, shape, kp, w, slots, lds, s);
     case FMT_Q4G32: return launch_q4g32(a.m, a.grouped, L.G, shape, kp, w, slots, lds, s);

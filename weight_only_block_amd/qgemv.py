@@ -27,6 +27,8 @@ FMT_GROUPED_Q4G32 = 2
 FMT_Q8G128 = 3
 FMT_Q8PC = 4
 FMT_GROUPED_Q4G32_SWIGLU = 5
+FMT_Q8G64_ARGMAX = 6
+FMT_Q8G128_ARGMAX = 7
 
 _lib = None
 
@@ -72,6 +74,8 @@ def lib() -> ctypes.CDLL:
             "qunpack_q4g32_gate_up": ([p, sz, i64, i64, p, p, p, p, p, p], st),
             "qgemv_grouped_q4g32_swiglu": ([p, i64, i32, p, i32, p, i64, p, i64, i64, i64, p], st),
             "qg_argmax_workspace_size": ([i64], sz),
+            "qgemv_q8g64_argmax": ([p, p, p, p, i64, i64, i64, i64, i64, p, sz, p], st),
+            "qgemv_q8g128_argmax": ([p, p, p, p, i64, i64, i64, i64, i64, p, sz, p], st),
             "qg_argmax_f32": ([p, i64, i64, i64, p, p, sz, p], st),
             "qg_route_counts_reset": ([], None),
             "qg_route_count": ([ctypes.c_char_p], ctypes.c_uint64),
@@ -363,6 +367,42 @@ def argmax_f32(x, idx_out, workspace, N=None, m=None, ldx=None, stream=None, che
     return st
 
 
+def _argmax_gemv_args(w_packed, x, logits, idx_out, workspace, N, K, m, ldx, ldy, stream):
+    if m is None:
+        m = 1 if x.dim() == 1 else x.shape[0]
+    if ldx is None:
+        ldx = x.stride(0) if x.dim() == 2 else K
+    if ldy is None:
+        ldy = logits.stride(0) if logits is not None and logits.dim() == 2 else N
+    nbytes = workspace.numel() * workspace.element_size()
+    return (w_packed.data_ptr(), x.data_ptr(), None if logits is None else logits.data_ptr(),
+            idx_out.data_ptr(), m, N, K, ldx, ldy, workspace.data_ptr(), nbytes,
+            _stream_handle(stream))
+
+
+def qgemv_q8g64_argmax(w_packed, x, logits, idx_out, workspace, N: int, K: int, m=None, ldx=None,
+                       ldy=None, stream=None, check=True):
+    """LM head and greedy choice in one launch: as qgemv_q8g64 (logits may be
+    None to skip writing them) plus idx_out[i] = argmax of output row i.
+    workspace: as argmax_f32 (argmax_workspace_size(m) bytes, zero before
+    the first call, left zero by every call)."""
+    st = lib().qgemv_q8g64_argmax(*_argmax_gemv_args(w_packed, x, logits, idx_out, workspace, N,
+                                                      K, m, ldx, ldy, stream))
+    if check:
+        _check(st, "qgemv_q8g64_argmax")
+    return st
+
+
+def qgemv_q8g128_argmax(w_packed, x, logits, idx_out, workspace, N: int, K: int, m=None, ldx=None,
+                        ldy=None, stream=None, check=True):
+    """As qgemv_q8g64_argmax for Q8G128 weights."""
+    st = lib().qgemv_q8g128_argmax(*_argmax_gemv_args(w_packed, x, logits, idx_out, workspace, N,
+                                                       K, m, ldx, ldy, stream))
+    if check:
+        _check(st, "qgemv_q8g128_argmax")
+    return st
+
+
 # ------------------------------------------------------- prepared launches
 
 class BoundCall:
@@ -448,6 +488,14 @@ def bound_argmax_f32(x, idx_out, workspace, N: int, m: int = 1, ldx=None, stream
     args = (x.data_ptr(), m, N, ldx, idx_out.data_ptr(), workspace.data_ptr(), nbytes,
             _stream_handle(stream))
     return BoundCall(lib().qg_argmax_f32, args, "qg_argmax_f32", (x, idx_out, workspace))
+
+
+def bound_q8g64_argmax(w_packed, x, logits, idx_out, workspace, N: int, K: int, m: int = 1,
+                       ldx=None, ldy=None, stream=None):
+    """As bound_q8g64 for qgemv_q8g64_argmax (logits may be None)."""
+    args = _argmax_gemv_args(w_packed, x, logits, idx_out, workspace, N, K, m, ldx, ldy, stream)
+    keep = [t for t in (w_packed, x, logits, idx_out, workspace) if t is not None]
+    return BoundCall(lib().qgemv_q8g64_argmax, args, "qgemv_q8g64_argmax", keep)
 
 
 # --------------------------------------------------------------- test hooks
