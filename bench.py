@@ -42,7 +42,7 @@ TRAFFIC = {
 
 
 KERNEL_SOURCES = ("kernel_body.h", "kern_q8g64.hip", "kern_q4g32.hip", "kern_q8g128.hip",
-                  "kern_q8pc.hip", "kern_q4g32_swiglu.hip", "kern_argmax_epi.hip", "argmax.hip",
+                  "kern_q8pc.hip", "kern_q4g32_swiglu.hip", "kern_argmax_epi.hip", "kern_mma.hip", "argmax.hip",
                   "argmax.h", "argmax_key.h", "launch.hip", "layout.h", "launch.h")
 
 
@@ -189,6 +189,49 @@ def setup_lm_head_argmax_fused(torch, Q, synth):
             "format": "q8g64", "m": 1, "N": N, "K": K, "weight_copies": copies, "period": copies,
             "kernel": Q.variant_name(Q.FMT_Q8G64_ARGMAX, 1, N, K)}
     return step, weight_bytes + 2 * K + 4, weight_bytes, 1, info, {"fmt": "q8g64", "q": q, "s": s, "x": x}
+
+
+def setup_mma(torch, Q, synth, name, m):
+    """Batched decode on the matrix cores (weights in the matrix-core
+    layout): the LM head (Q8G64) or the Qwen3-14B TP4 W8A16 layer, m rows."""
+    if name == "lm_head_mma":
+        _, _, N, K = synth.LM_HEAD
+        mats = [("lm_head", "q8g64", N, K)]
+        desc = "lm_head Q8G64 matrix-core GEMV m=%d, N=151936 x K=2560" % m
+        wid = synth.WORKLOAD_IDS["lm_head"]
+    else:
+        mats = synth.W8A16_QWEN3_14B_TP4
+        desc = ("Qwen3-14B TP4 rank-local decode layer, per-output-channel W8A16 on the matrix "
+                "cores m=%d: qkv 5120->1792, o 1280->5120, gate/up 5120->8704, down 4352->5120" % m)
+        wid = synth.WORKLOAD_IDS["w8a16_qwen3_14b_tp4"]
+    layer, wbytes, io = [], 0, 0
+    for j, (label, fmt, N, K) in enumerate(mats):
+        rng = synth.rng_for(wid, j)
+        if fmt == "q8g64":
+            packed = Q.qpack_q8g64_mma(*synth.q8g64_weights(rng, N, K))
+            wbytes += synth.bytes_q8g64(N, K)
+        else:
+            packed = Q.qpack_q8pc_mma(*synth.q8pc_weights(rng, N, K))
+            wbytes += synth.bytes_q8pc(N, K)
+        x = dev(torch, synth.activations(rng, m, K))
+        y = torch.empty((m, N), dtype=torch.float32, device="cuda")
+        io += m * (2 * K + 4 * N)
+        layer.append((fmt, N, K, packed, x, y))
+    set_bytes = sum(l[3].nbytes for l in layer)
+    copies = max(2 if len(layer) == 1 else 1, -(-2 * LLC_BYTES // set_bytes))
+    dev_sets = [[dev(torch, l[3]) for l in layer] for _ in range(copies)]
+    calls = [[Q.bound_mma(fmt, w, x, y, N, K, m=m) for (fmt, N, K, _, x, y), w in zip(layer, ws)]
+             for ws in dev_sets]
+
+    def step(i):
+        for c in calls[i % copies]:
+            c()
+
+    fid = {"q8g64": Q.FMT_Q8G64_MMA, "q8pc": Q.FMT_Q8PC_MMA}
+    info = {"workload": desc, "format": mats[0][1] + "_mma", "m": m, "weight_copies": copies,
+            "period": copies,
+            "kernel": sorted({Q.variant_name(fid[f], m, N, K) for (_, f, N, K) in mats})}
+    return step, wbytes + io, wbytes, len(mats), info, None
 
 
 def cpu_lm_head(oracle, cpu, threads, reps):
@@ -425,9 +468,10 @@ def main():
     ap.add_argument("--workload", default="lm_head",
                     choices=["lm_head", "lm_head_q8g128", "lm_head_argmax", "lm_head_argmax_fused",
                              "moe_experts", "moe_experts_merged",
-                             "moe_experts_swiglu", "q8_small", "qwen3_0.6b", "q4_k2560", "w8a16_qwen3_14b_tp4"])
+                             "moe_experts_swiglu", "q8_small", "qwen3_0.6b", "q4_k2560", "w8a16_qwen3_14b_tp4",
+                             "lm_head_mma", "w8a16_qwen3_14b_tp4_mma"])
     ap.add_argument("--m", type=int, default=1,
-                    help="activation rows (q4_k2560 and w8a16_qwen3_14b_tp4)")
+                    help="activation rows (q4_k2560, w8a16_qwen3_14b_tp4: 1..4; *_mma: 1..16)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the timed steps from a captured HIP graph (no host launch cost)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -461,7 +505,9 @@ def main():
 
     def measure(name):
         t0 = time.time()
-        if name == "lm_head_argmax_fused":
+        if name in ("lm_head_mma", "w8a16_qwen3_14b_tp4_mma"):
+            step, alg, wbytes, launches, info, cpu = setup_mma(torch, Q, synth, name, args.m)
+        elif name == "lm_head_argmax_fused":
             step, alg, wbytes, launches, info, cpu = setup_lm_head_argmax_fused(torch, Q, synth)
         elif name == "lm_head_argmax":
             step, alg, wbytes, launches, info, cpu = setup_lm_head_argmax(torch, Q, synth)

@@ -151,6 +151,41 @@ qg_status qgemv_q8pc(const void *w_packed, const uint16_t *x_bf16, float *y,
                      int64_t m, int64_t N, int64_t K, int64_t ldx, int64_t ldy,
                      void *hip_stream);
 
+/* ------------------------------------------------- batched decode, m <= 16
+ * Decode with up to 16 activation rows on the matrix cores: the larger-batch
+ * ("B8/B16") decode of the Qwen3 C++ Reference Runtime (MetaInfer-cpp)
+ * README, where the input rows are reused from LDS across every weight.  The
+ * weights use their own packed layout (one 1 KiB wave load = 16 rows x 64 K,
+ * the MFMA operand order), made by qpack_*_mma; y is the same product as the
+ * plain GEMV:
+ *   y[i*ldy + n] = sum_k W[n][k] * x[i*ldx + k],  0 <= i < m <= 16.
+ * K must be a multiple of 64 (128 for Q8G128).  The m activation rows are
+ * staged in LDS: m * K * 2 bytes must fit in 159 KiB (e.g. m = 16 with
+ * K <= 5088, m = 15 with K = 5120), else QG_ERR_UNSUPPORTED.  Pointers,
+ * strides, ownership and errors as qgemv_q8g64.  Each output row is
+ * computed on its own (rows do not affect one another's bits). */
+size_t    qpack_q8g64_mma_size(int64_t N, int64_t K);
+size_t    qpack_q8g128_mma_size(int64_t N, int64_t K);
+size_t    qpack_q8pc_mma_size(int64_t N, int64_t K);
+qg_status qpack_q8g64_mma(const int8_t *q, const uint16_t *scales_f16, int64_t N, int64_t K,
+                          void *out, size_t out_bytes);
+qg_status qpack_q8g128_mma(const int8_t *q, const uint16_t *scales_f16, int64_t N, int64_t K,
+                           void *out, size_t out_bytes);
+qg_status qpack_q8pc_mma(const int8_t *q, const float *scales_f32, int64_t N, int64_t K,
+                         void *out, size_t out_bytes);
+qg_status qunpack_q8g64_mma(const void *packed, size_t packed_bytes, int64_t N, int64_t K,
+                            int8_t *q, uint16_t *scales_f16);
+qg_status qunpack_q8g128_mma(const void *packed, size_t packed_bytes, int64_t N, int64_t K,
+                             int8_t *q, uint16_t *scales_f16);
+qg_status qunpack_q8pc_mma(const void *packed, size_t packed_bytes, int64_t N, int64_t K,
+                           int8_t *q, float *scales_f32);
+qg_status qgemv_q8g64_mma(const void *w_packed, const uint16_t *x_bf16, float *y, int64_t m,
+                          int64_t N, int64_t K, int64_t ldx, int64_t ldy, void *hip_stream);
+qg_status qgemv_q8g128_mma(const void *w_packed, const uint16_t *x_bf16, float *y, int64_t m,
+                           int64_t N, int64_t K, int64_t ldx, int64_t ldy, void *hip_stream);
+qg_status qgemv_q8pc_mma(const void *w_packed, const uint16_t *x_bf16, float *y, int64_t m,
+                         int64_t N, int64_t K, int64_t ldx, int64_t ldy, void *hip_stream);
+
 /* Routed-expert decode (one token, several experts), Q4G32:
  *   for each slot j < n_slots, with e = expert_ids_dev[j]:
  *     y[j*y_slot_stride + n] = sum_k W_e[n][k] * x[j*x_slot_stride + k]
@@ -258,8 +293,9 @@ uint64_t qg_route_count(const char *variant);
 /* Writes the name of the variant qgemv_* would launch for (fmt, m, N, K)
  * into buf (fmt 0 = Q8G64, 1 = Q4G32, 2 = grouped Q4G32, 3 = Q8G128,
  * 4 = Q8PC, 5 = grouped Q4G32 with SwiGLU, N = gate rows, 6 = Q8G64 with
- * the argmax epilogue, 7 = Q8G128 with the argmax epilogue).  Returns QG_OK
- * or the status the call itself would return for that shape. */
+ * the argmax epilogue, 7 = Q8G128 with the argmax epilogue, 8/9/10 = the
+ * matrix-core kernel for Q8G64/Q8G128/Q8PC, named "<fmt>_mma_m<m>").
+ * Returns QG_OK or the status the call itself would return for that shape. */
 qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char *buf, size_t buf_len);
 
 #ifdef __cplusplus

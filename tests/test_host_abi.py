@@ -319,3 +319,33 @@ def test_fused_argmax_validation():
         assert f(W, X, Y, IDS, 0, 16, K, K, 16, IDS, ws_need, None) == Q.QG_OK   # empty batch
     assert Q.variant_name(Q.FMT_Q8G64_ARGMAX, 1, 151936, 2560) == "q8g64_argmax_m1_g32_r2"
     assert Q.variant_name(Q.FMT_Q8G128_ARGMAX, 3, 151936, 2560) == "q8g128_argmax_m3_g32_r2"
+
+
+@pytest.mark.parametrize("fmt", ["q8g64", "q8g128", "q8pc"])
+def test_mma_pack_roundtrip_sizes_and_validation(fmt):
+    gen = {"q8g64": synth.q8g64_weights, "q8g128": synth.q8g128_weights,
+           "q8pc": synth.q8pc_weights}[fmt]
+    pack = getattr(Q, "qpack_%s_mma" % fmt)
+    alg = {"q8g64": synth.bytes_q8g64, "q8g128": synth.bytes_q8g128, "q8pc": synth.bytes_q8pc}[fmt]
+    for N, K in [(1, 128), (17, 256), (48, 1280), (5120, 1280)]:
+        q, s = gen(synth.rng_for(12, N, K), N, K)
+        packed = pack(q, s)
+        assert packed.nbytes == Q.qpack_mma_size(fmt, N, K)
+        q2, s2 = Q.qunpack_mma(fmt, packed, N, K)
+        assert np.array_equal(q, q2) and np.array_equal(s, s2)
+        if N % 16 == 0:
+            assert packed.nbytes == -(-alg(N, K) // 256) * 256
+    assert Q.qpack_mma_size(fmt, 4, 96) == 0            # K not a multiple of 64
+    f = getattr(Q.lib(), "qgemv_%s_mma" % fmt)
+    K = 1024
+    # Every call below must fail validation (no launch on fake addresses).
+    assert f(W, X, Y, 17, 16, K, K, 16, None) == Q.QG_ERR_UNSUPPORTED          # m > 16
+    assert f(W, X, Y, 16, 16, 5120, 5120, 16, None) == Q.QG_ERR_UNSUPPORTED    # LDS
+    assert f(W, X, Y, 2, 16, 96, 96, 16, None) == Q.QG_ERR_INVALID_ARG
+    assert f(W, X, Y, 2, 16, K, K - 2, 16, None) == Q.QG_ERR_INVALID_ARG
+    assert f(W, X, Y, 2, 16, K, K, 15, None) == Q.QG_ERR_INVALID_ARG
+    assert f(W + 16, X, Y, 2, 16, K, K, 16, None) == Q.QG_ERR_ALIGNMENT
+    assert f(W, X, Y, 2, 16, K, K + 1, 16, None) == Q.QG_ERR_ALIGNMENT
+    assert f(W, X, Y, 0, 16, K, K, 16, None) == Q.QG_OK
+    fid = {"q8g64": Q.FMT_Q8G64_MMA, "q8g128": Q.FMT_Q8G128_MMA, "q8pc": Q.FMT_Q8PC_MMA}[fmt]
+    assert Q.variant_name(fid, 16, 151936, 2560) == "%s_mma_m16" % fmt

@@ -1,0 +1,194 @@
+"""GPU parity for the matrix-core decode kernel (m = 1..16), through the
+C ABI: qgemv_q8g64_mma, qgemv_q8g128_mma, qgemv_q8pc_mma on weights packed
+in the matrix-core layout.  Same acceptance as the other GEMV parity tests
+(|y - y_ref| <= 2e-3 sum|w x| per output, bit-exact on exact inputs, NaN
+canary, untouched elements past N).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from weight_only_block_amd import qgemv as Q
+from weight_only_block_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+CANARY_BITS = 0x7FC0DEAD
+THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+FMT = {
+    "q8g64": (synth.q8g64_weights, Q.qpack_q8g64_mma, Q.qgemv_q8g64_mma, oracle.q8g64, 64),
+    "q8g128": (synth.q8g128_weights, Q.qpack_q8g128_mma, Q.qgemv_q8g128_mma, oracle.q8g128, 128),
+    "q8pc": (synth.q8pc_weights, Q.qpack_q8pc_mma, Q.qgemv_q8pc_mma, oracle.q8pc, 64),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    Q.lib()
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    elif a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).to("cuda")
+
+
+def canary(shape):
+    return torch.full(shape, CANARY_BITS, dtype=torch.int32, device="cuda").view(torch.float32)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def run(fmt, q, s, x, ldx=None, ldy=None, packed=None):
+    _, pack, gemv, _, _ = FMT[fmt]
+    N, K = q.shape
+    m = x.shape[0]
+    ldx = K if ldx is None else ldx
+    ldy = N if ldy is None else ldy
+    xb = np.zeros((m, ldx), np.uint16)
+    xb[:, :K] = x[:, :K]
+    y = canary((m, ldy))
+    w = packed if packed is not None else dev(pack(q, s))
+    gemv(w, dev(xb), y, N, K, m=m, ldx=ldx, ldy=ldy)
+    return host(y)
+
+
+def check(fmt, q, s, x, y, what):
+    ref = FMT[fmt][3]
+    y_ref, a_ref = ref(q, s, x, threads=THREADS)
+    ok = oracle.within_tolerance(y, y_ref, a_ref, TOL)
+    if not ok.all():
+        bad = np.argwhere(~ok)[:5]
+        raise AssertionError("%s: %d of %d bad, e.g. %s" % (
+            what, (~ok).sum(), ok.size, [(tuple(b), y[tuple(b)], y_ref[tuple(b)]) for b in bad]))
+
+
+# ----------------------------------------------------------- workload configs
+
+@pytest.mark.parametrize("m", [8, 16])
+@pytest.mark.parametrize("fmt", ["q8g64", "q8g128"])
+def test_lm_head_batched_full_size(fmt, m):
+    _, _, N, K = synth.LM_HEAD
+    gen = FMT[fmt][0]
+    rng = synth.rng_for(100, m)
+    q, s = gen(rng, N, K)
+    x = synth.activations(rng, m, K)
+    y = run(fmt, q, s, x)
+    check(fmt, q, s, x, y, "lm_head %s m=%d" % (fmt, m))
+
+
+@pytest.mark.parametrize("m", [8, 15])
+@pytest.mark.parametrize("j,label,N,K", [(j, c[0], c[2], c[3])
+                                         for j, c in enumerate(synth.W8A16_QWEN3_14B_TP4)])
+def test_w8a16_qwen3_14b_tp4_batched(j, label, N, K, m):
+    rng = synth.rng_for(101, j, m)
+    q, s = synth.q8pc_weights(rng, N, K)
+    x = synth.activations(rng, m, K)
+    y = run("q8pc", q, s, x)
+    check("q8pc", q, s, x, y, "w8a16 %s m=%d" % (label, m))
+
+
+# ------------------------------------------------------------ shape sweep
+
+@pytest.mark.parametrize("m", [1, 2, 5, 16])
+@pytest.mark.parametrize("N", [1, 15, 17, 1000])
+@pytest.mark.parametrize("K", [128, 384, 2560])
+@pytest.mark.parametrize("fmt", ["q8g64", "q8g128", "q8pc"])
+def test_ragged_shapes_and_strides(fmt, K, N, m):
+    gen = FMT[fmt][0]
+    rng = synth.rng_for(102, N, K, m)
+    q, s = gen(rng, N, K)
+    x = synth.activations(rng, m, K)
+    y = run(fmt, q, s, x, ldx=K + 4, ldy=N + 3)
+    assert np.all(y[:, N:].view(np.uint32) == CANARY_BITS), "wrote past N"
+    check(fmt, q, s, x, y[:, :N], "%s N=%d K=%d m=%d" % (fmt, N, K, m))
+
+
+def test_every_m_from_1_to_16():
+    N, K = 3000, 1024
+    rng = synth.rng_for(103, 0)
+    q, s = synth.q8g64_weights(rng, N, K)
+    w = dev(Q.qpack_q8g64_mma(q, s))
+    x = synth.activations(rng, 16, K)
+    y_ref, a_ref = oracle.q8g64(q, s, x, threads=THREADS)
+    for m in range(1, 17):
+        y = run("q8g64", q, s, x[:m], packed=w)
+        assert oracle.within_tolerance(y, y_ref[:m], a_ref[:m], TOL).all(), "m=%d" % m
+
+
+# ------------------------------------------------------- exact arithmetic
+
+@pytest.mark.parametrize("fmt,N,K,m", [("q8g64", 4096, 2560, 16), ("q8g128", 1000, 4096, 9),
+                                       ("q8pc", 5120, 1280, 12)])
+def test_exact_inputs_bit_exact(fmt, N, K, m):
+    rng = synth.rng_for(104, N, K)
+    q = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+    if fmt == "q8pc":
+        s = (2.0 ** rng.integers(-40, -30, size=N)).astype(np.float32).view(np.uint32)
+    else:
+        s = synth.to_fp16_bits(2.0 ** rng.integers(-6, -2, size=(N, K // FMT[fmt][4])))
+    x = synth.to_bf16_bits(rng.integers(-4, 5, size=(m, K)).astype(np.float32))
+    y = run(fmt, q, s, x)
+    y_ref, _ = FMT[fmt][3](q, s, x, threads=THREADS)
+    assert np.array_equal(y.astype(np.float64), y_ref)
+
+
+# -------------------------------------------------------- degenerate cases
+
+@pytest.mark.parametrize("fmt", ["q8g64", "q8g128", "q8pc"])
+def test_zero_codes_scales_and_activations_give_exact_zero(fmt):
+    gen = FMT[fmt][0]
+    rng = synth.rng_for(105, 0)
+    q, s = gen(rng, 300, 2560)
+    x = synth.activations(rng, 7, 2560)
+    assert np.all(run(fmt, np.zeros_like(q), s, x) == 0.0)
+    assert np.all(run(fmt, q, np.zeros_like(s), x) == 0.0)
+    assert np.all(run(fmt, q, s, np.zeros_like(x)) == 0.0)
+
+
+# ------------------------------------------------- structural identities
+
+def test_rows_do_not_depend_on_the_batch():
+    # Each output row of the matrix product is computed on its own, so the
+    # rows of an m = 16 call equal m = 1 calls bit for bit.
+    N, K = 2000, 2560
+    rng = synth.rng_for(106, 0)
+    q, s = synth.q8g64_weights(rng, N, K)
+    w = dev(Q.qpack_q8g64_mma(q, s))
+    x = synth.activations(rng, 16, K)
+    y16 = run("q8g64", q, s, x, packed=w)
+    for i in (0, 5, 15):
+        assert np.array_equal(y16[i], run("q8g64", q, s, x[i:i + 1], packed=w)[0])
+
+
+def test_matches_the_plain_gemv_within_rounding():
+    N, K, m = 4000, 2560, 4
+    rng = synth.rng_for(107, 0)
+    q, s = synth.q8g64_weights(rng, N, K)
+    x = synth.activations(rng, m, K)
+    y_mma = run("q8g64", q, s, x)
+    y = canary((m, N))
+    Q.qgemv_q8g64(dev(Q.qpack_q8g64(q, s)), dev(x), y, N, K, m=m)
+    _, a_ref = oracle.q8g64(q, s, x, threads=THREADS)
+    assert np.all(np.abs(y_mma.astype(np.float64) - host(y)) <= 2 * TOL * a_ref)
+
+
+def test_route_counter_names_the_variant():
+    Q.route_counts_reset()
+    rng = synth.rng_for(108, 0)
+    q, s = synth.q8pc_weights(rng, 64, 1280)
+    run("q8pc", q, s, synth.activations(rng, 11, 1280))
+    assert Q.route_count("q8pc_mma_m11") == 1
+    assert Q.variant_name(Q.FMT_Q8PC_MMA, 11, 64, 1280) == "q8pc_mma_m11"

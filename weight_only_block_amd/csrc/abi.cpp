@@ -20,8 +20,10 @@ namespace {
 
 // Route counters: one per (kind, m, log2 G).  kind 0 Q8G64, 1 Q4G32,
 // 2 grouped Q4G32, 3 Q8G128, 4 Q8PC, 5 grouped Q4G32 with SwiGLU,
-// 6 Q8G64 with the argmax epilogue, 7 Q8G128 with the argmax epilogue.
-constexpr int kKinds = 8, kMs = 4, kGs = 7;
+// 6 Q8G64 with the argmax epilogue, 7 Q8G128 with the argmax epilogue,
+// 8..10 the matrix-core kernel for Q8G64, Q8G128, Q8PC (m up to 16; one
+// shape per format, counted in the first G slot).
+constexpr int kKinds = 11, kMs = 16, kGs = 7;
 std::atomic<uint64_t> g_route[kKinds][kMs][kGs];
 
 int log2i(int v)
@@ -41,7 +43,10 @@ const char* kind_name(int kind)
     case 4: return "q8pc";
     case 5: return "q4g32_grouped_swiglu";
     case 6: return "q8g64_argmax";
-    default: return "q8g128_argmax";
+    case 7: return "q8g128_argmax";
+    case 8: return "q8g64_mma";
+    case 9: return "q8g128_mma";
+    default: return "q8pc_mma";
     }
 }
 
@@ -58,7 +63,8 @@ int kind_of(int fmt)
 
 void format_variant(int kind, int m, int G, char* buf, size_t len)
 {
-    snprintf(buf, len, "%s_m%d_g%d_r%d", kind_name(kind), m, G, qg::kRowSlots);
+    if (kind >= 8) snprintf(buf, len, "%s_m%d", kind_name(kind), m);   // one shape per format
+    else snprintf(buf, len, "%s_m%d_g%d_r%d", kind_name(kind), m, G, qg::kRowSlots);
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -82,6 +88,47 @@ qg_status check_gate_up(int64_t N, int64_t K, qg::Layout* L)
 }
 
 // Dense GEMV; with idx_out the argmax epilogue (y may then be null).
+// Matrix-core GEMV (MmaLayout), m = 1..16.
+qg_status check_mma(int fmt, int64_t m, int64_t N, int64_t K, qg::MmaLayout* L)
+{
+    if (m < 1 || m > 16) return QG_ERR_UNSUPPORTED;
+    if (!qg::make_mma_layout(fmt, N, K, L)) return QG_ERR_INVALID_ARG;
+    if (size_t(m) * size_t(K) * 2 > qg::kMaxDynLdsBytes) return QG_ERR_UNSUPPORTED;
+    return QG_OK;
+}
+
+qg_status run_mma(int fmt, int kind, const void* w_packed, const uint16_t* x, float* y, int64_t m,
+                  int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* stream)
+{
+    if (!w_packed || !x || !y) return QG_ERR_INVALID_ARG;
+    if (m == 0) return QG_OK;
+    qg::MmaLayout L;
+    const qg_status st = check_mma(fmt, m, N, K, &L);
+    if (st != QG_OK) return st;
+    if (ldx < K || ldy < N) return QG_ERR_INVALID_ARG;
+    if (!aligned(w_packed, 256) || !aligned(x, 4) || !aligned(y, 4)) return QG_ERR_ALIGNMENT;
+    if (m > 1 && (ldx % 2) != 0) return QG_ERR_ALIGNMENT;
+    qg::MmaParams kp;
+    kp.w = static_cast<const uint8_t*>(w_packed);
+    kp.x = x;
+    kp.y = y;
+    kp.ldx = ldx;
+    kp.ldy = ldy;
+    kp.m = int32_t(m);
+    kp.N = int32_t(N);
+    kp.K = K;
+    kp.J = L.J;
+    kp.tiles = L.tiles;
+    kp.code_bytes = L.code_bytes;
+    kp.meta_tile_bytes = L.meta_tile_bytes;
+    (void)hipGetLastError();
+    if (qg::launch_mma_sized(fmt, kp, size_t(m) * size_t(K) * 2, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return QG_ERR_HIP;
+    g_route[kind][m - 1][0].fetch_add(1, std::memory_order_relaxed);
+    return QG_OK;
+}
+
 qg_status run_dense(int fmt, const void* w_packed, const uint16_t* x, float* y, int64_t m,
                     int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* stream,
                     int32_t* idx_out = nullptr, void* workspace = nullptr, size_t workspace_bytes = 0)
@@ -284,6 +331,24 @@ qg_status qgemv_q8g128_argmax(const void* w_packed, const uint16_t* x_bf16, floa
                      idx_out, workspace, workspace_bytes);
 }
 
+qg_status qgemv_q8g64_mma(const void* w_packed, const uint16_t* x_bf16, float* y, int64_t m,
+                          int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* hip_stream)
+{
+    return run_mma(qg::FMT_Q8G64, 8, w_packed, x_bf16, y, m, N, K, ldx, ldy, hip_stream);
+}
+
+qg_status qgemv_q8g128_mma(const void* w_packed, const uint16_t* x_bf16, float* y, int64_t m,
+                           int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* hip_stream)
+{
+    return run_mma(qg::FMT_Q8G128, 9, w_packed, x_bf16, y, m, N, K, ldx, ldy, hip_stream);
+}
+
+qg_status qgemv_q8pc_mma(const void* w_packed, const uint16_t* x_bf16, float* y, int64_t m,
+                         int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* hip_stream)
+{
+    return run_mma(qg::FMT_Q8PC, 10, w_packed, x_bf16, y, m, N, K, ldx, ldy, hip_stream);
+}
+
 size_t qg_argmax_workspace_size(int64_t m)
 {
     if (m < 0 || m > 65535) return 0;
@@ -331,8 +396,16 @@ qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char* buf, s
     if (!buf || buf_len == 0) return QG_ERR_INVALID_ARG;
     static const int kind_format[kKinds] = {qg::FMT_Q8G64, qg::FMT_Q4G32, qg::FMT_Q4G32,
                                             qg::FMT_Q8G128, qg::FMT_Q8PC, qg::FMT_Q4G32,
-                                            qg::FMT_Q8G64, qg::FMT_Q8G128};
+                                            qg::FMT_Q8G64, qg::FMT_Q8G128, qg::FMT_Q8G64,
+                                            qg::FMT_Q8G128, qg::FMT_Q8PC};
     if (fmt < 0 || fmt >= kKinds) return QG_ERR_INVALID_ARG;
+    if (fmt >= 8) {
+        qg::MmaLayout ML;
+        const qg_status sm = check_mma(kind_format[fmt], m, N, K, &ML);
+        if (sm != QG_OK) return sm;
+        format_variant(fmt, int(m), 4, buf, buf_len);
+        return QG_OK;
+    }
     if ((fmt == 2 || fmt == 5) && m != 1) return QG_ERR_UNSUPPORTED;
     qg::Layout L;
     const qg_status st = fmt == 5 ? check_gate_up(N, K, &L) : check_shape(kind_format[fmt], m, N, K, &L);

@@ -1,0 +1,271 @@
+// Batched decode GEMV (m = 1..16 activation rows) on the gfx950 matrix
+// cores, for the 8-bit formats in the matrix-core layout (layout.h,
+// MmaLayout).  The larger-batch decode of the Qwen3 C++ Reference Runtime
+// (MetaInfer-cpp) README ("B8/B16" kernels with the input rows reused from
+// LDS) is the operation; with up to 16 rows sharing each weight the dot
+// products become a 16 x 16 x 32 bf16 matrix product per 64-wide step:
+//
+//  * A (16 x 32): the activation rows (row i = lane mod 16, zero past m),
+//    read from LDS, where x is staged once per work-group.
+//  * B (32 x 16): 16 weight rows, 16 biased codes per lane exactly as one
+//    wave load brings them in (the layout puts row lane mod 16, k-slice
+//    lane div 16 in lane order), widened to bf16 (integers 0..255 are exact).
+//  * D (16 x 16, fp32): lane l holds D[4*(l div 16) + v][l mod 16].
+//
+// The codes carry a +128 bias, so the MFMA gives D = sum x (q + 128) over a
+// scale group.  A second MFMA with the same A and an all-ones B gives
+// X = sum x over the group in the same arithmetic, so D - 128 X is exactly
+// zero when all codes are zero (scaling B by 128 commutes with rounding).
+// Per group:  acc += s * (D - 128 X)   (s: the row's fp16 group scale, or
+// its fp32 row scale for Q8PC).  Each output is a complete sum when its
+// tile ends, so there is no cross-lane reduction and no atomic.
+//
+// A 16-row tile spans all of K, so a mid-size matrix has few tiles.  With
+// KSPLIT = 4 the four waves of a work-group share each tile, one contiguous
+// quarter of its steps each; at the tile end each wave parks its partial
+// sums in LDS and, after a barrier, the work-group adds the four quarters in
+// K order and stores (the same bits on every run and for every m).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace qg {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
+
+// Eight biased codes (two dwords, k order) -> eight bf16 in k order.
+__device__ __forceinline__ bf16x8 widen8(uint32_t lo, uint32_t hi)
+{
+    const uint32_t v[2] = {lo, hi};
+    u32x4 pr;
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        const float f0 = (float)(v[d] & 0xffu);
+        const float f1 = (float)((v[d] >> 8) & 0xffu);
+        const float f2 = (float)((v[d] >> 16) & 0xffu);
+        const float f3 = (float)(v[d] >> 24);
+        // The top half of the fp32 pattern of an integer 0..255 is its bf16.
+        pr[2 * d] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+        pr[2 * d + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+    }
+    return __builtin_bit_cast(bf16x8, pr);
+}
+
+__device__ __forceinline__ float half_bits(uint32_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xffffu));
+}
+
+// LDS position (16-byte chunk) of chunk c of activation row i: chunks are
+// XOR-swizzled by the row inside each 64-wide step so that the 16 rows an
+// MFMA reads at one k fall into different banks.
+__device__ __forceinline__ int xs_chunk(int i, int c, int chunks_per_row)
+{
+    return i * chunks_per_row + (c ^ (i & 7));
+}
+
+struct MmaItem {
+    u32x4 c;        // 16 biased codes
+    uint32_t s;     // fp16 scale (low half) or fp32 row scale bits
+};
+
+template <int FMT, int DEPTH, int KSPLIT>
+__global__ __launch_bounds__(kThreads) void qgemv_mma(const MmaParams p)
+{
+    static_assert(KSPLIT == 1 || KSPLIT == kThreads / 64, "a K split spans the work-group's waves");
+    extern __shared__ __align__(16) u32x4 xs[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+    const int rho = lane & 15;      // weight row in the tile; activation row of A
+    const int qs = lane >> 4;       // k-slice of the step
+    const int m = p.m;
+    const int64_t J = p.J;
+    const int cpr = int(p.K / 8);   // 16-byte chunks per activation row
+    // Steps per scale group: 1 (Q8G64, and Q8PC, whose row scale is applied
+    // per step), 2 (Q8G128).
+    constexpr int SPG = FMT == FMT_Q8G128 ? 2 : 1;
+
+    // Tile mapping.  KSPLIT = 1: wave gw streams tiles gw, gw + W, ...  and
+    // all their steps.  KSPLIT = 4: work-group b takes tiles b, b + B, ...
+    // and its wave w the steps of scale groups [G w / 4, G (w + 1) / 4) of
+    // each (G = groups per row).
+    int64_t W, gw, j_lo, j_hi;
+    if constexpr (KSPLIT == 1) {
+        W = int64_t(gridDim.x) * (kThreads / 64);
+        gw = int64_t(blockIdx.x) * (kThreads / 64) + wave;
+        j_lo = 0;
+        j_hi = J;
+    } else {
+        // Quarters in whole scale groups, so no group is cut between waves.
+        const int64_t G = J / SPG;
+        W = gridDim.x;
+        gw = blockIdx.x;
+        j_lo = G * wave / KSPLIT * SPG;
+        j_hi = G * (wave + 1) / KSPLIT * SPG;
+    }
+    const int64_t my_tiles = gw < p.tiles ? (p.tiles - 1 - gw) / W + 1 : 0;
+    const int64_t n_items = my_tiles * (j_hi - j_lo);
+
+    const uint8_t* code_lane = p.w + lane * 16;
+    const uint8_t* meta = p.w + p.code_bytes;
+    auto load = [&](MmaItem& it, int64_t tile, int64_t j) {
+        it.c = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(code_lane + (tile * J + j) * 1024));
+        const uint8_t* mt = meta + tile * p.meta_tile_bytes;
+        if (FMT == FMT_Q8PC) it.s = *reinterpret_cast<const uint32_t*>(mt + rho * 4);
+        else it.s = *reinterpret_cast<const uint16_t*>(mt + ((j / SPG) * 16 + rho) * 2);
+    };
+
+    // Weights first: they do not depend on x.  Spare ring slots load item 0
+    // of the matrix (never consumed) so every path issues the same loads.
+    int64_t ld_tile = gw, ld_j = j_lo;
+    MmaItem ring[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+        if (d < n_items) {
+            load(ring[d], ld_tile, ld_j);
+            if (++ld_j == j_hi) { ld_j = j_lo; ld_tile += W; }
+        } else {
+            load(ring[d], 0, 0);
+        }
+    }
+
+    // Stage the m activation rows in LDS (16-byte chunks, swizzled).
+    for (int idx = threadIdx.x; idx < m * cpr; idx += kThreads) {
+        const int i = idx / cpr, c = idx - i * cpr;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(p.x + int64_t(i) * p.ldx + c * 8);
+        u32x4 v;
+        v.x = src[0]; v.y = src[1]; v.z = src[2]; v.w = src[3];
+        xs[xs_chunk(i, c, cpr)] = v;
+    }
+    __syncthreads();
+    // (With the K split every wave takes part in each tile's closing barrier.)
+    if (KSPLIT == 1 && n_items == 0) return;
+    // K split: parked partial sums, two buffers of [wave][lane][4] floats
+    // after the staged activations (one barrier per tile).
+    f32x4* part = reinterpret_cast<f32x4*>(xs + m * cpr);
+    int buf = 0;
+
+    const bool row_live = rho < m;
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    const u32x4 ones4 = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, ones4);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 D = acc, X = acc;
+    int64_t tile = gw, j = j_lo;
+
+    auto consume = [&](const MmaItem& it) {
+        const int c0 = int(j) * 8 + 2 * qs;
+        const u32x4 a0u = row_live ? xs[xs_chunk(rho, c0, cpr)] : zero4;
+        const u32x4 a1u = row_live ? xs[xs_chunk(rho, c0 + 1, cpr)] : zero4;
+        const bf16x8 a0 = __builtin_bit_cast(bf16x8, a0u);
+        const bf16x8 a1 = __builtin_bit_cast(bf16x8, a1u);
+        const bf16x8 b0 = widen8(it.c.x, it.c.y);
+        const bf16x8 b1 = widen8(it.c.z, it.c.w);
+        if (j % SPG == 0) {
+            D = f32x4{0.f, 0.f, 0.f, 0.f};
+            X = D;
+        }
+        D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, D, 0, 0, 0);
+        D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, D, 0, 0, 0);
+        X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, ones, X, 0, 0, 0);
+        X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ones, X, 0, 0, 0);
+        if (j % SPG == SPG - 1) {
+            const float s = FMT == FMT_Q8PC ? __uint_as_float(it.s) : half_bits(it.s);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] = fmaf(s, fmaf(-128.0f, X[v], D[v]), acc[v]);
+        }
+        if (++j == j_hi) {
+            if constexpr (KSPLIT == 1) {
+                const int64_t row = tile * 16 + rho;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int i = 4 * qs + v;
+                    if (i < m && row < p.N) p.y[int64_t(i) * p.ldy + row] = acc[v];
+                }
+            } else {
+                part[(buf * KSPLIT + wave) * 64 + lane] = acc;
+                __syncthreads();
+                // Thread t adds value t of the 16 x 16 output tile over the
+                // four quarters, in K order.
+                const int t = threadIdx.x, L = t >> 2, v = t & 3;
+                float sum = part[(buf * KSPLIT) * 64 + L][v];
+#pragma unroll
+                for (int w = 1; w < KSPLIT; ++w) sum += part[(buf * KSPLIT + w) * 64 + L][v];
+                const int i = 4 * (L >> 4) + v;
+                const int64_t row = tile * 16 + (L & 15);
+                if (i < m && row < p.N) p.y[int64_t(i) * p.ldy + row] = sum;
+                buf ^= 1;
+            }
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            tile += W;
+            j = j_lo;
+        }
+    };
+
+    int64_t n = 0;
+    for (; n + 2 * DEPTH <= n_items; n += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            consume(ring[d]);
+            load(ring[d], ld_tile, ld_j);
+            if (++ld_j == j_hi) { ld_j = j_lo; ld_tile += W; }
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+        if (n + d < n_items) {
+            consume(ring[d]);
+            if (n + DEPTH + d < n_items) {
+                load(ring[d], ld_tile, ld_j);
+                if (++ld_j == j_hi) { ld_j = j_lo; ld_tile += W; }
+            }
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+        if (n + DEPTH + d < n_items) consume(ring[d]);
+}
+
+template <int FMT, int KSPLIT>
+hipError_t launch_fmt(const MmaParams& kp, int64_t waves, size_t lds, hipStream_t s)
+{
+    auto kern = qgemv_mma<FMT, 8, KSPLIT>;
+    static const hipError_t attr = [&] {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 int(kMaxDynLdsBytes));
+        if (e != hipSuccess) (void)hipGetLastError();
+        return e;
+    }();
+    if (attr != hipSuccess && lds > 64 * 1024) return attr;
+    const int64_t wpg = kThreads / 64;
+    hipLaunchKernelGGL(kern, dim3(unsigned((waves + wpg - 1) / wpg)), dim3(kThreads), lds, s, kp);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mma(int fmt, bool ksplit, const MmaParams& kp, int64_t waves, size_t lds,
+                      hipStream_t s)
+{
+    switch (fmt) {
+    case FMT_Q8G64:
+        return ksplit ? launch_fmt<FMT_Q8G64, 4>(kp, waves, lds, s) : launch_fmt<FMT_Q8G64, 1>(kp, waves, lds, s);
+    case FMT_Q8G128:
+        return ksplit ? launch_fmt<FMT_Q8G128, 4>(kp, waves, lds, s) : launch_fmt<FMT_Q8G128, 1>(kp, waves, lds, s);
+    case FMT_Q8PC:
+        return ksplit ? launch_fmt<FMT_Q8PC, 4>(kp, waves, lds, s) : launch_fmt<FMT_Q8PC, 1>(kp, waves, lds, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qg

@@ -87,6 +87,25 @@ QG_DECLARE_LAUNCHER(launch_q4g32);
 QG_DECLARE_LAUNCHER(launch_q8g128);
 QG_DECLARE_LAUNCHER(launch_q8pc);
 #undef QG_DECLARE_LAUNCHER
+// Matrix-core kernel (kern_mma.hip): 8-bit formats in the MmaLayout,
+// m = 1..16 activation rows.
+struct MmaParams {
+    const uint8_t* w;
+    const uint16_t* x;
+    float* y;
+    int64_t ldx, ldy;
+    int32_t m;
+    int32_t N;
+    int64_t K, J, tiles, code_bytes, meta_tile_bytes;
+};
+hipError_t launch_mma(int fmt, bool ksplit, const MmaParams& kp, int64_t waves, size_t lds,
+                      hipStream_t s);
+// LDS the K split adds after the staged activations: two buffers of
+// 4 waves x 64 lanes x 4 floats.
+constexpr size_t kMmaSplitLdsBytes = 2 * 4 * 64 * 16;
+// Picks the wave count for the matrix-core kernel and launches it.
+hipError_t launch_mma_sized(int fmt, const MmaParams& kp, size_t lds, hipStream_t s);
+
 // Dense Q8G64 / Q8G128 with the argmax epilogue (kern_argmax_epi.hip).
 hipError_t launch_argmax_epilogue(int fmt, int m, int G, int shape, const KernelParams& kp,
                                   int64_t waves, size_t lds, hipStream_t s);

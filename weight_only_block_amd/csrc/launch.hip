@@ -9,12 +9,14 @@
 namespace qg {
 
 namespace {
-// Wave counts are per compute unit: a dense sweep runs one 4-wave
+// Wave counts are per compute unit: a dense sweep at m = 1 runs one 4-wave
 // work-group per CU (every CU streams the same bytes and the launch reads
-// one window of about CUs*4 tiles at a time), routed-expert launches two.
-// Both were measured best on MI355X; uneven work-groups per CU (some CUs
-// holding two) measured up to 25% slower.
+// one window of about CUs*4 tiles at a time); at m >= 2, where each byte
+// costs more VALU work, two work-groups per CU hide more of it (LM head at
+// m = 4: 90 -> 79 us); routed-expert launches run two.  All measured best on
+// MI355X; at m = 1, two work-groups per CU measured 7% slower.
 constexpr int64_t kWavesPerCuDense = 4;
+constexpr int64_t kWavesPerCuDenseMulti = 8;
 constexpr int64_t kWavesPerCuGrouped = 8;
 }  // namespace
 
@@ -77,7 +79,9 @@ hipError_t launch(const LaunchArgs& a)
     }();
     const int64_t cus = compute_units();
     const int64_t target_waves =
-        env_waves ? env_waves : cus * (a.grouped ? kWavesPerCuGrouped : kWavesPerCuDense);
+        env_waves ? env_waves
+                  : cus * (a.grouped ? kWavesPerCuGrouped
+                                     : (a.m > 1 ? kWavesPerCuDenseMulti : kWavesPerCuDense));
     int64_t cap = target_waves / slots;
     if (cap < 1) cap = 1;
     // Up to twice the cap, a dense launch is latency-bound rather than
@@ -114,6 +118,42 @@ hipError_t launch(const LaunchArgs& a)
     case FMT_Q8PC: return launch_q8pc(a.m, a.grouped, L.G, shape, kp, w, slots, lds, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_mma_sized(int fmt, const MmaParams& kp, size_t lds, hipStream_t s)
+{
+    // Two 4-wave work-groups per CU.  With at least two tiles per wave the
+    // waves stream whole tiles on their own (k tiles each, the fewest waves
+    // that cover the tiles with k each); with fewer, the four waves of a
+    // work-group split each tile's K (QG_MMA_KSPLIT=0/1 forces it off/on).
+    static const int64_t env_waves = [] {
+        const char* e = getenv("QG_MMA_WAVES");   // tuning sweeps only
+        const long v = e ? strtol(e, nullptr, 10) : 0;
+        return v > 0 ? int64_t(v) : int64_t(0);
+    }();
+    static const int env_split = [] {
+        const char* e = getenv("QG_MMA_KSPLIT");
+        return e ? int(strtol(e, nullptr, 10)) : -1;
+    }();
+    const int64_t cap = env_waves ? env_waves : compute_units() * 8;
+    const int64_t groups_per_row = fmt == FMT_Q8G128 ? kp.J / 2 : kp.J;
+    bool ksplit = kp.tiles < 2 * cap && groups_per_row >= 4;
+    if (env_split >= 0) ksplit = env_split != 0;
+    if (lds + kMmaSplitLdsBytes > kMaxDynLdsBytes) ksplit = false;
+    if (ksplit) {
+        // As many work-groups as can be resident at once (the staged
+        // activations bound how many fit in a CU's LDS), each looping over
+        // its tiles: more than that would run in uneven rounds.
+        const size_t per_wg = lds + kMmaSplitLdsBytes;
+        int64_t per_cu = int64_t(kMaxLdsBytes / per_wg);
+        per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);
+        const int64_t resident = compute_units() * per_cu;
+        const int64_t wgs = kp.tiles < resident ? kp.tiles : resident;
+        return launch_mma(fmt, true, kp, wgs * 4, per_wg, s);
+    }
+    const int64_t k = (kp.tiles + cap - 1) / cap;
+    const int64_t waves = (kp.tiles + k - 1) / k;
+    return launch_mma(fmt, false, kp, waves, lds, s);
 }
 
 }  // namespace qg

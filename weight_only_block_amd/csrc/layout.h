@@ -118,4 +118,57 @@ static inline bool make_gate_up_layout(int64_t N, int64_t K, Layout* L, int64_t*
     return true;
 }
 
+// Matrix-core ("mma") layout of the 8-bit formats, for the kernel that
+// feeds the 16x16x32 bf16 MFMA (m = 1..16 activation rows share the B-side
+// weights).  A tile is 16 rows; a step covers 64 consecutive K.  Item
+// (tile t, step j) is one 1 KiB block at (t*J + j)*1024 in which lane l
+// holds the 16 biased codes (q + 128) of row t*16 + (l mod 16) at
+// k = 64j + 16*(l div 16) .. +15: the MFMA's B operand (lane l supplies
+// column l mod 16, k-slice l div 16) with no shuffling.  Meta after all
+// code blocks:
+//   Q8G64:  [tile][64-group][16 rows] fp16 scales
+//   Q8G128: [tile][128-group][16 rows] fp16 scales
+//   Q8PC:   [tile][16 rows] fp32 row scales
+// K must be a multiple of 64 (128 for Q8G128).  Rows past N are padding
+// (code 0x80, scale 0).  Every weight byte is stored once.
+struct MmaLayout {
+    int fmt;
+    int64_t N, K;
+    int group;              // codes per scale (K for Q8PC)
+    int64_t J;              // 64-wide steps per row
+    int64_t groups;         // scale groups per row
+    int64_t tiles;          // 16-row tiles
+    int64_t code_bytes;
+    int64_t meta_tile_bytes;
+    int64_t total_bytes;    // rounded up to 256
+};
+
+static const int kMmaRows = 16;
+
+static inline bool make_mma_layout(int fmt, int64_t N, int64_t K, MmaLayout* L)
+{
+    int group;
+    switch (fmt) {
+    case FMT_Q8G64: group = 64; break;
+    case FMT_Q8G128: group = 128; break;
+    case FMT_Q8PC: group = 0; break;
+    default: return false;
+    }
+    if (N < 1 || K < 64 || K % 64 != 0 || (group && K % group != 0)) return false;
+    if (N > (int64_t(1) << 31) - 1 || K > (int64_t(1) << 31) - 1) return false;
+    MmaLayout l;
+    l.fmt = fmt;
+    l.N = N;
+    l.K = K;
+    l.group = group ? group : int(K);
+    l.J = K / 64;
+    l.groups = group ? K / group : 1;
+    l.tiles = (N + kMmaRows - 1) / kMmaRows;
+    l.code_bytes = l.tiles * l.J * 1024;
+    l.meta_tile_bytes = fmt == FMT_Q8PC ? 4 * kMmaRows : 2 * kMmaRows * l.groups;
+    l.total_bytes = (l.code_bytes + l.tiles * l.meta_tile_bytes + 255) / 256 * 256;
+    *L = l;
+    return true;
+}
+
 }  // namespace qg

@@ -225,6 +225,72 @@ inline const Q4Rows* gate_up_source(int64_t v, int64_t N, int64_t rps, const Q4R
     return w < rps ? &gate : &up;
 }
 
+// Matrix-core layout (layout.h, MmaLayout): pack / unpack any 8-bit format.
+// scales: fp16 [N][K/group] (Q8G64, Q8G128) or fp32 bit patterns [N] (Q8PC).
+qg_status pack_q8_mma(int fmt, const int8_t* q, const void* scales, int64_t N, int64_t K, void* out,
+                      size_t out_bytes)
+{
+    qg::MmaLayout L;
+    if (!q || !scales || !out) return QG_ERR_INVALID_ARG;
+    if (!qg::make_mma_layout(fmt, N, K, &L)) return QG_ERR_INVALID_ARG;
+    if (out_bytes < size_t(L.total_bytes)) return QG_ERR_INVALID_ARG;
+    uint8_t* o = static_cast<uint8_t*>(out);
+    memset(o, 0x80, size_t(L.code_bytes));
+    memset(o + L.code_bytes, 0, size_t(L.total_bytes - L.code_bytes));
+    const uint16_t* s16 = static_cast<const uint16_t*>(scales);
+    const uint32_t* s32 = static_cast<const uint32_t*>(scales);
+    for (int64_t t = 0; t < L.tiles; ++t)
+        for (int rho = 0; rho < qg::kMmaRows; ++rho) {
+            const int64_t n = t * qg::kMmaRows + rho;
+            if (n >= N) continue;
+            for (int64_t j = 0; j < L.J; ++j)
+                for (int qs = 0; qs < 4; ++qs) {
+                    const int lane = qs * 16 + rho;
+                    const int8_t* src = q + n * K + 64 * j + 16 * qs;
+                    uint8_t* dst = o + (t * L.J + j) * 1024 + lane * 16;
+                    for (int b = 0; b < 16; ++b) dst[b] = uint8_t(int(src[b]) + 128);
+                }
+            uint8_t* meta = o + L.code_bytes + t * L.meta_tile_bytes;
+            if (fmt == qg::FMT_Q8PC) {
+                memcpy(meta + rho * 4, &s32[n], 4);
+            } else {
+                for (int64_t g = 0; g < L.groups; ++g)
+                    memcpy(meta + (g * qg::kMmaRows + rho) * 2, &s16[n * L.groups + g], 2);
+            }
+        }
+    return QG_OK;
+}
+
+qg_status unpack_q8_mma(int fmt, const void* packed, size_t packed_bytes, int64_t N, int64_t K,
+                        int8_t* q, void* scales)
+{
+    qg::MmaLayout L;
+    if (!packed || !q || !scales) return QG_ERR_INVALID_ARG;
+    if (!qg::make_mma_layout(fmt, N, K, &L)) return QG_ERR_INVALID_ARG;
+    if (packed_bytes < size_t(L.total_bytes)) return QG_ERR_INVALID_ARG;
+    const uint8_t* p = static_cast<const uint8_t*>(packed);
+    uint16_t* s16 = static_cast<uint16_t*>(scales);
+    uint32_t* s32 = static_cast<uint32_t*>(scales);
+    for (int64_t t = 0; t < L.tiles; ++t)
+        for (int rho = 0; rho < qg::kMmaRows; ++rho) {
+            const int64_t n = t * qg::kMmaRows + rho;
+            if (n >= N) continue;
+            for (int64_t j = 0; j < L.J; ++j)
+                for (int qs = 0; qs < 4; ++qs) {
+                    const uint8_t* src = p + (t * L.J + j) * 1024 + (qs * 16 + rho) * 16;
+                    for (int b = 0; b < 16; ++b) q[n * K + 64 * j + 16 * qs + b] = int8_t(int(src[b]) - 128);
+                }
+            const uint8_t* meta = p + L.code_bytes + t * L.meta_tile_bytes;
+            if (fmt == qg::FMT_Q8PC) {
+                memcpy(&s32[n], meta + rho * 4, 4);
+            } else {
+                for (int64_t g = 0; g < L.groups; ++g)
+                    memcpy(&s16[n * L.groups + g], meta + (g * qg::kMmaRows + rho) * 2, 2);
+            }
+        }
+    return QG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -311,6 +377,60 @@ qg_status qunpack_q4g32(const void* packed, size_t packed_bytes, int64_t N, int6
     const Q4Rows m{codes, scales_f16, mins_f16};
     unpack_q4(L, K, [&](int64_t n, int64_t* row) { *row = n; return n < N ? &m : nullptr; }, packed);
     return QG_OK;
+}
+
+size_t qpack_q8g64_mma_size(int64_t N, int64_t K)
+{
+    qg::MmaLayout L;
+    return qg::make_mma_layout(qg::FMT_Q8G64, N, K, &L) ? size_t(L.total_bytes) : 0;
+}
+
+size_t qpack_q8g128_mma_size(int64_t N, int64_t K)
+{
+    qg::MmaLayout L;
+    return qg::make_mma_layout(qg::FMT_Q8G128, N, K, &L) ? size_t(L.total_bytes) : 0;
+}
+
+size_t qpack_q8pc_mma_size(int64_t N, int64_t K)
+{
+    qg::MmaLayout L;
+    return qg::make_mma_layout(qg::FMT_Q8PC, N, K, &L) ? size_t(L.total_bytes) : 0;
+}
+
+qg_status qpack_q8g64_mma(const int8_t* q, const uint16_t* scales_f16, int64_t N, int64_t K,
+                          void* out, size_t out_bytes)
+{
+    return pack_q8_mma(qg::FMT_Q8G64, q, scales_f16, N, K, out, out_bytes);
+}
+
+qg_status qpack_q8g128_mma(const int8_t* q, const uint16_t* scales_f16, int64_t N, int64_t K,
+                           void* out, size_t out_bytes)
+{
+    return pack_q8_mma(qg::FMT_Q8G128, q, scales_f16, N, K, out, out_bytes);
+}
+
+qg_status qpack_q8pc_mma(const int8_t* q, const float* scales_f32, int64_t N, int64_t K, void* out,
+                         size_t out_bytes)
+{
+    return pack_q8_mma(qg::FMT_Q8PC, q, scales_f32, N, K, out, out_bytes);
+}
+
+qg_status qunpack_q8g64_mma(const void* packed, size_t packed_bytes, int64_t N, int64_t K, int8_t* q,
+                            uint16_t* scales_f16)
+{
+    return unpack_q8_mma(qg::FMT_Q8G64, packed, packed_bytes, N, K, q, scales_f16);
+}
+
+qg_status qunpack_q8g128_mma(const void* packed, size_t packed_bytes, int64_t N, int64_t K,
+                             int8_t* q, uint16_t* scales_f16)
+{
+    return unpack_q8_mma(qg::FMT_Q8G128, packed, packed_bytes, N, K, q, scales_f16);
+}
+
+qg_status qunpack_q8pc_mma(const void* packed, size_t packed_bytes, int64_t N, int64_t K, int8_t* q,
+                           float* scales_f32)
+{
+    return unpack_q8_mma(qg::FMT_Q8PC, packed, packed_bytes, N, K, q, scales_f32);
 }
 
 size_t qpack_q4g32_gate_up_size(int64_t N, int64_t K)

@@ -29,6 +29,9 @@ FMT_Q8PC = 4
 FMT_GROUPED_Q4G32_SWIGLU = 5
 FMT_Q8G64_ARGMAX = 6
 FMT_Q8G128_ARGMAX = 7
+FMT_Q8G64_MMA = 8
+FMT_Q8G128_MMA = 9
+FMT_Q8PC_MMA = 10
 
 _lib = None
 
@@ -74,6 +77,18 @@ def lib() -> ctypes.CDLL:
             "qunpack_q4g32_gate_up": ([p, sz, i64, i64, p, p, p, p, p, p], st),
             "qgemv_grouped_q4g32_swiglu": ([p, i64, i32, p, i32, p, i64, p, i64, i64, i64, p], st),
             "qg_argmax_workspace_size": ([i64], sz),
+            "qpack_q8g64_mma_size": ([i64, i64], sz),
+            "qpack_q8g128_mma_size": ([i64, i64], sz),
+            "qpack_q8pc_mma_size": ([i64, i64], sz),
+            "qpack_q8g64_mma": ([p, p, i64, i64, p, sz], st),
+            "qpack_q8g128_mma": ([p, p, i64, i64, p, sz], st),
+            "qpack_q8pc_mma": ([p, p, i64, i64, p, sz], st),
+            "qunpack_q8g64_mma": ([p, sz, i64, i64, p, p], st),
+            "qunpack_q8g128_mma": ([p, sz, i64, i64, p, p], st),
+            "qunpack_q8pc_mma": ([p, sz, i64, i64, p, p], st),
+            "qgemv_q8g64_mma": ([p, p, p, i64, i64, i64, i64, i64, p], st),
+            "qgemv_q8g128_mma": ([p, p, p, i64, i64, i64, i64, i64, p], st),
+            "qgemv_q8pc_mma": ([p, p, p, i64, i64, i64, i64, i64, p], st),
             "qgemv_q8g64_argmax": ([p, p, p, p, i64, i64, i64, i64, i64, p, sz, p], st),
             "qgemv_q8g128_argmax": ([p, p, p, p, i64, i64, i64, i64, i64, p, sz, p], st),
             "qg_argmax_f32": ([p, i64, i64, i64, p, p, sz, p], st),
@@ -227,6 +242,54 @@ def qunpack_q4g32(packed: np.ndarray, N: int, K: int):
     return codes, s, mn
 
 
+def _mma_pack(fmt, q, scales, scale_dtype, scale_shape):
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s = np.ascontiguousarray(scales)
+    if s.dtype != scale_dtype:
+        s = np.ascontiguousarray(s, dtype=scale_dtype if scale_dtype != np.uint32 else np.float32)
+    N, K = q.shape
+    size = int(getattr(lib(), "qpack_%s_mma_size" % fmt)(N, K))
+    if size == 0 or s.shape != scale_shape(N, K):
+        raise QGError(QG_ERR_INVALID_ARG, "qpack_%s_mma" % fmt)
+    out = np.empty(size, np.uint8)
+    _check(getattr(lib(), "qpack_%s_mma" % fmt)(_np_ptr(q), _np_ptr(s), N, K, _np_ptr(out), size),
+           "qpack_%s_mma" % fmt)
+    return out
+
+
+def qpack_q8g64_mma(q: np.ndarray, scales_f16: np.ndarray) -> np.ndarray:
+    """Q8G64 weights in the matrix-core layout (for qgemv_q8g64_mma; K % 64 == 0)."""
+    return _mma_pack("q8g64", q, scales_f16, np.uint16, lambda N, K: (N, K // 64))
+
+
+def qpack_q8g128_mma(q: np.ndarray, scales_f16: np.ndarray) -> np.ndarray:
+    """Q8G128 weights in the matrix-core layout (K % 128 == 0)."""
+    return _mma_pack("q8g128", q, scales_f16, np.uint16, lambda N, K: (N, K // 128))
+
+
+def qpack_q8pc_mma(q: np.ndarray, scales_f32: np.ndarray) -> np.ndarray:
+    """Per-output-channel Q8 in the matrix-core layout (K % 64 == 0); scales
+    float32 [N] or their uint32 bit patterns."""
+    return _mma_pack("q8pc", q, scales_f32, np.uint32, lambda N, K: (N,))
+
+
+def qpack_mma_size(fmt: str, N: int, K: int) -> int:
+    return int(getattr(lib(), "qpack_%s_mma_size" % fmt)(N, K))
+
+
+def qunpack_mma(fmt: str, packed: np.ndarray, N: int, K: int):
+    """-> (q int8 [N][K], scales) from a matrix-core buffer of format fmt."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    q = np.empty((N, K), np.int8)
+    if fmt == "q8pc":
+        s = np.empty(N, np.uint32)
+    else:
+        s = np.empty((N, K // (64 if fmt == "q8g64" else 128)), np.uint16)
+    _check(getattr(lib(), "qunpack_%s_mma" % fmt)(_np_ptr(packed), packed.nbytes, N, K, _np_ptr(q),
+                                                  _np_ptr(s)), "qunpack_%s_mma" % fmt)
+    return q, s
+
+
 def qpack_q4g32_gate_up_size(N: int, K: int) -> int:
     return int(lib().qpack_q4g32_gate_up_size(N, K))
 
@@ -303,6 +366,25 @@ def qgemv_q8pc(w_packed, x, y, N: int, K: int, m=None, ldx=None, ldy=None, strea
                check=True):
     """As qgemv_q8g64 for per-output-channel Q8 weights packed by qpack_q8pc."""
     return _dense("qgemv_q8pc", w_packed, x, y, N, K, m, ldx, ldy, stream, check)
+
+
+def qgemv_q8g64_mma(w_packed, x, y, N: int, K: int, m=None, ldx=None, ldy=None, stream=None,
+                    check=True):
+    """Batched decode on the matrix cores, m = 1..16: as qgemv_q8g64 with W
+    packed by qpack_q8g64_mma."""
+    return _dense("qgemv_q8g64_mma", w_packed, x, y, N, K, m, ldx, ldy, stream, check)
+
+
+def qgemv_q8g128_mma(w_packed, x, y, N: int, K: int, m=None, ldx=None, ldy=None, stream=None,
+                     check=True):
+    """As qgemv_q8g64_mma for qpack_q8g128_mma buffers."""
+    return _dense("qgemv_q8g128_mma", w_packed, x, y, N, K, m, ldx, ldy, stream, check)
+
+
+def qgemv_q8pc_mma(w_packed, x, y, N: int, K: int, m=None, ldx=None, ldy=None, stream=None,
+                   check=True):
+    """As qgemv_q8g64_mma for qpack_q8pc_mma buffers."""
+    return _dense("qgemv_q8pc_mma", w_packed, x, y, N, K, m, ldx, ldy, stream, check)
 
 
 def qgemv_grouped_q4g32(w_experts, expert_stride_bytes: int, n_experts: int, expert_ids, x,
@@ -488,6 +570,11 @@ def bound_argmax_f32(x, idx_out, workspace, N: int, m: int = 1, ldx=None, stream
     args = (x.data_ptr(), m, N, ldx, idx_out.data_ptr(), workspace.data_ptr(), nbytes,
             _stream_handle(stream))
     return BoundCall(lib().qg_argmax_f32, args, "qg_argmax_f32", (x, idx_out, workspace))
+
+
+def bound_mma(fmt: str, w_packed, x, y, N: int, K: int, m: int = 1, ldx=None, ldy=None, stream=None):
+    """As bound_q8g64 for qgemv_<fmt>_mma."""
+    return _bind("qgemv_%s_mma" % fmt, w_packed, x, y, N, K, m, ldx, ldy, stream)
 
 
 def bound_q8g64_argmax(w_packed, x, logits, idx_out, workspace, N: int, K: int, m: int = 1,
