@@ -41,15 +41,28 @@ TRAFFIC = {
 }
 
 
-KERNEL_SOURCES = ("kernel_body.h", "kern_q8g64.hip", "kern_q4g32.hip", "kern_q8g128.hip",
-                  "kern_q8pc.hip", "kern_q4g32_swiglu.hip", "kern_argmax_epi.hip", "kern_mma.hip", "argmax.hip",
-                  "argmax.h", "argmax_key.h", "launch.hip", "layout.h", "launch.h")
+# The sources that build each workload's kernels: the digest of these files
+# names the kernel version a TRAFFIC entry was measured on, so an edit to an
+# unrelated kernel leaves the entry valid.
+_COMMON_SOURCES = ("kernel_body.h", "argmax_key.h", "launch.hip", "layout.h", "launch.h")
+KERNEL_SOURCES = {
+    "lm_head": _COMMON_SOURCES + ("kern_q8g64.hip",),
+    "lm_head_q8g128": _COMMON_SOURCES + ("kern_q8g128.hip",),
+    "moe_experts": _COMMON_SOURCES + ("kern_q4g32.hip",),
+    "moe_experts_swiglu": _COMMON_SOURCES + ("kern_q4g32_swiglu.hip", "kern_q4g32.hip"),
+    "lm_head_argmax": _COMMON_SOURCES + ("kern_q8g64.hip", "argmax.hip", "argmax.h"),
+    "lm_head_argmax_fused": _COMMON_SOURCES + ("kern_argmax_epi.hip", "argmax.h"),
+    "lm_head_mma": ("kern_mma.hip", "launch.hip", "layout.h", "launch.h"),
+    "w8a16_qwen3_14b_tp4_mma": ("kern_mma.hip", "launch.hip", "layout.h", "launch.h"),
+}
 
 
-def kernel_source_digest():
+def kernel_source_digest(workload):
     import hashlib
+    files = KERNEL_SOURCES.get(workload, _COMMON_SOURCES + (
+        "kern_q8g64.hip", "kern_q4g32.hip", "kern_q8g128.hip", "kern_q8pc.hip"))
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "weight_only_block_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -556,7 +569,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
     }
-    digest = kernel_source_digest()
+    digest = kernel_source_digest(args.workload)
     if TRAFFIC.get(args.workload, {}).get("source_digest") == digest:
         out["roofline"]["traffic"] = TRAFFIC[args.workload]["bytes_per_launch"]
     out["config"]["kernel_source_digest"] = digest

@@ -319,3 +319,98 @@ def swiglu_tolerance(act_ref, g, u, a_g, a_u, rel: float = 2e-3):
     that overflows for very negative g), so 2^-126 is added."""
     E = swiglu_propagated_bound(g, u, a_g, a_u, rel)
     return (1.0 + 2.0 ** -7) * E + (2.0 ** -8 + 2.0 ** -19) * np.abs(act_ref) + 2.0 ** -126
+
+
+# ------------------------------------------------------- routed-expert MLP
+#
+# The SwiGLU output is written as the down projection's bf16 input (Qwen3
+# C++ Reference Runtime (MetaInfer-cpp) README, milestone M6.5-D: the packed
+# Gate/Up GEMM and SwiGLU write the down projection's input), so the MLP of
+# one routed expert is y = Down_e bf16(silu(Gate_e x) * (Up_e x)).  The pages
+# do not say how that input is rounded; the reading taken is IEEE
+# round-to-nearest-even, the rounding of every other bf16 value here.
+
+def _bf16_quantum_exp(v):
+    # bf16 keeps 8 significant bits over binary32's exponent range: a value
+    # m 2^e (0.5 <= |m| < 1) is a multiple of 2^(e-8) when normal
+    # (e >= -125), and of 2^-133 below that.
+    _, e = np.frexp(v)
+    return np.maximum(e, -125) - 8
+
+
+def _bf16_bits_of_exact(val):
+    # val holds bf16-representable fp64 values (or +-inf, NaN).
+    out = (val.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    out[np.isnan(val)] = 0x7FC0
+    return out
+
+
+def bf16_round(v) -> np.ndarray:
+    """fp64 values -> bf16 bit patterns, rounded to nearest with ties to
+    even (8 significant bits, binary32 exponent range); past the largest
+    finite bf16 the result is +-inf, NaN gives 0x7FC0."""
+    v = np.asarray(v, np.float64)
+    q = _bf16_quantum_exp(v)
+    with np.errstate(invalid="ignore", over="ignore"):
+        # Scaling by a power of two is exact; rint rounds half to even.
+        val = np.ldexp(np.rint(np.ldexp(v, -q)), q)
+        val = np.where(np.abs(val) >= 2.0 ** 128, np.copysign(np.inf, v), val)
+    return _bf16_bits_of_exact(np.where(np.isfinite(v), val, v))
+
+
+def bf16_round_up_abs(v) -> np.ndarray:
+    """The smallest bf16 >= |v| for finite fp64 v (bit patterns), for bounds
+    that a bf16-input GEMV evaluates."""
+    v = np.abs(np.asarray(v, np.float64))
+    if not np.all(np.isfinite(v)):
+        raise ValueError("bf16_round_up_abs needs finite values")
+    q = _bf16_quantum_exp(v)
+    with np.errstate(over="ignore"):
+        val = np.ldexp(np.ceil(np.ldexp(v, -q)), q)
+    return _bf16_bits_of_exact(val)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns -> exact fp64 values (vectorised)."""
+    b = np.asarray(bits, np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+class MlpRef:
+    """Reference values of the routed-expert MLP, each float64 [n_slots][.]:
+    act (fp64 silu(g) u), act_bits (its bf16 rounding, the down projection's
+    input), y (Down act_bits), a_y (sum |w act_bits| of the down GEMV), and
+    the gate/up sums g, u with their sum |w x| a_g, a_u."""
+
+    def __init__(self, act, act_bits, y, a_y, g, u, a_g, a_u):
+        self.act, self.act_bits, self.y, self.a_y = act, act_bits, y, a_y
+        self.g, self.u, self.a_g, self.a_u = g, u, a_g, a_u
+
+
+def expert_mlp(gate_experts, up_experts, down_experts, ids, x_slots, threads: int = 1) -> MlpRef:
+    """Routed-expert MLP: for slot j with e = ids[j],
+      act_j = silu(Gate_e x_j) * (Up_e x_j)      (grouped_q4g32_swiglu)
+      y_j   = Down_e bf16(act_j)                 (grouped_q4g32)."""
+    act, g, u, a_g, a_u = grouped_q4g32_swiglu(gate_experts, up_experts, ids, x_slots,
+                                               threads=threads)
+    act_bits = bf16_round(act)
+    y, a_y = grouped_q4g32(down_experts, ids, act_bits, threads=threads)
+    return MlpRef(act, act_bits, y, a_y, g, u, a_g, a_u)
+
+
+def expert_mlp_tolerance(ref: MlpRef, down_experts, ids, rel: float = 2e-3, threads: int = 1):
+    """Per-output bounds (tol_act, tol_y) for an MLP whose gate/up sums and
+    down sums each meet the GEMV bar (rel sum |w x| of their own inputs).
+
+    tol_act is swiglu_tolerance.  For y: a kernel's bf16 activation a_k is
+    within tol_act of act, so |a_k - a_r| <= d := tol_act + |act - a_r| with
+    a_r = bf16(act).  The down GEMV meets the bar on a_k:
+      |y_k - Down a_k| <= rel sum |w| |a_k| <= rel (a_y + sum |w| d),
+    and |Down a_k - Down a_r| <= sum |w| d, so
+      |y_k - y| <= rel a_y + (1 + rel) sum |w| d.
+    sum |w| d is taken from the oracle GEMV's sum |w x| with d rounded up to
+    bf16, which only enlarges it."""
+    tol_act = swiglu_tolerance(ref.act, ref.g, ref.u, ref.a_g, ref.a_u, rel)
+    d = tol_act + np.abs(ref.act - bf16_to_f64(ref.act_bits))
+    _, wd = grouped_q4g32(down_experts, ids, bf16_round_up_abs(d), threads=threads)
+    return tol_act, rel * ref.a_y + (1.0 + rel) * wd
