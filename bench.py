@@ -34,10 +34,10 @@ METRIC = "effective weight GB/s and % of HBM peak, m=1 quantized GEMV (µs/call)
 # and WRITE_SIZE runs scaled by the same counters on a plain copy kernel of
 # known size.  Valid only for the kernel sources they were taken on.
 TRAFFIC = {
-    "lm_head": {"source_digest": "bf2137386b126dd9", "bytes_per_launch": 401967616},
-    "lm_head_q8g128": {"source_digest": "bf2137386b126dd9", "bytes_per_launch": 395898368},
-    "moe_experts": {"source_digest": "bf2137386b126dd9", "bytes_per_launch": 31824896},
-    "moe_experts_swiglu": {"source_digest": "bf2137386b126dd9", "bytes_per_launch": 47600384},
+    "lm_head": {"source_digest": "66a30d19c66d2d70", "bytes_per_launch": 401967616},
+    "lm_head_q8g128": {"source_digest": "aeb2417dd63abf15", "bytes_per_launch": 395898368},
+    "moe_experts": {"source_digest": "b4af3740f63bac63", "bytes_per_launch": 31824896},
+    "moe_experts_swiglu": {"source_digest": "6211a8ee49214558", "bytes_per_launch": 47600384},
 }
 
 
