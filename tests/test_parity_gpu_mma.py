@@ -116,6 +116,32 @@ def test_ragged_shapes_and_strides(fmt, K, N, m):
     check(fmt, q, s, x, y[:, :N], "%s N=%d K=%d m=%d" % (fmt, N, K, m))
 
 
+# The launch picks how a tile's K is shared: by no wave (many tiles), by
+# the four waves of a work-group (4..63 scale groups per row), or by
+# sixteen (64 or more groups, when the staged x leaves room in LDS); where
+# no split's partial sums fit beside the staged x, four waves share the
+# tile and read x from memory.  These shapes reach each choice, with
+# uneven shares, ragged tiles and both x load widths.
+@pytest.mark.parametrize("fmt,N,K,m,pad", [
+    ("q8g64", 1000, 4096, 3, 0),       # 64 groups: sixteen waves, four groups each
+    ("q8g64", 17, 4160, 12, 2),        # 65 groups: uneven sixteen-way shares
+    ("q8pc", 333, 6400, 9, 0),         # 100 steps over sixteen waves
+    ("q8g128", 500, 8192, 5, 0),       # 64 groups of two steps
+    ("q8g128", 64, 4096, 16, 0),       # 32 groups: four waves
+    ("q8g64", 1000, 4864, 16, 0),      # x fills the LDS: x from memory
+    ("q8pc", 700, 4864, 16, 2),        # the same with 4-byte x loads
+    ("q8g128", 130, 4864, 16, 8),      # 38 groups, x from memory, 16-byte loads
+])
+def test_k_split_choices(fmt, N, K, m, pad):
+    gen = FMT[fmt][0]
+    rng = synth.rng_for(109, N, K, m)
+    q, s = gen(rng, N, K)
+    x = synth.activations(rng, m, K)
+    y = run(fmt, q, s, x, ldx=K + pad, ldy=N + 1)
+    assert np.all(y[:, N:].view(np.uint32) == CANARY_BITS), "wrote past N"
+    check(fmt, q, s, x, y[:, :N], "%s N=%d K=%d m=%d" % (fmt, N, K, m))
+
+
 def test_every_m_from_1_to_16():
     N, K = 3000, 1024
     rng = synth.rng_for(103, 0)

@@ -21,10 +21,13 @@
 // tile ends, so there is no cross-lane reduction and no atomic.
 //
 // A 16-row tile spans all of K, so a mid-size matrix has few tiles.  With
-// KSPLIT = 4 the four waves of a work-group share each tile, one contiguous
-// quarter of its steps each; at the tile end each wave parks its partial
-// sums in LDS and, after a barrier, the work-group adds the four quarters in
-// K order and stores (the same bits on every run and for every m).
+// KSPLIT = 4 (16) the four (sixteen) waves of a work-group share each tile,
+// one contiguous part of its steps each; at the tile end each wave parks
+// its partial sums in LDS and, after a barrier, the work-group adds the
+// parts in K order and stores (the same bits on every run and for every m).
+// Sixteen waves keep four times the bytes in flight per staged copy of x,
+// which matters when the staged activations leave room for one work-group
+// per CU.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,7 +41,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
 
 // Eight biased codes (two dwords, k order) -> eight bf16 in k order.
@@ -75,11 +77,25 @@ __device__ __forceinline__ int xs_chunk(int i, int c, int chunks_per_row)
 struct MmaItem {
     u32x4 c;        // 16 biased codes
     uint32_t s;     // fp16 scale (low half) or fp32 row scale bits
+    u32x4 a0, a1;   // the step's A fragment, when x is read from memory (XG)
 };
 
-template <int FMT, int DEPTH, int KSPLIT>
-__global__ __launch_bounds__(kThreads) void qgemv_mma(const MmaParams p)
+// Threads per work-group: four waves, or sixteen for the 16-way K split.
+template <int KSPLIT>
+constexpr int mma_threads()
 {
+    return KSPLIT == 16 ? 1024 : 256;
+}
+
+// XG: the A fragments come from memory with each item (x is read through
+// the L2, once per tile) instead of from a copy of x staged in LDS; for
+// m * K too large to stage next to a K split's partial sums (built for the
+// four-wave split: with sixteen waves the longer ring does not fit in
+// registers).
+template <int FMT, int DEPTH, int KSPLIT, bool XG>
+__global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaParams p)
+{
+    constexpr int kThreads = mma_threads<KSPLIT>();
     static_assert(KSPLIT == 1 || KSPLIT == kThreads / 64, "a K split spans the work-group's waves");
     extern __shared__ __align__(16) u32x4 xs[];
     const int lane = threadIdx.x & 63;
@@ -94,9 +110,9 @@ __global__ __launch_bounds__(kThreads) void qgemv_mma(const MmaParams p)
     constexpr int SPG = FMT == FMT_Q8G128 ? 2 : 1;
 
     // Tile mapping.  KSPLIT = 1: wave gw streams tiles gw, gw + W, ...  and
-    // all their steps.  KSPLIT = 4: work-group b takes tiles b, b + B, ...
-    // and its wave w the steps of scale groups [G w / 4, G (w + 1) / 4) of
-    // each (G = groups per row).
+    // all their steps.  KSPLIT > 1: work-group b takes tiles b, b + B, ...
+    // and its wave w the steps of scale groups [G w / KSPLIT,
+    // G (w + 1) / KSPLIT) of each (G = groups per row).
     int64_t W, gw, j_lo, j_hi;
     if constexpr (KSPLIT == 1) {
         W = int64_t(gridDim.x) * (kThreads / 64);
@@ -116,16 +132,73 @@ __global__ __launch_bounds__(kThreads) void qgemv_mma(const MmaParams p)
 
     const uint8_t* code_lane = p.w + lane * 16;
     const uint8_t* meta = p.w + p.code_bytes;
+    // 16-byte loads of x when x and its row stride allow them (the same in
+    // every lane), else 4-byte loads.
+    const bool x_wide = ((reinterpret_cast<uintptr_t>(p.x) | uintptr_t(p.ldx * 2)) & 15u) == 0;
+    auto load_x16 = [&](const uint16_t* src) {
+        u32x4 v;
+        if (x_wide) {
+            v = *reinterpret_cast<const u32x4*>(src);
+        } else {
+            const uint32_t* s4 = reinterpret_cast<const uint32_t*>(src);
+            v.x = s4[0]; v.y = s4[1]; v.z = s4[2]; v.w = s4[3];
+        }
+        return v;
+    };
+    const bool row_live = rho < m;
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
     auto load = [&](MmaItem& it, int64_t tile, int64_t j) {
         it.c = __builtin_nontemporal_load(
             reinterpret_cast<const u32x4*>(code_lane + (tile * J + j) * 1024));
         const uint8_t* mt = meta + tile * p.meta_tile_bytes;
         if (FMT == FMT_Q8PC) it.s = *reinterpret_cast<const uint32_t*>(mt + rho * 4);
         else it.s = *reinterpret_cast<const uint16_t*>(mt + ((j / SPG) * 16 + rho) * 2);
+        if constexpr (XG) {
+            // Row rho of x, k = 64 j + 16 qs .. + 15 (lanes past m read nothing).
+            if (row_live) {
+                const uint16_t* src = p.x + int64_t(rho) * p.ldx + j * 64 + qs * 16;
+                it.a0 = load_x16(src);
+                it.a1 = load_x16(src + 8);
+            } else {
+                it.a0 = zero4;
+                it.a1 = zero4;
+            }
+        }
     };
 
-    // Weights first: they do not depend on x.  Spare ring slots load item 0
-    // of the matrix (never consumed) so every path issues the same loads.
+    // Activations first, then weights: vector-memory loads complete in
+    // issue order, so storing the staged x waits for x alone while the
+    // weight ring is already in flight.  A thread loads up to kXBatch
+    // 16-byte chunks of x before it stores any (one memory latency per
+    // batch); past the first batch (long rows, four-wave groups) the
+    // batches also wait for the ring.  Chunks are XOR-swizzled in LDS.
+    constexpr int kXBatch = 8;
+    const int x_total = XG ? 0 : m * cpr;
+    u32x4 xv[kXBatch];
+    auto x_load = [&](int base) {
+#pragma unroll
+        for (int b = 0; b < kXBatch; ++b) {
+            const int idx = base + b * kThreads + int(threadIdx.x);
+            if (idx < x_total) {
+                const int i = idx / cpr, c = idx - i * cpr;
+                xv[b] = load_x16(p.x + int64_t(i) * p.ldx + c * 8);
+            }
+        }
+    };
+    auto x_store = [&](int base) {
+#pragma unroll
+        for (int b = 0; b < kXBatch; ++b) {
+            const int idx = base + b * kThreads + int(threadIdx.x);
+            if (idx < x_total) {
+                const int i = idx / cpr, c = idx - i * cpr;
+                xs[xs_chunk(i, c, cpr)] = xv[b];
+            }
+        }
+    };
+    x_load(0);
+
+    // Spare ring slots load item 0 of the matrix (never consumed) so every
+    // path issues the same loads.
     int64_t ld_tile = gw, ld_j = j_lo;
     MmaItem ring[DEPTH];
 #pragma unroll
@@ -138,24 +211,19 @@ __global__ __launch_bounds__(kThreads) void qgemv_mma(const MmaParams p)
         }
     }
 
-    // Stage the m activation rows in LDS (16-byte chunks, swizzled).
-    for (int idx = threadIdx.x; idx < m * cpr; idx += kThreads) {
-        const int i = idx / cpr, c = idx - i * cpr;
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(p.x + int64_t(i) * p.ldx + c * 8);
-        u32x4 v;
-        v.x = src[0]; v.y = src[1]; v.z = src[2]; v.w = src[3];
-        xs[xs_chunk(i, c, cpr)] = v;
+    x_store(0);
+    for (int base = kXBatch * kThreads; base < x_total; base += kXBatch * kThreads) {
+        x_load(base);
+        x_store(base);
     }
     __syncthreads();
     // (With the K split every wave takes part in each tile's closing barrier.)
     if (KSPLIT == 1 && n_items == 0) return;
     // K split: parked partial sums, two buffers of [wave][lane][4] floats
     // after the staged activations (one barrier per tile).
-    f32x4* part = reinterpret_cast<f32x4*>(xs + m * cpr);
+    f32x4* part = reinterpret_cast<f32x4*>(xs + x_total);
     int buf = 0;
 
-    const bool row_live = rho < m;
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
     const u32x4 ones4 = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
     const bf16x8 ones = __builtin_bit_cast(bf16x8, ones4);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -164,8 +232,14 @@ __global__ __launch_bounds__(kThreads) void qgemv_mma(const MmaParams p)
 
     auto consume = [&](const MmaItem& it) {
         const int c0 = int(j) * 8 + 2 * qs;
-        const u32x4 a0u = row_live ? xs[xs_chunk(rho, c0, cpr)] : zero4;
-        const u32x4 a1u = row_live ? xs[xs_chunk(rho, c0 + 1, cpr)] : zero4;
+        u32x4 a0u, a1u;
+        if constexpr (XG) {
+            a0u = it.a0;
+            a1u = it.a1;
+        } else {
+            a0u = row_live ? xs[xs_chunk(rho, c0, cpr)] : zero4;
+            a1u = row_live ? xs[xs_chunk(rho, c0 + 1, cpr)] : zero4;
+        }
         const bf16x8 a0 = __builtin_bit_cast(bf16x8, a0u);
         const bf16x8 a1 = __builtin_bit_cast(bf16x8, a1u);
         const bf16x8 b0 = widen8(it.c.x, it.c.y);
@@ -194,15 +268,18 @@ __global__ __launch_bounds__(kThreads) void qgemv_mma(const MmaParams p)
             } else {
                 part[(buf * KSPLIT + wave) * 64 + lane] = acc;
                 __syncthreads();
-                // Thread t adds value t of the 16 x 16 output tile over the
-                // four quarters, in K order.
-                const int t = threadIdx.x, L = t >> 2, v = t & 3;
-                float sum = part[(buf * KSPLIT) * 64 + L][v];
+                // Thread t < 256 adds value t of the 16 x 16 output tile over
+                // the parts, in K order.
+                const int t = threadIdx.x;
+                if (t < 256) {
+                    const int L = t >> 2, v = t & 3;
+                    float sum = part[(buf * KSPLIT) * 64 + L][v];
 #pragma unroll
-                for (int w = 1; w < KSPLIT; ++w) sum += part[(buf * KSPLIT + w) * 64 + L][v];
-                const int i = 4 * (L >> 4) + v;
-                const int64_t row = tile * 16 + (L & 15);
-                if (i < m && row < p.N) p.y[int64_t(i) * p.ldy + row] = sum;
+                    for (int w = 1; w < KSPLIT; ++w) sum += part[(buf * KSPLIT + w) * 64 + L][v];
+                    const int i = 4 * (L >> 4) + v;
+                    const int64_t row = tile * 16 + (L & 15);
+                    if (i < m && row < p.N) p.y[int64_t(i) * p.ldy + row] = sum;
+                }
                 buf ^= 1;
             }
             acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -235,10 +312,12 @@ __global__ __launch_bounds__(kThreads) void qgemv_mma(const MmaParams p)
         if (n + DEPTH + d < n_items) consume(ring[d]);
 }
 
-template <int FMT, int KSPLIT>
+template <int FMT, int KSPLIT, bool XG>
 hipError_t launch_fmt(const MmaParams& kp, int64_t waves, size_t lds, hipStream_t s)
 {
-    auto kern = qgemv_mma<FMT, 8, KSPLIT>;
+    // Ring depth 8, or 6 with sixteen waves (a CU then has 96 KiB in
+    // flight), or 4 when the ring also carries the A fragments.
+    auto kern = qgemv_mma<FMT, XG ? 4 : (KSPLIT == 16 ? 6 : 8), KSPLIT, XG>;
     static const hipError_t attr = [&] {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -247,23 +326,35 @@ hipError_t launch_fmt(const MmaParams& kp, int64_t waves, size_t lds, hipStream_
         return e;
     }();
     if (attr != hipSuccess && lds > 64 * 1024) return attr;
-    const int64_t wpg = kThreads / 64;
-    hipLaunchKernelGGL(kern, dim3(unsigned((waves + wpg - 1) / wpg)), dim3(kThreads), lds, s, kp);
+    constexpr int threads = mma_threads<KSPLIT>();
+    const int64_t wpg = threads / 64;
+    hipLaunchKernelGGL(kern, dim3(unsigned((waves + wpg - 1) / wpg)), dim3(threads), lds, s, kp);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_mma(int fmt, bool ksplit, const MmaParams& kp, int64_t waves, size_t lds,
+namespace {
+template <int FMT>
+hipError_t launch_split(int ksplit, bool xg, const MmaParams& kp, int64_t waves, size_t lds, hipStream_t s)
+{
+    switch (ksplit * 2 + (xg ? 1 : 0)) {
+    case 2: return launch_fmt<FMT, 1, false>(kp, waves, lds, s);
+    case 8: return launch_fmt<FMT, 4, false>(kp, waves, lds, s);
+    case 9: return launch_fmt<FMT, 4, true>(kp, waves, lds, s);
+    case 32: return launch_fmt<FMT, 16, false>(kp, waves, lds, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+}  // namespace
+
+hipError_t launch_mma(int fmt, int ksplit, bool xg, const MmaParams& kp, int64_t waves, size_t lds,
                       hipStream_t s)
 {
     switch (fmt) {
-    case FMT_Q8G64:
-        return ksplit ? launch_fmt<FMT_Q8G64, 4>(kp, waves, lds, s) : launch_fmt<FMT_Q8G64, 1>(kp, waves, lds, s);
-    case FMT_Q8G128:
-        return ksplit ? launch_fmt<FMT_Q8G128, 4>(kp, waves, lds, s) : launch_fmt<FMT_Q8G128, 1>(kp, waves, lds, s);
-    case FMT_Q8PC:
-        return ksplit ? launch_fmt<FMT_Q8PC, 4>(kp, waves, lds, s) : launch_fmt<FMT_Q8PC, 1>(kp, waves, lds, s);
+    case FMT_Q8G64: return launch_split<FMT_Q8G64>(ksplit, xg, kp, waves, lds, s);
+    case FMT_Q8G128: return launch_split<FMT_Q8G128>(ksplit, xg, kp, waves, lds, s);
+    case FMT_Q8PC: return launch_split<FMT_Q8PC>(ksplit, xg, kp, waves, lds, s);
     default: return hipErrorInvalidValue;
     }
 }

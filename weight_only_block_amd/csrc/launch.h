@@ -98,11 +98,17 @@ struct MmaParams {
     int32_t N;
     int64_t K, J, tiles, code_bytes, meta_tile_bytes;
 };
-hipError_t launch_mma(int fmt, bool ksplit, const MmaParams& kp, int64_t waves, size_t lds,
+// ksplit: 1 (each wave streams whole tiles), 4 or 16 (the waves of a
+// work-group share each tile's K).  xg (with ksplit 4): x is read from
+// memory with each item instead of staged in LDS.
+hipError_t launch_mma(int fmt, int ksplit, bool xg, const MmaParams& kp, int64_t waves, size_t lds,
                       hipStream_t s);
-// LDS the K split adds after the staged activations: two buffers of
-// 4 waves x 64 lanes x 4 floats.
-constexpr size_t kMmaSplitLdsBytes = 2 * 4 * 64 * 16;
+// LDS a K split adds after the staged activations: two buffers of
+// ksplit waves x 64 lanes x 4 floats.
+constexpr size_t mma_split_lds_bytes(int ksplit)
+{
+    return size_t(2) * ksplit * 64 * 16;
+}
 // Picks the wave count for the matrix-core kernel and launches it.
 hipError_t launch_mma_sized(int fmt, const MmaParams& kp, size_t lds, hipStream_t s);
 

@@ -124,8 +124,12 @@ hipError_t launch_mma_sized(int fmt, const MmaParams& kp, size_t lds, hipStream_
 {
     // Two 4-wave work-groups per CU.  With at least two tiles per wave the
     // waves stream whole tiles on their own (k tiles each, the fewest waves
-    // that cover the tiles with k each); with fewer, the four waves of a
-    // work-group split each tile's K (QG_MMA_KSPLIT=0/1 forces it off/on).
+    // that cover the tiles with k each); with fewer, the waves of a
+    // work-group split each tile's K: sixteen of them where the row has at
+    // least 64 scale groups and the LDS allows, else four (with fewer
+    // groups per wave the per-tile fold outweighs the wider stream:
+    // 5120 x 1280 Q8PC at m = 8 measured 6.3 us with four, 7.5 with sixteen).
+    // QG_MMA_KSPLIT = 1, 4 or 16 forces the split (tuning sweeps).
     static const int64_t env_waves = [] {
         const char* e = getenv("QG_MMA_WAVES");   // tuning sweeps only
         const long v = e ? strtol(e, nullptr, 10) : 0;
@@ -135,25 +139,46 @@ hipError_t launch_mma_sized(int fmt, const MmaParams& kp, size_t lds, hipStream_
         const char* e = getenv("QG_MMA_KSPLIT");
         return e ? int(strtol(e, nullptr, 10)) : -1;
     }();
+    static const int env_xg = [] {
+        const char* e = getenv("QG_MMA_XG");        // tuning sweeps only
+        return e ? int(strtol(e, nullptr, 10)) : -1;
+    }();
     const int64_t cap = env_waves ? env_waves : compute_units() * 8;
     const int64_t groups_per_row = fmt == FMT_Q8G128 ? kp.J / 2 : kp.J;
-    bool ksplit = kp.tiles < 2 * cap && groups_per_row >= 4;
-    if (env_split >= 0) ksplit = env_split != 0;
-    if (lds + kMmaSplitLdsBytes > kMaxDynLdsBytes) ksplit = false;
-    if (ksplit) {
-        // As many work-groups as can be resident at once (the staged
-        // activations bound how many fit in a CU's LDS), each looping over
-        // its tiles: more than that would run in uneven rounds.
-        const size_t per_wg = lds + kMmaSplitLdsBytes;
+    int split = (kp.tiles < 2 * cap && groups_per_row >= 4) ? 4 : 1;
+    if (split == 4 && groups_per_row >= 64) split = 16;
+    if ((env_split == 4 && groups_per_row >= 4) || (env_split == 16 && groups_per_row >= 16) || env_split == 1)
+        split = env_split;
+    // Where the sixteen-way split's partial sums do not fit beside the
+    // staged x, four waves share the tile; where the staged x would leave
+    // room for only one such group per CU, they read x from memory with
+    // each item instead (two groups per CU; Q8PC at m = 15 measured 15.0 ->
+    // 11.1 us on 1792 x 5120 and 17.2 -> 13.6 us on 5120 x 4352).
+    // QG_MMA_XG = 0/1 forces staging on / x from memory (tuning sweeps).
+    bool xg = false;
+    if (split == 16 && lds + mma_split_lds_bytes(16) > kMaxDynLdsBytes) split = 4;
+    if (split == 4 && lds + mma_split_lds_bytes(4) > kMaxLdsBytes / 2) xg = true;
+    if (split == 4 && env_xg == 0 && lds + mma_split_lds_bytes(4) <= kMaxDynLdsBytes) xg = false;
+    if (split > 1 && env_xg == 1) {
+        split = 4;
+        xg = true;
+    }
+    if (split > 1) {
+        // As many work-groups as can be resident at once (staged x bounds
+        // how many fit in a CU's LDS; a 16-wave group takes a CU's share of
+        // waves), each looping over its tiles: more than that would run in
+        // uneven rounds.
+        const size_t per_wg = (xg ? 0 : lds) + mma_split_lds_bytes(split);
         int64_t per_cu = int64_t(kMaxLdsBytes / per_wg);
-        per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);
+        const int64_t most = split == 16 ? 1 : 2;
+        per_cu = per_cu < 1 ? 1 : (per_cu > most ? most : per_cu);
         const int64_t resident = compute_units() * per_cu;
         const int64_t wgs = kp.tiles < resident ? kp.tiles : resident;
-        return launch_mma(fmt, true, kp, wgs * 4, per_wg, s);
+        return launch_mma(fmt, split, xg, kp, wgs * split, per_wg, s);
     }
     const int64_t k = (kp.tiles + cap - 1) / cap;
     const int64_t waves = (kp.tiles + k - 1) / k;
-    return launch_mma(fmt, false, kp, waves, lds, s);
+    return launch_mma(fmt, 1, false, kp, waves, lds, s);
 }
 
 }  // namespace qg
