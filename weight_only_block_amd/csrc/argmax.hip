@@ -53,12 +53,15 @@ __global__ __launch_bounds__(kThreads) void argmax_rows(const float* __restrict_
 #pragma unroll
         for (int w = 1; w < kThreads / 64; ++w) best = max_key(best, wave_best[w]);
         atomicMax(&keys[row], (unsigned long long)best);
-        __threadfence();
+        // The max is performed before this work-group counts itself; keys
+        // are read back only through atomics, so waiting for the atomic
+        // (no fence, which would write back and invalidate the whole L2)
+        // is all the ordering needed.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         const unsigned int done = atomicAdd(&counts[row], 1u);
         if (done == gridDim.x - 1) {
             // Every other work-group of the row has added its key: read the
             // winner and leave the workspace zeroed for the next call.
-            __threadfence();
             const unsigned long long fin = atomicExch(&keys[row], 0ull);
             atomicExch(&counts[row], 0u);
             out[row] = key_index(fin);

@@ -492,10 +492,13 @@ __device__ __forceinline__ void finish_argmax(uint64_t (&best)[M], const KernelP
             for (int w = 1; w < 4; ++w) k = max_key(k, wave_best[w][i]);
             atomicMax(&p.keys[i], (unsigned long long)k);
         }
-        __threadfence();
+        // The maxima are performed before this work-group counts itself.
+        // Keys are read back only through atomics, so a wait for the
+        // atomics (not a fence, which writes back and invalidates the whole
+        // L2) is all the ordering needed.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         const unsigned int done = atomicAdd(p.counter, 1u);
         if (done == gridDim.x - 1) {
-            __threadfence();
 #pragma unroll
             for (int i = 0; i < M; ++i) p.idx_out[i] = key_index(atomicExch(&p.keys[i], 0ull));
             atomicExch(p.counter, 0u);
