@@ -54,6 +54,7 @@ KERNEL_SOURCES = {
     "lm_head_argmax_fused": _COMMON_SOURCES + ("kern_argmax_epi.hip", "argmax.h"),
     "lm_head_mma": ("kern_mma.hip", "launch.hip", "layout.h", "launch.h"),
     "w8a16_qwen3_14b_tp4_mma": ("kern_mma.hip", "launch.hip", "layout.h", "launch.h"),
+    "q4_k2560_mma": ("kern_mma.hip", "launch.hip", "layout.h", "launch.h"),
 }
 
 
@@ -212,6 +213,11 @@ def setup_mma(torch, Q, synth, name, m):
         mats = [("lm_head", "q8g64", N, K)]
         desc = "lm_head Q8G64 matrix-core GEMV m=%d, N=151936 x K=2560" % m
         wid = synth.WORKLOAD_IDS["lm_head"]
+    elif name == "q4_k2560_mma":
+        mats = synth.Q4_K2560
+        desc = ("Q4G32 K=2560 family on the matrix cores m=%d: gate/up 2560->9216, "
+                "down 9216->2560" % m)
+        wid = synth.WORKLOAD_IDS["q4_k2560"]
     else:
         mats = synth.W8A16_QWEN3_14B_TP4
         desc = ("Qwen3-14B TP4 rank-local decode layer, per-output-channel W8A16 on the matrix "
@@ -223,6 +229,9 @@ def setup_mma(torch, Q, synth, name, m):
         if fmt == "q8g64":
             packed = Q.qpack_q8g64_mma(*synth.q8g64_weights(rng, N, K))
             wbytes += synth.bytes_q8g64(N, K)
+        elif fmt == "q4g32":
+            packed = Q.qpack_q4g32_mma(*synth.q4g32_weights(rng, N, K))
+            wbytes += synth.bytes_q4g32(N, K)
         else:
             packed = Q.qpack_q8pc_mma(*synth.q8pc_weights(rng, N, K))
             wbytes += synth.bytes_q8pc(N, K)
@@ -240,7 +249,7 @@ def setup_mma(torch, Q, synth, name, m):
         for c in calls[i % copies]:
             c()
 
-    fid = {"q8g64": Q.FMT_Q8G64_MMA, "q8pc": Q.FMT_Q8PC_MMA}
+    fid = {"q8g64": Q.FMT_Q8G64_MMA, "q8pc": Q.FMT_Q8PC_MMA, "q4g32": Q.FMT_Q4G32_MMA}
     info = {"workload": desc, "format": mats[0][1] + "_mma", "m": m, "weight_copies": copies,
             "period": copies,
             "kernel": sorted({Q.variant_name(fid[f], m, N, K) for (_, f, N, K) in mats})}
@@ -482,9 +491,10 @@ def main():
                     choices=["lm_head", "lm_head_q8g128", "lm_head_argmax", "lm_head_argmax_fused",
                              "moe_experts", "moe_experts_merged",
                              "moe_experts_swiglu", "q8_small", "qwen3_0.6b", "q4_k2560", "w8a16_qwen3_14b_tp4",
-                             "lm_head_mma", "w8a16_qwen3_14b_tp4_mma"])
+                             "lm_head_mma", "w8a16_qwen3_14b_tp4_mma", "q4_k2560_mma"])
     ap.add_argument("--m", type=int, default=1,
-                    help="activation rows (q4_k2560, w8a16_qwen3_14b_tp4: 1..4; *_mma: 1..16)")
+                    help="activation rows (q4_k2560, w8a16_qwen3_14b_tp4: 1..4; *_mma: 1..16, "
+                         "with m*K*2 <= 159 KiB: q4_k2560_mma up to 8, w8a16 up to 15)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the timed steps from a captured HIP graph (no host launch cost)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -495,6 +505,11 @@ def main():
     ap.add_argument("--no-secondary", dest="secondary", action="store_false",
                     help="skip timing the other workload beside the headline")
     args = ap.parse_args()
+    mma_k = {"lm_head_mma": 2560, "w8a16_qwen3_14b_tp4_mma": 5120, "q4_k2560_mma": 9216}
+    if args.workload in mma_k and not 1 <= args.m <= min(16, 159 * 1024 // (2 * mma_k[args.workload])):
+        print("--m %d is outside what %s stages (m * K * 2 <= 159 KiB, m <= 16)"
+              % (args.m, args.workload), file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print("bench.py measures one GPU: the decode GEMV is single-GPU work here "
               "(--gpus %d requested). Rows of N shard across GPUs with no exchange; "
@@ -518,7 +533,7 @@ def main():
 
     def measure(name):
         t0 = time.time()
-        if name in ("lm_head_mma", "w8a16_qwen3_14b_tp4_mma"):
+        if name in ("lm_head_mma", "w8a16_qwen3_14b_tp4_mma", "q4_k2560_mma"):
             step, alg, wbytes, launches, info, cpu = setup_mma(torch, Q, synth, name, args.m)
         elif name == "lm_head_argmax_fused":
             step, alg, wbytes, launches, info, cpu = setup_lm_head_argmax_fused(torch, Q, synth)

@@ -185,6 +185,20 @@ qg_status qgemv_q8g128_mma(const void *w_packed, const uint16_t *x_bf16, float *
                            int64_t N, int64_t K, int64_t ldx, int64_t ldy, void *hip_stream);
 qg_status qgemv_q8pc_mma(const void *w_packed, const uint16_t *x_bf16, float *y, int64_t m,
                          int64_t N, int64_t K, int64_t ldx, int64_t ldy, void *hip_stream);
+/* Q4G32 on the matrix cores, same contract: one MFMA per 32-group (its
+ * B operand the group's codes widened to bf16, its sum then scaled, plus
+ * the min times the group's activation sum).  Packed by qpack_q4g32_mma
+ * (1 KiB wave load = 16 rows x 128 K); K must be a multiple of 128 (else
+ * QG_ERR_INVALID_ARG).  codes, scales and mins are the canonical Q4G32
+ * arrays of qpack_q4g32. */
+size_t    qpack_q4g32_mma_size(int64_t N, int64_t K);
+qg_status qpack_q4g32_mma(const uint8_t *codes, const uint16_t *scales_f16,
+                          const uint16_t *mins_f16, int64_t N, int64_t K, void *out,
+                          size_t out_bytes);
+qg_status qunpack_q4g32_mma(const void *packed, size_t packed_bytes, int64_t N, int64_t K,
+                            uint8_t *codes, uint16_t *scales_f16, uint16_t *mins_f16);
+qg_status qgemv_q4g32_mma(const void *w_packed, const uint16_t *x_bf16, float *y, int64_t m,
+                          int64_t N, int64_t K, int64_t ldx, int64_t ldy, void *hip_stream);
 
 /* Routed-expert decode (one token, several experts), Q4G32:
  *   for each slot j < n_slots, with e = expert_ids_dev[j]:
@@ -294,7 +308,8 @@ uint64_t qg_route_count(const char *variant);
  * into buf (fmt 0 = Q8G64, 1 = Q4G32, 2 = grouped Q4G32, 3 = Q8G128,
  * 4 = Q8PC, 5 = grouped Q4G32 with SwiGLU, N = gate rows, 6 = Q8G64 with
  * the argmax epilogue, 7 = Q8G128 with the argmax epilogue, 8/9/10 = the
- * matrix-core kernel for Q8G64/Q8G128/Q8PC, named "<fmt>_mma_m<m>").
+ * matrix-core kernel for Q8G64/Q8G128/Q8PC, named "<fmt>_mma_m<m>", 11 =
+ * the matrix-core kernel for Q4G32, "q4g32_mma_m<m>").
  * Returns QG_OK or the status the call itself would return for that shape. */
 qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char *buf, size_t buf_len);
 

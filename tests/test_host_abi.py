@@ -349,3 +349,41 @@ def test_mma_pack_roundtrip_sizes_and_validation(fmt):
     assert f(W, X, Y, 0, 16, K, K, 16, None) == Q.QG_OK
     fid = {"q8g64": Q.FMT_Q8G64_MMA, "q8g128": Q.FMT_Q8G128_MMA, "q8pc": Q.FMT_Q8PC_MMA}[fmt]
     assert Q.variant_name(fid, 16, 151936, 2560) == "%s_mma_m16" % fmt
+
+
+def test_q4g32_mma_pack_layout_and_roundtrip():
+    # Layout of the Q4G32 matrix-core packing, checked against the
+    # documented formula: in block (tile t, step j), lane l = 16 qs + rho,
+    # dword g holds the codes of row 16 t + rho at k = 128 j + 32 g + 8 qs + e
+    # with e at nibble position (0, 4, 1, 5, 2, 6, 3, 7)[e]; then the meta
+    # dwords scale | min << 16 at [tile][step][row][group].
+    N, K = 37, 384
+    n_idx = np.arange(N)[:, None]
+    k_idx = np.arange(K)[None, :]
+    c = (k_idx * 7 + n_idx * 3) % 16
+    codes = synth.pack_nibbles(c)
+    s = (np.arange(N * K // 32, dtype=np.uint16).reshape(N, K // 32) + 0x3C00).astype(np.uint16)
+    mn = (np.arange(N * K // 32, dtype=np.uint16).reshape(N, K // 32) + 0x8000).astype(np.uint16)
+    buf = Q.qpack_q4g32_mma(codes, s, mn)
+    tiles, J = (N + 15) // 16, K // 128
+    assert buf.nbytes == Q.qpack_mma_size("q4g32", N, K) == -(-(tiles * J * 1024 + tiles * J * 256) // 256) * 256
+    pos = (0, 4, 1, 5, 2, 6, 3, 7)
+    for (t, j, qs, rho, g) in [(0, 0, 0, 0, 0), (1, 2, 3, 5, 1), (2, 1, 2, 4, 3), (0, 2, 1, 15, 2)]:
+        n = 16 * t + rho
+        word = int(buf[(t * J + j) * 1024 + (16 * qs + rho) * 16 + 4 * g:][:4].view(np.uint32)[0])
+        for e in range(8):
+            assert (word >> (4 * pos[e])) & 15 == c[n, 128 * j + 32 * g + 8 * qs + e]
+        meta = buf[tiles * J * 1024 + ((t * J + j) * 16 + rho) * 16 + 4 * g:][:4].view(np.uint16)
+        assert meta[0] == s[n, 4 * j + g] and meta[1] == mn[n, 4 * j + g]
+    # Padding rows of the last tile are all zero.
+    pad = buf[(2 * J) * 1024:(3 * J) * 1024].reshape(J, 64, 16)[:, [16 * q + r for q in range(4) for r in range(5, 16)]]
+    assert not pad.any()
+    c2, s2, m2 = Q.qunpack_mma("q4g32", buf, N, K)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, s) and np.array_equal(m2, mn)
+    assert Q.qpack_mma_size("q4g32", N, 320) == 0          # K not a multiple of 128
+    f = Q.lib().qgemv_q4g32_mma
+    assert f(W, X, Y, 1, 16, 320, 320, 16, None) == Q.QG_ERR_INVALID_ARG
+    assert f(W, X, Y, 17, 16, 256, 256, 16, None) == Q.QG_ERR_UNSUPPORTED
+    assert f(W + 16, X, Y, 1, 16, 256, 256, 16, None) == Q.QG_ERR_ALIGNMENT
+    assert f(W, X, Y, 0, 16, 256, 256, 16, None) == Q.QG_OK
+    assert Q.variant_name(Q.FMT_Q4G32_MMA, 4, 9216, 2560) == "q4g32_mma_m4"

@@ -21,9 +21,10 @@ namespace {
 // Route counters: one per (kind, m, log2 G).  kind 0 Q8G64, 1 Q4G32,
 // 2 grouped Q4G32, 3 Q8G128, 4 Q8PC, 5 grouped Q4G32 with SwiGLU,
 // 6 Q8G64 with the argmax epilogue, 7 Q8G128 with the argmax epilogue,
-// 8..10 the matrix-core kernel for Q8G64, Q8G128, Q8PC (m up to 16; one
-// shape per format, counted in the first G slot).
-constexpr int kKinds = 11, kMs = 16, kGs = 7;
+// 8..10 the matrix-core kernel for Q8G64, Q8G128, Q8PC, 11 the matrix-core
+// kernel for Q4G32 (m up to 16; one shape per format, counted in the first
+// G slot).
+constexpr int kKinds = 12, kMs = 16, kGs = 7;
 std::atomic<uint64_t> g_route[kKinds][kMs][kGs];
 
 int log2i(int v)
@@ -46,7 +47,8 @@ const char* kind_name(int kind)
     case 7: return "q8g128_argmax";
     case 8: return "q8g64_mma";
     case 9: return "q8g128_mma";
-    default: return "q8pc_mma";
+    case 10: return "q8pc_mma";
+    default: return "q4g32_mma";
     }
 }
 
@@ -343,6 +345,12 @@ qg_status qgemv_q8g128_mma(const void* w_packed, const uint16_t* x_bf16, float* 
     return run_mma(qg::FMT_Q8G128, 9, w_packed, x_bf16, y, m, N, K, ldx, ldy, hip_stream);
 }
 
+qg_status qgemv_q4g32_mma(const void* w_packed, const uint16_t* x_bf16, float* y, int64_t m,
+                          int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* hip_stream)
+{
+    return run_mma(qg::FMT_Q4G32, 11, w_packed, x_bf16, y, m, N, K, ldx, ldy, hip_stream);
+}
+
 qg_status qgemv_q8pc_mma(const void* w_packed, const uint16_t* x_bf16, float* y, int64_t m,
                          int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* hip_stream)
 {
@@ -397,7 +405,7 @@ qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char* buf, s
     static const int kind_format[kKinds] = {qg::FMT_Q8G64, qg::FMT_Q4G32, qg::FMT_Q4G32,
                                             qg::FMT_Q8G128, qg::FMT_Q8PC, qg::FMT_Q4G32,
                                             qg::FMT_Q8G64, qg::FMT_Q8G128, qg::FMT_Q8G64,
-                                            qg::FMT_Q8G128, qg::FMT_Q8PC};
+                                            qg::FMT_Q8G128, qg::FMT_Q8PC, qg::FMT_Q4G32};
     if (fmt < 0 || fmt >= kKinds) return QG_ERR_INVALID_ARG;
     if (fmt >= 8) {
         qg::MmaLayout ML;

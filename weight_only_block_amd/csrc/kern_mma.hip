@@ -61,6 +61,17 @@ __device__ __forceinline__ bf16x8 widen8(uint32_t lo, uint32_t hi)
     return __builtin_bit_cast(bf16x8, pr);
 }
 
+// Eight Q4 codes (one dword in the matrix-core nibble order, layout.h) ->
+// eight bf16 values 128 + c in k order: the bf16 pattern 0x4300 | c is
+// exactly 128 + c for c = 0..15.
+__device__ __forceinline__ bf16x8 widen_q4(uint32_t u)
+{
+    u32x4 pr;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pr[t] = ((u >> (4 * t)) & 0x000F000Fu) | 0x43004300u;
+    return __builtin_bit_cast(bf16x8, pr);
+}
+
 __device__ __forceinline__ float half_bits(uint32_t h)
 {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xffffu));
@@ -75,8 +86,9 @@ __device__ __forceinline__ int xs_chunk(int i, int c, int chunks_per_row)
 }
 
 struct MmaItem {
-    u32x4 c;        // 16 biased codes
-    uint32_t s;     // fp16 scale (low half) or fp32 row scale bits
+    u32x4 c;        // 16 biased 8-bit codes, or 32 Q4 codes (one dword per 32-group)
+    uint32_t s;     // fp16 scale (low half) or fp32 row scale bits (8-bit formats)
+    u32x4 m4;       // Q4G32: scale | min << 16 of the row's four groups
     u32x4 a0, a1;   // the step's A fragment, when x is read from memory (XG)
 };
 
@@ -106,8 +118,11 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
     const int64_t J = p.J;
     const int cpr = int(p.K / 8);   // 16-byte chunks per activation row
     // Steps per scale group: 1 (Q8G64, and Q8PC, whose row scale is applied
-    // per step), 2 (Q8G128).
+    // per step), 2 (Q8G128).  A Q4G32 step (128 K) holds four whole groups,
+    // so K splits fall between steps there too.
     constexpr int SPG = FMT == FMT_Q8G128 ? 2 : 1;
+    constexpr bool Q4 = FMT == FMT_Q4G32;
+    static_assert(!(Q4 && XG), "Q4G32 stages x in LDS");
 
     // Tile mapping.  KSPLIT = 1: wave gw streams tiles gw, gw + W, ...  and
     // all their steps.  KSPLIT > 1: work-group b takes tiles b, b + B, ...
@@ -151,7 +166,8 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
         it.c = __builtin_nontemporal_load(
             reinterpret_cast<const u32x4*>(code_lane + (tile * J + j) * 1024));
         const uint8_t* mt = meta + tile * p.meta_tile_bytes;
-        if (FMT == FMT_Q8PC) it.s = *reinterpret_cast<const uint32_t*>(mt + rho * 4);
+        if constexpr (Q4) it.m4 = *reinterpret_cast<const u32x4*>(mt + (j * 16 + rho) * 16);
+        else if (FMT == FMT_Q8PC) it.s = *reinterpret_cast<const uint32_t*>(mt + rho * 4);
         else it.s = *reinterpret_cast<const uint16_t*>(mt + ((j / SPG) * 16 + rho) * 2);
         if constexpr (XG) {
             // Row rho of x, k = 64 j + 16 qs .. + 15 (lanes past m read nothing).
@@ -231,31 +247,50 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
     int64_t tile = gw, j = j_lo;
 
     auto consume = [&](const MmaItem& it) {
-        const int c0 = int(j) * 8 + 2 * qs;
-        u32x4 a0u, a1u;
-        if constexpr (XG) {
-            a0u = it.a0;
-            a1u = it.a1;
-        } else {
-            a0u = row_live ? xs[xs_chunk(rho, c0, cpr)] : zero4;
-            a1u = row_live ? xs[xs_chunk(rho, c0 + 1, cpr)] : zero4;
-        }
-        const bf16x8 a0 = __builtin_bit_cast(bf16x8, a0u);
-        const bf16x8 a1 = __builtin_bit_cast(bf16x8, a1u);
-        const bf16x8 b0 = widen8(it.c.x, it.c.y);
-        const bf16x8 b1 = widen8(it.c.z, it.c.w);
-        if (j % SPG == 0) {
-            D = f32x4{0.f, 0.f, 0.f, 0.f};
-            X = D;
-        }
-        D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, D, 0, 0, 0);
-        D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, D, 0, 0, 0);
-        X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, ones, X, 0, 0, 0);
-        X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ones, X, 0, 0, 0);
-        if (j % SPG == SPG - 1) {
-            const float s = FMT == FMT_Q8PC ? __uint_as_float(it.s) : half_bits(it.s);
+        if constexpr (Q4) {
+            // One MFMA per 32-group: D = sum x (c + 128), X = sum x, then
+            // acc += s (D - 128 X) + min X.
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[v] = fmaf(s, fmaf(-128.0f, X[v], D[v]), acc[v]);
+            for (int g = 0; g < 4; ++g) {
+                const int c = int(j) * 16 + 4 * g + qs;
+                const u32x4 au = row_live ? xs[xs_chunk(rho, c, cpr)] : zero4;
+                const bf16x8 a = __builtin_bit_cast(bf16x8, au);
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 Dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, widen_q4(it.c[g]), z, 0, 0, 0);
+                const f32x4 Xg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones, z, 0, 0, 0);
+                const float s = half_bits(it.m4[g]);
+                const float mn = half_bits(it.m4[g] >> 16);
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[v] = fmaf(mn, Xg[v], fmaf(s, fmaf(-128.0f, Xg[v], Dg[v]), acc[v]));
+            }
+        } else {
+            const int c0 = int(j) * 8 + 2 * qs;
+            u32x4 a0u, a1u;
+            if constexpr (XG) {
+                a0u = it.a0;
+                a1u = it.a1;
+            } else {
+                a0u = row_live ? xs[xs_chunk(rho, c0, cpr)] : zero4;
+                a1u = row_live ? xs[xs_chunk(rho, c0 + 1, cpr)] : zero4;
+            }
+            const bf16x8 a0 = __builtin_bit_cast(bf16x8, a0u);
+            const bf16x8 a1 = __builtin_bit_cast(bf16x8, a1u);
+            const bf16x8 b0 = widen8(it.c.x, it.c.y);
+            const bf16x8 b1 = widen8(it.c.z, it.c.w);
+            if (j % SPG == 0) {
+                D = f32x4{0.f, 0.f, 0.f, 0.f};
+                X = D;
+            }
+            D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, D, 0, 0, 0);
+            D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, D, 0, 0, 0);
+            X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, ones, X, 0, 0, 0);
+            X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ones, X, 0, 0, 0);
+            if (j % SPG == SPG - 1) {
+                const float s = FMT == FMT_Q8PC ? __uint_as_float(it.s) : half_bits(it.s);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] = fmaf(s, fmaf(-128.0f, X[v], D[v]), acc[v]);
+            }
         }
         if (++j == j_hi) {
             if constexpr (KSPLIT == 1) {
@@ -316,8 +351,12 @@ template <int FMT, int KSPLIT, bool XG>
 hipError_t launch_fmt(const MmaParams& kp, int64_t waves, size_t lds, hipStream_t s)
 {
     // Ring depth 8, or 6 with sixteen waves (a CU then has 96 KiB in
-    // flight), or 4 when the ring also carries the A fragments.
-    auto kern = qgemv_mma<FMT, XG ? 4 : (KSPLIT == 16 ? 6 : 8), KSPLIT, XG>;
+    // flight), or 4 when the ring also carries the A fragments.  Q4G32
+    // items carry 16 bytes of meta per lane: 6, or 4 with sixteen waves.
+    constexpr int depth = XG ? 4
+                        : FMT == FMT_Q4G32 ? (KSPLIT == 16 ? 4 : 6)
+                                           : (KSPLIT == 16 ? 6 : 8);
+    auto kern = qgemv_mma<FMT, depth, KSPLIT, XG>;
     static const hipError_t attr = [&] {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -341,7 +380,9 @@ hipError_t launch_split(int ksplit, bool xg, const MmaParams& kp, int64_t waves,
     switch (ksplit * 2 + (xg ? 1 : 0)) {
     case 2: return launch_fmt<FMT, 1, false>(kp, waves, lds, s);
     case 8: return launch_fmt<FMT, 4, false>(kp, waves, lds, s);
-    case 9: return launch_fmt<FMT, 4, true>(kp, waves, lds, s);
+    case 9:
+        if constexpr (FMT != FMT_Q4G32) return launch_fmt<FMT, 4, true>(kp, waves, lds, s);
+        return hipErrorInvalidValue;
     case 32: return launch_fmt<FMT, 16, false>(kp, waves, lds, s);
     default: return hipErrorInvalidValue;
     }
@@ -355,6 +396,7 @@ hipError_t launch_mma(int fmt, int ksplit, bool xg, const MmaParams& kp, int64_t
     case FMT_Q8G64: return launch_split<FMT_Q8G64>(ksplit, xg, kp, waves, lds, s);
     case FMT_Q8G128: return launch_split<FMT_Q8G128>(ksplit, xg, kp, waves, lds, s);
     case FMT_Q8PC: return launch_split<FMT_Q8PC>(ksplit, xg, kp, waves, lds, s);
+    case FMT_Q4G32: return launch_split<FMT_Q4G32>(ksplit, xg, kp, waves, lds, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -163,6 +163,12 @@ hipError_t launch_mma_sized(int fmt, const MmaParams& kp, size_t lds, hipStream_
         split = 4;
         xg = true;
     }
+    // Q4G32 always stages x (a step's A fragments are four 16-byte chunks):
+    // without room for the four-wave split's sums it streams whole tiles.
+    if (fmt == FMT_Q4G32 && xg) {
+        xg = false;
+        if (lds + mma_split_lds_bytes(4) > kMaxDynLdsBytes) split = 1;
+    }
     if (split > 1) {
         // As many work-groups as can be resident at once (staged x bounds
         // how many fit in a CU's LDS; a 16-wave group takes a CU's share of

@@ -131,11 +131,22 @@ static inline bool make_gate_up_layout(int64_t N, int64_t K, Layout* L, int64_t*
 //   Q8PC:   [tile][16 rows] fp32 row scales
 // K must be a multiple of 64 (128 for Q8G128).  Rows past N are padding
 // (code 0x80, scale 0).  Every weight byte is stored once.
+//
+// Q4G32 uses the same tiles with 128-wide steps, so that an item is still
+// 1 KiB: lane l holds four dwords, dword g being the eight codes of row
+// t*16 + (l mod 16) at k = 128j + 32g + 8*(l div 16) + e (e = 0..7), one
+// nibble each, in the nibble order e = 0, 2, 4, 6, 1, 3, 5, 7.  Masking
+// the dword (and its shifts by 4, 8, 12) with 0x000F000F then yields the
+// bf16 pairs (e0, e1), (e2, e3), (e4, e5), (e6, e7): the B operand of one
+// MFMA, which thus covers exactly one 32-group.  Meta after all code
+// blocks: [tile][step][16 rows][4 groups] dwords, scale (fp16) in the low
+// half and min (fp16) in the high half.  K must be a multiple of 128.
+// Rows past N are padding (code 0, scale 0, min 0).
 struct MmaLayout {
     int fmt;
     int64_t N, K;
     int group;              // codes per scale (K for Q8PC)
-    int64_t J;              // 64-wide steps per row
+    int64_t J;              // steps per row (64 wide; 128 for Q4G32)
     int64_t groups;         // scale groups per row
     int64_t tiles;          // 16-row tiles
     int64_t code_bytes;
@@ -152,20 +163,24 @@ static inline bool make_mma_layout(int fmt, int64_t N, int64_t K, MmaLayout* L)
     case FMT_Q8G64: group = 64; break;
     case FMT_Q8G128: group = 128; break;
     case FMT_Q8PC: group = 0; break;
+    case FMT_Q4G32: group = 32; break;
     default: return false;
     }
-    if (N < 1 || K < 64 || K % 64 != 0 || (group && K % group != 0)) return false;
+    const int64_t step = fmt == FMT_Q4G32 ? 128 : 64;
+    if (N < 1 || K < step || K % step != 0 || (group && K % group != 0)) return false;
     if (N > (int64_t(1) << 31) - 1 || K > (int64_t(1) << 31) - 1) return false;
     MmaLayout l;
     l.fmt = fmt;
     l.N = N;
     l.K = K;
     l.group = group ? group : int(K);
-    l.J = K / 64;
+    l.J = K / step;
     l.groups = group ? K / group : 1;
     l.tiles = (N + kMmaRows - 1) / kMmaRows;
     l.code_bytes = l.tiles * l.J * 1024;
-    l.meta_tile_bytes = fmt == FMT_Q8PC ? 4 * kMmaRows : 2 * kMmaRows * l.groups;
+    l.meta_tile_bytes = fmt == FMT_Q8PC ? 4 * kMmaRows
+                      : fmt == FMT_Q4G32 ? 4 * kMmaRows * l.groups
+                                         : 2 * kMmaRows * l.groups;
     l.total_bytes = (l.code_bytes + l.tiles * l.meta_tile_bytes + 255) / 256 * 256;
     *L = l;
     return true;

@@ -291,6 +291,86 @@ qg_status unpack_q8_mma(int fmt, const void* packed, size_t packed_bytes, int64_
     return QG_OK;
 }
 
+// Q4G32 in the matrix-core layout (layout.h): codes [N][K/2] canonical
+// (even k in the low nibble), scale and min fp16 [N][K/32].
+constexpr int kQ4MmaNibble[8] = {0, 4, 1, 5, 2, 6, 3, 7};   // position of e in the dword
+
+qg_status pack_q4_mma(const uint8_t* codes, const uint16_t* scale, const uint16_t* minv, int64_t N,
+                      int64_t K, void* out, size_t out_bytes)
+{
+    qg::MmaLayout L;
+    if (!codes || !scale || !minv || !out) return QG_ERR_INVALID_ARG;
+    if (!qg::make_mma_layout(qg::FMT_Q4G32, N, K, &L)) return QG_ERR_INVALID_ARG;
+    if (out_bytes < size_t(L.total_bytes)) return QG_ERR_INVALID_ARG;
+    uint8_t* o = static_cast<uint8_t*>(out);
+    memset(o, 0, size_t(L.total_bytes));
+    const int64_t G = K / 32;
+    for (int64_t t = 0; t < L.tiles; ++t)
+        for (int rho = 0; rho < qg::kMmaRows; ++rho) {
+            const int64_t n = t * qg::kMmaRows + rho;
+            if (n >= N) continue;
+            for (int64_t j = 0; j < L.J; ++j) {
+                for (int qs = 0; qs < 4; ++qs) {
+                    uint8_t* dst = o + (t * L.J + j) * 1024 + (qs * 16 + rho) * 16;
+                    for (int g = 0; g < 4; ++g) {
+                        uint32_t word = 0;
+                        for (int e = 0; e < 8; ++e) {
+                            const int64_t k = 128 * j + 32 * g + 8 * qs + e;
+                            const uint32_t c = (codes[n * (K / 2) + k / 2] >> (4 * (k & 1))) & 0xFu;
+                            word |= c << (4 * kQ4MmaNibble[e]);
+                        }
+                        memcpy(dst + 4 * g, &word, 4);
+                    }
+                }
+                uint8_t* meta = o + L.code_bytes + t * L.meta_tile_bytes + (j * qg::kMmaRows + rho) * 16;
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t gi = n * G + 4 * j + g;
+                    memcpy(meta + 4 * g, &scale[gi], 2);
+                    memcpy(meta + 4 * g + 2, &minv[gi], 2);
+                }
+            }
+        }
+    return QG_OK;
+}
+
+qg_status unpack_q4_mma(const void* packed, size_t packed_bytes, int64_t N, int64_t K, uint8_t* codes,
+                        uint16_t* scale, uint16_t* minv)
+{
+    qg::MmaLayout L;
+    if (!packed || !codes || !scale || !minv) return QG_ERR_INVALID_ARG;
+    if (!qg::make_mma_layout(qg::FMT_Q4G32, N, K, &L)) return QG_ERR_INVALID_ARG;
+    if (packed_bytes < size_t(L.total_bytes)) return QG_ERR_INVALID_ARG;
+    const uint8_t* p = static_cast<const uint8_t*>(packed);
+    const int64_t G = K / 32;
+    memset(codes, 0, size_t(N * (K / 2)));
+    for (int64_t t = 0; t < L.tiles; ++t)
+        for (int rho = 0; rho < qg::kMmaRows; ++rho) {
+            const int64_t n = t * qg::kMmaRows + rho;
+            if (n >= N) continue;
+            for (int64_t j = 0; j < L.J; ++j) {
+                for (int qs = 0; qs < 4; ++qs) {
+                    const uint8_t* src = p + (t * L.J + j) * 1024 + (qs * 16 + rho) * 16;
+                    for (int g = 0; g < 4; ++g) {
+                        uint32_t word;
+                        memcpy(&word, src + 4 * g, 4);
+                        for (int e = 0; e < 8; ++e) {
+                            const int64_t k = 128 * j + 32 * g + 8 * qs + e;
+                            const uint8_t c = uint8_t((word >> (4 * kQ4MmaNibble[e])) & 0xFu);
+                            codes[n * (K / 2) + k / 2] |= uint8_t(c << (4 * (k & 1)));
+                        }
+                    }
+                }
+                const uint8_t* meta = p + L.code_bytes + t * L.meta_tile_bytes + (j * qg::kMmaRows + rho) * 16;
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t gi = n * G + 4 * j + g;
+                    memcpy(&scale[gi], meta + 4 * g, 2);
+                    memcpy(&minv[gi], meta + 4 * g + 2, 2);
+                }
+            }
+        }
+    return QG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -413,6 +493,24 @@ qg_status qpack_q8pc_mma(const int8_t* q, const float* scales_f32, int64_t N, in
                          size_t out_bytes)
 {
     return pack_q8_mma(qg::FMT_Q8PC, q, scales_f32, N, K, out, out_bytes);
+}
+
+size_t qpack_q4g32_mma_size(int64_t N, int64_t K)
+{
+    qg::MmaLayout L;
+    return qg::make_mma_layout(qg::FMT_Q4G32, N, K, &L) ? size_t(L.total_bytes) : 0;
+}
+
+qg_status qpack_q4g32_mma(const uint8_t* codes, const uint16_t* scales_f16, const uint16_t* mins_f16,
+                          int64_t N, int64_t K, void* out, size_t out_bytes)
+{
+    return pack_q4_mma(codes, scales_f16, mins_f16, N, K, out, out_bytes);
+}
+
+qg_status qunpack_q4g32_mma(const void* packed, size_t packed_bytes, int64_t N, int64_t K,
+                            uint8_t* codes, uint16_t* scales_f16, uint16_t* mins_f16)
+{
+    return unpack_q4_mma(packed, packed_bytes, N, K, codes, scales_f16, mins_f16);
 }
 
 qg_status qunpack_q8g64_mma(const void* packed, size_t packed_bytes, int64_t N, int64_t K, int8_t* q,

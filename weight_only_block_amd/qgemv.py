@@ -32,6 +32,7 @@ FMT_Q8G128_ARGMAX = 7
 FMT_Q8G64_MMA = 8
 FMT_Q8G128_MMA = 9
 FMT_Q8PC_MMA = 10
+FMT_Q4G32_MMA = 11
 
 _lib = None
 
@@ -89,6 +90,10 @@ def lib() -> ctypes.CDLL:
             "qgemv_q8g64_mma": ([p, p, p, i64, i64, i64, i64, i64, p], st),
             "qgemv_q8g128_mma": ([p, p, p, i64, i64, i64, i64, i64, p], st),
             "qgemv_q8pc_mma": ([p, p, p, i64, i64, i64, i64, i64, p], st),
+            "qpack_q4g32_mma_size": ([i64, i64], sz),
+            "qpack_q4g32_mma": ([p, p, p, i64, i64, p, sz], st),
+            "qunpack_q4g32_mma": ([p, sz, i64, i64, p, p, p], st),
+            "qgemv_q4g32_mma": ([p, p, p, i64, i64, i64, i64, i64, p], st),
             "qgemv_q8g64_argmax": ([p, p, p, p, i64, i64, i64, i64, i64, p, sz, p], st),
             "qgemv_q8g128_argmax": ([p, p, p, p, i64, i64, i64, i64, i64, p, sz, p], st),
             "qg_argmax_f32": ([p, i64, i64, i64, p, p, sz, p], st),
@@ -273,13 +278,38 @@ def qpack_q8pc_mma(q: np.ndarray, scales_f32: np.ndarray) -> np.ndarray:
     return _mma_pack("q8pc", q, scales_f32, np.uint32, lambda N, K: (N,))
 
 
+def qpack_q4g32_mma(codes: np.ndarray, scales_f16: np.ndarray, mins_f16: np.ndarray) -> np.ndarray:
+    """Q4G32 canonical arrays (as qpack_q4g32) in the matrix-core layout
+    (for qgemv_q4g32_mma; K % 128 == 0)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    s = np.ascontiguousarray(scales_f16, dtype=np.uint16)
+    mn = np.ascontiguousarray(mins_f16, dtype=np.uint16)
+    N, half_k = codes.shape
+    K = 2 * half_k
+    size = qpack_mma_size("q4g32", N, K)
+    if size == 0 or s.shape != (N, K // 32) or mn.shape != (N, K // 32):
+        raise QGError(QG_ERR_INVALID_ARG, "qpack_q4g32_mma")
+    out = np.empty(size, np.uint8)
+    _check(lib().qpack_q4g32_mma(_np_ptr(codes), _np_ptr(s), _np_ptr(mn), N, K, _np_ptr(out), size),
+           "qpack_q4g32_mma")
+    return out
+
+
 def qpack_mma_size(fmt: str, N: int, K: int) -> int:
     return int(getattr(lib(), "qpack_%s_mma_size" % fmt)(N, K))
 
 
 def qunpack_mma(fmt: str, packed: np.ndarray, N: int, K: int):
-    """-> (q int8 [N][K], scales) from a matrix-core buffer of format fmt."""
+    """-> (q int8 [N][K], scales) from a matrix-core buffer of format fmt
+    ((codes, scales, mins) as qunpack_q4g32 for q4g32)."""
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    if fmt == "q4g32":
+        codes = np.empty((N, K // 2), np.uint8)
+        sc = np.empty((N, K // 32), np.uint16)
+        mn = np.empty((N, K // 32), np.uint16)
+        _check(lib().qunpack_q4g32_mma(_np_ptr(packed), packed.nbytes, N, K, _np_ptr(codes), _np_ptr(sc),
+                                       _np_ptr(mn)), "qunpack_q4g32_mma")
+        return codes, sc, mn
     q = np.empty((N, K), np.int8)
     if fmt == "q8pc":
         s = np.empty(N, np.uint32)
@@ -379,6 +409,12 @@ def qgemv_q8g128_mma(w_packed, x, y, N: int, K: int, m=None, ldx=None, ldy=None,
                      check=True):
     """As qgemv_q8g64_mma for qpack_q8g128_mma buffers."""
     return _dense("qgemv_q8g128_mma", w_packed, x, y, N, K, m, ldx, ldy, stream, check)
+
+
+def qgemv_q4g32_mma(w_packed, x, y, N: int, K: int, m=None, ldx=None, ldy=None, stream=None,
+                    check=True):
+    """As qgemv_q8g64_mma for qpack_q4g32_mma buffers."""
+    return _dense("qgemv_q4g32_mma", w_packed, x, y, N, K, m, ldx, ldy, stream, check)
 
 
 def qgemv_q8pc_mma(w_packed, x, y, N: int, K: int, m=None, ldx=None, ldy=None, stream=None,
