@@ -211,8 +211,10 @@ qg_status qgemv_q4g32_mma(const void *w_packed, const uint16_t *x_bf16, float *y
  *                     e * expert_stride_bytes; 256-B aligned
  *   expert_stride_bytes  multiple of 256, >= qpack_q4g32_size(N, K)
  *   expert_ids_dev    device int32[n_slots]; read by the kernel, not the
- *                     host.  A slot whose id is outside [0, n_experts) reads
- *                     no weights and has its N outputs set to NaN.
+ *                     host.  A slot whose id is outside [0, n_experts)
+ *                     streams no weights (it may read the first KiB of
+ *                     matrix 0, never memory outside the buffer) and has
+ *                     its N outputs set to NaN.
  *   n_slots           1..64
  *   x_slot_stride     elements between slot activations; 0 = one shared x
  *                     (gate and up projections); even
@@ -242,7 +244,8 @@ qg_status qgemv_grouped_q4g32(const void *w_experts_packed, int64_t expert_strid
  *                     e * expert_stride_bytes; 256-B aligned
  *   expert_stride_bytes  multiple of 256, >= qpack_q4g32_gate_up_size(N, K)
  *   expert_ids_dev    as qgemv_grouped_q4g32; a slot with an id outside
- *                     [0, n_experts) reads no weights and gets NaN (0x7FC0)
+ *                     [0, n_experts) streams no weights (as there) and
+ *                     gets NaN (0x7FC0)
  *   act_bf16          device bf16, 2-byte aligned; act_slot_stride >= N
  *   n_slots, x_bf16, x_slot_stride, K: as qgemv_grouped_q4g32. */
 qg_status qgemv_grouped_q4g32_swiglu(const void *w_gate_up_packed, int64_t expert_stride_bytes,

@@ -558,7 +558,6 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
         tstep = W;
         my_tiles = gw < p.tiles ? (p.tiles - 1 - gw) / W + 1 : 0;
     }
-    const int64_t n_items = my_tiles * p.J;
     static_assert(EPI != 1 || (FMT == FMT_Q4G32 && M == 1 && GROUPED && R == 2),
                   "the SwiGLU epilogue is built for grouped Q4G32 gate/up pairs");
     static_assert(EPI != 2 || (!GROUPED && WAVES == 4), "the argmax epilogue is for dense launches");
@@ -567,33 +566,24 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     const uint16_t* x = p.x + int64_t(slot) * p.x_slot_stride;
 
     // Activations first (see XStage), then the expert id, then the weights.
+    // The id is read with a scalar load; nothing branches on it before the
+    // weight ring is issued, so the x loads go out while the id is in
+    // flight instead of waiting behind it.
     XStage<FMT, M, kThreads> xstage;
     xstage.fetch(p, x, U);
 
     const uint8_t* w = p.w;
+    bool bad_expert = false;
     if (GROUPED) {
         const int e = p.ids[slot];
-        if (e < 0 || e >= p.n_experts) {
-            // Out-of-range expert id: read no weights, report NaN outputs.
-            // The whole work-group takes this branch (e is per work-group),
-            // so no barrier below is skipped by part of it.
-            for (int64_t n = 0, t = t0; n < my_tiles; ++n, t += tstep) {
-                if constexpr (EPI == 1) {
-                    for (int idx = lane; idx < RPS; idx += 64) {
-                        const int64_t row = t * RPS + idx;
-                        if (row < p.n_out) act[row] = uint16_t(0x7fc0);
-                    }
-                } else {
-                    for (int idx = lane; idx < TR; idx += 64) {
-                        const int64_t row = t * TR + idx;
-                        if (row < p.N) y[row] = __builtin_nanf("");
-                    }
-                }
-            }
-            return;
-        }
-        w += int64_t(e) * p.expert_stride;
+        // Out-of-range expert id: the work-group streams nothing (the ring's
+        // spare loads read the first item of expert 0, which is in bounds)
+        // and reports NaN outputs below.  e is per work-group, so every
+        // wave takes the same path.
+        bad_expert = e < 0 || e >= p.n_experts;
+        if (!bad_expert) w += int64_t(e) * p.expert_stride;
     }
+    const int64_t n_items = bad_expert ? 0 : my_tiles * p.J;
 
     const uint8_t* code_lane = w + lane * 16;
     int lane_meta;
@@ -639,6 +629,22 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     }
 #undef QG_FILL_RING
     __syncthreads();
+    if (GROUPED && bad_expert) {
+        for (int64_t n = 0, t = t0; n < my_tiles; ++n, t += tstep) {
+            if constexpr (EPI == 1) {
+                for (int idx = lane; idx < RPS; idx += 64) {
+                    const int64_t row = t * RPS + idx;
+                    if (row < p.n_out) act[row] = uint16_t(0x7fc0);
+                }
+            } else {
+                for (int idx = lane; idx < TR; idx += 64) {
+                    const int64_t row = t * TR + idx;
+                    if (row < p.N) y[row] = __builtin_nanf("");
+                }
+            }
+        }
+        return;
+    }
     // (The argmax epilogue needs every wave at its closing barrier.)
     if (EPI != 2 && n_items == 0) return;
     uint64_t best[M];
