@@ -212,9 +212,9 @@ qg_status qgemv_q4g32_mma(const void *w_packed, const uint16_t *x_bf16, float *y
  *   expert_stride_bytes  multiple of 256, >= qpack_q4g32_size(N, K)
  *   expert_ids_dev    device int32[n_slots]; read by the kernel, not the
  *                     host.  A slot whose id is outside [0, n_experts)
- *                     streams no weights (it may read the first KiB of
- *                     matrix 0, never memory outside the buffer) and has
- *                     its N outputs set to NaN.
+ *                     streams no weights (it may read the first work item
+ *                     of matrix 0, never memory outside the buffer) and
+ *                     has its N outputs set to NaN.
  *   n_slots           1..64
  *   x_slot_stride     elements between slot activations; 0 = one shared x
  *                     (gate and up projections); even
