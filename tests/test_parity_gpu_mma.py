@@ -218,3 +218,36 @@ def test_route_counter_names_the_variant():
     run("q8pc", q, s, synth.activations(rng, 11, 1280))
     assert Q.route_count("q8pc_mma_m11") == 1
     assert Q.variant_name(Q.FMT_Q8PC_MMA, 11, 64, 1280) == "q8pc_mma_m11"
+
+
+@pytest.mark.parametrize("fmt,N,K,m", [("q8pc", 1792, 5120, 8),      # sixteen-wave K split
+                                       ("q8g64", 70000, 512, 12),     # whole tiles per wave
+                                       ("q8pc", 300, 4864, 16)])      # x read from memory
+def test_graph_replays_match_eager_calls(fmt, N, K, m):
+    # Captured once, replayed with new activations in place: every replay
+    # equals an eager call bit for bit (the K split's LDS fold and the
+    # staging are per launch, nothing is recorded that replays differently).
+    gen, pack, gemv, _, _ = FMT[fmt]
+    rng = synth.rng_for(120, N, K)
+    q, s = gen(rng, N, K)
+    w = dev(pack(q, s))
+    x = dev(synth.activations(rng, m, K))
+    y = canary((m, N))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call = Q.bound_mma(fmt, w, x, y, N, K, m=m)
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        call()
+    for r in range(3):
+        x.copy_(dev(synth.activations(synth.rng_for(120, 100 + r), m, K)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = host(y).copy()
+        ye = canary((m, N))
+        gemv(w, x, ye, N, K, m=m)
+        assert np.array_equal(got, host(ye)), "replay %d" % r

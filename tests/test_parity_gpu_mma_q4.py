@@ -195,3 +195,30 @@ def test_route_counter_names_the_variant():
     run(W, synth.activations(rng, 11, 1280))
     assert Q.route_count("q4g32_mma_m11") == 1
     assert Q.variant_name(Q.FMT_Q4G32_MMA, 11, 64, 1280) == "q4g32_mma_m11"
+
+
+def test_graph_replays_match_eager_calls():
+    N, K, m = 9216, 2560, 8
+    rng = synth.rng_for(121, 0)
+    W = synth.q4g32_weights(rng, N, K)
+    w = dev(Q.qpack_q4g32_mma(*W))
+    x = dev(synth.activations(rng, m, K))
+    y = torch.full((m, N), CANARY_BITS, dtype=torch.int32, device="cuda").view(torch.float32)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call = Q.bound_mma("q4g32", w, x, y, N, K, m=m)
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        call()
+    for r in range(3):
+        x.copy_(dev(synth.activations(synth.rng_for(121, 100 + r), m, K)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = host(y).copy()
+        ye = torch.full((m, N), CANARY_BITS, dtype=torch.int32, device="cuda").view(torch.float32)
+        Q.qgemv_q4g32_mma(w, x, ye, N, K, m=m)
+        assert np.array_equal(got, host(ye)), "replay %d" % r
