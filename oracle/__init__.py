@@ -10,10 +10,14 @@ splits output rows across threads when asked (each thread runs the same
 plain loop on its own rows, so the result does not depend on the split),
 loops over expert slots for the routed-expert case, and applies the SwiGLU
 activation (elementwise fp64 numpy, ``silu`` / ``swiglu`` below) to the
-GEMV results for the fused gate+up call.  The greedy argmax over logits is a
-plain left-to-right scan in ``oracle.c``.
+GEMV results for the fused gate+up call.  The routed-expert MLP rounds that
+activation to bf16 (``bf16_round``) before the down projection.  The greedy
+argmax over logits is a plain left-to-right scan in ``oracle.c``.
 
-Every function is pinned by ``tests/test_oracle_pins.py``.
+Every function is pinned by ``tests/test_oracle_pins.py``,
+``tests/test_oracle_swiglu.py``, ``tests/test_oracle_argmax.py`` and
+``tests/test_oracle_mlp.py``; ``tests/test_oracle_mutations.py`` plants
+mistakes in a copy of ``oracle.c`` and checks that the pins catch them.
 """
 from __future__ import annotations
 
