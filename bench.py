@@ -33,12 +33,15 @@ METRIC = "effective weight GB/s and % of HBM peak, m=1 quantized GEMV (µs/call)
 
 # HBM bytes per launch of the dominant kernel, from rocprofv3 --pmc FETCH_SIZE
 # and WRITE_SIZE runs scaled by the same counters on a plain copy kernel of
-# known size.  Valid only for the kernel sources they were taken on.
+# known size.  Valid only for the kernel sources they were taken on (and,
+# for an entry with "m", for that number of activation rows).
 TRAFFIC = {
-    "lm_head": {"source_digest": "66a30d19c66d2d70", "bytes_per_launch": 401967616},
-    "lm_head_q8g128": {"source_digest": "aeb2417dd63abf15", "bytes_per_launch": 395898368},
-    "moe_experts": {"source_digest": "b4af3740f63bac63", "bytes_per_launch": 31824896},
-    "moe_experts_swiglu": {"source_digest": "6211a8ee49214558", "bytes_per_launch": 47600384},
+    "lm_head": {"source_digest": "fb00ffa5aee1abdd", "bytes_per_launch": 401967616},
+    "lm_head_q8g128": {"source_digest": "38045f78095a8224", "bytes_per_launch": 395898368},
+    "moe_experts": {"source_digest": "dfe9b09b09e2b7b7", "bytes_per_launch": 31829685},
+    "moe_experts_swiglu": {"source_digest": "c36da2fe70881534", "bytes_per_launch": 47603792},
+    "lm_head_argmax_fused": {"source_digest": "11d94799103a6039", "bytes_per_launch": 401415904},
+    "lm_head_mma": {"source_digest": "508292aa3d6510c4", "bytes_per_launch": 406755328, "m": 8},
 }
 
 
@@ -597,7 +600,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
     }
     digest = kernel_source_digest(args.workload)
-    if not HOT and TRAFFIC.get(args.workload, {}).get("source_digest") == digest:
+    entry = TRAFFIC.get(args.workload, {})
+    if not HOT and entry.get("source_digest") == digest and entry.get("m", args.m) == args.m:
         out["roofline"]["traffic"] = TRAFFIC[args.workload]["bytes_per_launch"]
     out["config"]["kernel_source_digest"] = digest
     if not args.no_cpu and head["cpu"] is not None:
