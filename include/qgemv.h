@@ -160,10 +160,11 @@ qg_status qgemv_q8pc(const void *w_packed, const uint16_t *x_bf16, float *y,
  * plain GEMV:
  *   y[i*ldy + n] = sum_k W[n][k] * x[i*ldx + k],  0 <= i < m <= 16.
  * K must be a multiple of 64 (128 for Q8G128).  The m activation rows are
- * staged in LDS: m * K * 2 bytes must fit in 159 KiB (e.g. m = 16 with
- * K <= 5088, m = 15 with K = 5120), else QG_ERR_UNSUPPORTED.  Pointers,
- * strides, ownership and errors as qgemv_q8g64.  Each output row is
- * computed on its own (rows do not affect one another's bits). */
+ * staged in LDS when they fit (m * K * 2 bytes within 159 KiB, less the
+ * partial sums of a K split); longer rows are read from memory with each
+ * weight item instead, so any K is accepted.  Pointers, strides, ownership
+ * and errors as qgemv_q8g64, with m = 1..16.  Each output row is computed
+ * on its own (rows do not affect one another's bits). */
 size_t    qpack_q8g64_mma_size(int64_t N, int64_t K);
 size_t    qpack_q8g128_mma_size(int64_t N, int64_t K);
 size_t    qpack_q8pc_mma_size(int64_t N, int64_t K);

@@ -131,6 +131,7 @@ def test_ragged_shapes_and_strides(fmt, K, N, m):
     ("q8g64", 1000, 4864, 16, 0),      # x fills the LDS: x from memory
     ("q8pc", 700, 4864, 16, 2),        # the same with 4-byte x loads
     ("q8g128", 130, 4864, 16, 8),      # 38 groups, x from memory, 16-byte loads
+    ("q8g64", 40, 16384, 16, 0),       # 512 KiB of x: x from memory
 ])
 def test_k_split_choices(fmt, N, K, m, pad):
     gen = FMT[fmt][0]
@@ -140,6 +141,19 @@ def test_k_split_choices(fmt, N, K, m, pad):
     y = run(fmt, q, s, x, ldx=K + pad, ldy=N + 1)
     assert np.all(y[:, N:].view(np.uint32) == CANARY_BITS), "wrote past N"
     check(fmt, q, s, x, y[:, :N], "%s N=%d K=%d m=%d" % (fmt, N, K, m))
+
+
+def test_x_from_memory_without_a_split():
+    # Many tiles (no K split) and rows too long to stage: every wave reads
+    # x with its items.  Rows are checked against the oracle on slices (the
+    # oracle on the whole matrix would take minutes).
+    N, K, m = 65600, 5120, 16
+    rng = synth.rng_for(122, 0)
+    q, s = synth.q8g64_weights(rng, N, K)
+    x = synth.activations(rng, m, K)
+    y = run("q8g64", q, s, x)
+    for lo, hi in ((0, 1500), (31000, 32000), (N - 1500, N)):
+        check("q8g64", q[lo:hi], s[lo:hi], x, y[:, lo:hi], "rows %d..%d" % (lo, hi))
 
 
 def test_every_m_from_1_to_16():

@@ -90,12 +90,12 @@ qg_status check_gate_up(int64_t N, int64_t K, qg::Layout* L)
 }
 
 // Dense GEMV; with idx_out the argmax epilogue (y may then be null).
-// Matrix-core GEMV (MmaLayout), m = 1..16.
+// Matrix-core GEMV (MmaLayout), m = 1..16 (any K: rows of x too long to
+// stage in LDS are read from memory).
 qg_status check_mma(int fmt, int64_t m, int64_t N, int64_t K, qg::MmaLayout* L)
 {
     if (m < 1 || m > 16) return QG_ERR_UNSUPPORTED;
     if (!qg::make_mma_layout(fmt, N, K, L)) return QG_ERR_INVALID_ARG;
-    if (size_t(m) * size_t(K) * 2 > qg::kMaxDynLdsBytes) return QG_ERR_UNSUPPORTED;
     return QG_OK;
 }
 

@@ -89,7 +89,8 @@ struct MmaItem {
     u32x4 c;        // 16 biased 8-bit codes, or 32 Q4 codes (one dword per 32-group)
     uint32_t s;     // fp16 scale (low half) or fp32 row scale bits (8-bit formats)
     u32x4 m4;       // Q4G32: scale | min << 16 of the row's four groups
-    u32x4 a0, a1;   // the step's A fragment, when x is read from memory (XG)
+    u32x4 a0, a1;   // the step's A fragments, when x is read from memory (XG)
+    u32x4 a2, a3;   // (Q4G32: one per 32-group)
 };
 
 // Threads per work-group: four waves, or sixteen for the 16-way K split.
@@ -101,9 +102,9 @@ constexpr int mma_threads()
 
 // XG: the A fragments come from memory with each item (x is read through
 // the L2, once per tile) instead of from a copy of x staged in LDS; for
-// m * K too large to stage next to a K split's partial sums (built for the
-// four-wave split: with sixteen waves the longer ring does not fit in
-// registers).
+// m * K too large to stage (next to a K split's partial sums).  Built for
+// whole tiles per wave and for the four-wave split: with sixteen waves the
+// longer ring does not fit in registers.
 template <int FMT, int DEPTH, int KSPLIT, bool XG>
 __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaParams p)
 {
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
     // so K splits fall between steps there too.
     constexpr int SPG = FMT == FMT_Q8G128 ? 2 : 1;
     constexpr bool Q4 = FMT == FMT_Q4G32;
-    static_assert(!(Q4 && XG), "Q4G32 stages x in LDS");
+    static_assert(!(XG && KSPLIT == 16), "x from memory is built for whole tiles or four waves");
 
     // Tile mapping.  KSPLIT = 1: wave gw streams tiles gw, gw + W, ...  and
     // all their steps.  KSPLIT > 1: work-group b takes tiles b, b + B, ...
@@ -169,7 +170,19 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
         if constexpr (Q4) it.m4 = *reinterpret_cast<const u32x4*>(mt + (j * 16 + rho) * 16);
         else if (FMT == FMT_Q8PC) it.s = *reinterpret_cast<const uint32_t*>(mt + rho * 4);
         else it.s = *reinterpret_cast<const uint16_t*>(mt + ((j / SPG) * 16 + rho) * 2);
-        if constexpr (XG) {
+        if constexpr (XG && Q4) {
+            // Row rho of x, k = 128 j + 32 g + 8 qs .. + 7 for the four
+            // groups g (lanes past m read nothing).
+            if (row_live) {
+                const uint16_t* src = p.x + int64_t(rho) * p.ldx + j * 128 + qs * 8;
+                it.a0 = load_x16(src);
+                it.a1 = load_x16(src + 32);
+                it.a2 = load_x16(src + 64);
+                it.a3 = load_x16(src + 96);
+            } else {
+                it.a0 = it.a1 = it.a2 = it.a3 = zero4;
+            }
+        } else if constexpr (XG) {
             // Row rho of x, k = 64 j + 16 qs .. + 15 (lanes past m read nothing).
             if (row_live) {
                 const uint16_t* src = p.x + int64_t(rho) * p.ldx + j * 64 + qs * 16;
@@ -253,7 +266,9 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int c = int(j) * 16 + 4 * g + qs;
-                const u32x4 au = row_live ? xs[xs_chunk(rho, c, cpr)] : zero4;
+                u32x4 au;
+                if constexpr (XG) au = g == 0 ? it.a0 : g == 1 ? it.a1 : g == 2 ? it.a2 : it.a3;
+                else au = row_live ? xs[xs_chunk(rho, c, cpr)] : zero4;
                 const bf16x8 a = __builtin_bit_cast(bf16x8, au);
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
                 const f32x4 Dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, widen_q4(it.c[g]), z, 0, 0, 0);
@@ -352,8 +367,9 @@ hipError_t launch_fmt(const MmaParams& kp, int64_t waves, size_t lds, hipStream_
 {
     // Ring depth 8, or 6 with sixteen waves (a CU then has 96 KiB in
     // flight), or 4 when the ring also carries the A fragments.  Q4G32
-    // items carry 16 bytes of meta per lane: 6, or 4 with sixteen waves.
-    constexpr int depth = XG ? 4
+    // items carry 16 bytes of meta per lane: 6, or 4 with sixteen waves,
+    // or 3 with their four A fragments.
+    constexpr int depth = XG ? (FMT == FMT_Q4G32 ? 3 : 4)
                         : FMT == FMT_Q4G32 ? (KSPLIT == 16 ? 4 : 6)
                                            : (KSPLIT == 16 ? 6 : 8);
     auto kern = qgemv_mma<FMT, depth, KSPLIT, XG>;
@@ -379,10 +395,9 @@ hipError_t launch_split(int ksplit, bool xg, const MmaParams& kp, int64_t waves,
 {
     switch (ksplit * 2 + (xg ? 1 : 0)) {
     case 2: return launch_fmt<FMT, 1, false>(kp, waves, lds, s);
+    case 3: return launch_fmt<FMT, 1, true>(kp, waves, lds, s);
     case 8: return launch_fmt<FMT, 4, false>(kp, waves, lds, s);
-    case 9:
-        if constexpr (FMT != FMT_Q4G32) return launch_fmt<FMT, 4, true>(kp, waves, lds, s);
-        return hipErrorInvalidValue;
+    case 9: return launch_fmt<FMT, 4, true>(kp, waves, lds, s);
     case 32: return launch_fmt<FMT, 16, false>(kp, waves, lds, s);
     default: return hipErrorInvalidValue;
     }

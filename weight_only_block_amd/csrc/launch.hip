@@ -153,21 +153,21 @@ hipError_t launch_mma_sized(int fmt, const MmaParams& kp, size_t lds, hipStream_
     // staged x, four waves share the tile; where the staged x would leave
     // room for only one such group per CU, they read x from memory with
     // each item instead (two groups per CU; Q8PC at m = 15 measured 15.0 ->
-    // 11.1 us on 1792 x 5120 and 17.2 -> 13.6 us on 5120 x 4352).
-    // QG_MMA_XG = 0/1 forces staging on / x from memory (tuning sweeps).
+    // 11.1 us on 1792 x 5120 and 17.2 -> 13.6 us on 5120 x 4352).  Q4G32
+    // keeps staging as long as x fits.  Without a split, x is read from
+    // memory only when it does not fit in LDS at all.
+    // QG_MMA_XG = 0/1 forces staging on (where x fits) / x from memory.
     bool xg = false;
     if (split == 16 && lds + mma_split_lds_bytes(16) > kMaxDynLdsBytes) split = 4;
-    if (split == 4 && lds + mma_split_lds_bytes(4) > kMaxLdsBytes / 2) xg = true;
-    if (split == 4 && env_xg == 0 && lds + mma_split_lds_bytes(4) <= kMaxDynLdsBytes) xg = false;
+    if (split == 4) {
+        const size_t staged = lds + mma_split_lds_bytes(4);
+        xg = staged > kMaxDynLdsBytes || (fmt != FMT_Q4G32 && staged > kMaxLdsBytes / 2);
+        if (env_xg == 0 && staged <= kMaxDynLdsBytes) xg = false;
+    }
+    if (split == 1) xg = lds > kMaxDynLdsBytes;
     if (split > 1 && env_xg == 1) {
         split = 4;
         xg = true;
-    }
-    // Q4G32 always stages x (a step's A fragments are four 16-byte chunks):
-    // without room for the four-wave split's sums it streams whole tiles.
-    if (fmt == FMT_Q4G32 && xg) {
-        xg = false;
-        if (lds + mma_split_lds_bytes(4) > kMaxDynLdsBytes) split = 1;
     }
     if (split > 1) {
         // As many work-groups as can be resident at once (staged x bounds
@@ -184,7 +184,7 @@ hipError_t launch_mma_sized(int fmt, const MmaParams& kp, size_t lds, hipStream_
     }
     const int64_t k = (kp.tiles + cap - 1) / cap;
     const int64_t waves = (kp.tiles + k - 1) / k;
-    return launch_mma(fmt, 1, false, kp, waves, lds, s);
+    return launch_mma(fmt, 1, xg, kp, waves, xg ? 0 : lds, s);
 }
 
 }  // namespace qg
