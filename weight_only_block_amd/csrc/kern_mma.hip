@@ -169,7 +169,10 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
         const uint8_t* mt = meta + tile * p.meta_tile_bytes;
         if constexpr (Q4) it.m4 = *reinterpret_cast<const u32x4*>(mt + (j * 16 + rho) * 16);
         else if (FMT == FMT_Q8PC) it.s = *reinterpret_cast<const uint32_t*>(mt + rho * 4);
-        else it.s = *reinterpret_cast<const uint16_t*>(mt + ((j / SPG) * 16 + rho) * 2);
+        // Group scales are read once per call: non-temporal, like the codes
+        // (1% on the LM head at m = 8).  A Q8PC row scale is re-read at every
+        // step of its tile and stays a plain load (3% slower otherwise).
+        else it.s = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(mt + ((j / SPG) * 16 + rho) * 2));
         if constexpr (XG && Q4) {
             // Row rho of x, k = 128 j + 32 g + 8 qs .. + 7 for the four
             // groups g (lanes past m read nothing).

@@ -66,28 +66,30 @@ __device__ __forceinline__ u32x4 load_stream16(const uint8_t* p)
 }
 
 // Meta words a lane reads per step: Q8 R fp16 scales, Q4 R (scale|min<<16).
+// Non-temporal like the codes: each meta word is read once per call (about
+// 1% faster than plain loads on the LM head and the routed experts).
 template <int BYTES> struct Meta;
 template <> struct Meta<2> {
     uint32_t w[1];
-    __device__ __forceinline__ void load(const uint8_t* p) { w[0] = *reinterpret_cast<const uint16_t*>(p); }
+    __device__ __forceinline__ void load(const uint8_t* p) { w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p)); }
 };
 template <> struct Meta<4> {
     uint32_t w[1];
-    __device__ __forceinline__ void load(const uint8_t* p) { w[0] = *reinterpret_cast<const uint32_t*>(p); }
+    __device__ __forceinline__ void load(const uint8_t* p) { w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)); }
 };
 template <> struct Meta<8> {
     uint32_t w[2];
     __device__ __forceinline__ void load(const uint8_t* p)
     {
-        const uint2 v = *reinterpret_cast<const uint2*>(p);
-        w[0] = v.x; w[1] = v.y;
+        const uint64_t v = __builtin_nontemporal_load(reinterpret_cast<const uint64_t*>(p));
+        w[0] = uint32_t(v); w[1] = uint32_t(v >> 32);
     }
 };
 template <> struct Meta<16> {
     uint32_t w[4];
     __device__ __forceinline__ void load(const uint8_t* p)
     {
-        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
         w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
     }
 };
