@@ -111,14 +111,43 @@ __device__ __forceinline__ void q8_pairs(const u32x4& c, uint32_t (&pr)[8])
     }
 }
 
-// 32 reordered 4-bit codes -> 16 bf16 pairs (128 + c), in x order.
-__device__ __forceinline__ void q4_pairs(const u32x4& c, uint32_t (&pr)[16])
+// The two constants of the 4-bit decode, held in registers for the whole
+// kernel: the nibble-pair mask in a scalar register and the bf16 magic in a
+// vector register.  gfx9 VOP3 encodings take no literal constants, so with
+// both written as literals the compiler splits every (v & mask) | magic into
+// a v_and_b32 and a v_or_b32 (two VOP2 ops with literals); with the mask in
+// an SGPR and the magic in a VGPR it is one v_and_or_b32 (one SGPR operand
+// stays within the single constant-bus read).  Both values come out of asm so
+// the compiler can neither fold them back into literals nor rematerialise
+// them before each use.
+struct Q4Consts {
+    uint32_t mask;    // 0x000F000F, SGPR
+    uint32_t magic;   // kMagicBf16x2, VGPR
+    __device__ __forceinline__ static Q4Consts make()
+    {
+        Q4Consts k;
+        asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(k.mask));
+        asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(k.magic));
+        return k;
+    }
+};
+
+__device__ __forceinline__ uint32_t and_or(uint32_t v, const Q4Consts& k)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(k.mask), "v"(k.magic));
+    return r;
+}
+
+// 32 reordered 4-bit codes -> 16 bf16 pairs (128 + c), in x order: pair p of
+// a dword is ((v >> 4p) & 0x000F000F) | 0x43004300, seven VALU ops per dword.
+__device__ __forceinline__ void q4_pairs(const u32x4& c, const Q4Consts& k, uint32_t (&pr)[16])
 {
     const uint32_t v[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) pr[4 * d + p] = ((v[d] >> (4 * p)) & 0x000F000Fu) | kMagicBf16x2;
+        for (int p = 0; p < 4; ++p) pr[4 * d + p] = and_or(v[d] >> (4 * p), k);
     }
 }
 
@@ -206,7 +235,7 @@ struct Item {
 
 template <int FMT, int M, int R, int META_BYTES>
 __device__ __forceinline__ void consume(const Item<R, META_BYTES>& it, const uint32_t* xs,
-                                        const float* xsum, int KD, int U, int u,
+                                        const float* xsum, int KD, int U, int u, const Q4Consts& k4,
                                         float (&acc)[R][M])
 {
     constexpr int UD = FMT == FMT_Q4G32 ? 16 : 8;
@@ -244,7 +273,7 @@ __device__ __forceinline__ void consume(const Item<R, META_BYTES>& it, const uin
             const float s = half_lo(it.m.w[r]);
             const float mn = half_hi(it.m.w[r]);
             uint32_t pr[16];
-            q4_pairs(it.c[r], pr);
+            q4_pairs(it.c[r], k4, pr);
 #pragma unroll
             for (int i = 0; i < M; ++i) {
                 float D = 0.0f;
@@ -402,43 +431,69 @@ __device__ __forceinline__ uint16_t to_bf16(float v)
 }
 
 // Gate/up pair layout (layout.h): row slot 0 of a tile holds gate rows and
-// slot 1 the up rows with the same output indices.  After the reduction the
-// lane holding a gate sum fetches the matching up sum (from the lane that
-// differs in the transposed bit, or from its own second register when
-// nothing was transposed) and writes bf16(silu(g) * u).
+// slot 1 the up rows with the same output indices.  A tile yields only 64/G
+// outputs, so running silu, the bf16 rounding and the store once per tile
+// would cost a whole wave's issue slots for one or two values.  Instead the
+// reduced sums of up to B consecutive tiles wait in registers, tile b of the
+// batch in the lanes whose low bits equal b (after reduce_tile every lane of
+// a row group holds the full sum, so B is the number of lanes sharing a
+// value: G, or G/2 when the gate and up sums were transposed onto lane bit 5
+// or 4), and one pass over the batch writes bf16(silu(g) * u) for all of them.
 template <int G, int R>
-__device__ __forceinline__ void finish_tile_swiglu(float (&acc)[R][1], const KernelParams& p,
-                                                   uint16_t* act, int64_t tile, int g, int rho, int lane)
-{
+struct SwigluBatch {
     static_assert(R == 2, "gate and up occupy the two row slots");
     using TS = TileSums<1, G, R>;
-    constexpr int RPS = 64 / G;
-    TS ts;
-    reduce_tile<1, G, R>(acc, ts);
-    float gate, up;
-    bool writer = TS::holder(g);
-    if constexpr (TS::V2 == 1) {
-        // One transposed bit separates the gate lane (bit clear) from the up lane.
-        constexpr int BIT = TS::T5 ? 32 : 16;
-        const float other = __shfl_xor(ts.v[0], BIT, 64);
-        const bool is_up = (lane & BIT) != 0;
-        gate = is_up ? other : ts.v[0];
-        up = is_up ? ts.v[0] : other;
-        writer = writer && !is_up;
-    } else {
-        gate = ts.v[0];
-        up = ts.v[1];
+    static constexpr int RPS = 64 / G;
+    static constexpr int B = (TS::T5 || TS::T4) ? G / 2 : G;
+    float v0 = 0.0f, v1 = 0.0f;   // this lane's batch entry (gate|up, or gate and up)
+    int n = 0;                    // tiles in the batch (the same in every lane)
+    int64_t first = 0;            // tile index of batch entry 0
+
+    __device__ __forceinline__ bool full() const { return n == B; }
+
+    __device__ __forceinline__ void add(float (&acc)[R][1], int64_t tile, int lane)
+    {
+        TS ts;
+        reduce_tile<1, G, R>(acc, ts);
+        if (n == 0) first = tile;
+        if ((lane & (B - 1)) == n) {
+            v0 = ts.v[0];
+            if constexpr (TS::V2 == 2) v1 = ts.v[1];
+        }
+        ++n;
     }
-    const int64_t n = tile * RPS + rho;
-    if (writer && n < p.n_out) {
-        // sigmoid(g) from e = exp(-|g|) <= 1, so exp never overflows: for a
-        // very negative gate silu(g) = g e^g / (1 + e^g) stays a tiny
-        // nonzero number instead of g / inf.
-        const float e = expf(-fabsf(gate));
-        const float sig = (gate >= 0.0f ? 1.0f : e) / (1.0f + e);
-        act[n] = to_bf16(gate * sig * up);
+
+    // Writes the batch (tiles first, first + tstep, ...) and empties it.
+    __device__ __forceinline__ void flush(const KernelParams& p, uint16_t* act, int64_t tstep, int lane,
+                                          int rho)
+    {
+        float gate, up;
+        bool writer = true;
+        if constexpr (TS::V2 == 1) {
+            // One transposed bit separates the gate lanes (bit clear) from the up lanes.
+            constexpr int BIT = TS::T5 ? 32 : 16;
+            const float other = __shfl_xor(v0, BIT, 64);
+            const bool is_up = (lane & BIT) != 0;
+            gate = is_up ? other : v0;
+            up = is_up ? v0 : other;
+            writer = !is_up;
+        } else {
+            gate = v0;
+            up = v1;
+        }
+        const int b = lane & (B - 1);
+        const int64_t row = (first + int64_t(b) * tstep) * RPS + rho;
+        if (writer && b < n && row < p.n_out) {
+            // sigmoid(g) from e = exp(-|g|) <= 1, so exp never overflows: for a
+            // very negative gate silu(g) = g e^g / (1 + e^g) stays a tiny
+            // nonzero number instead of g / inf.
+            const float e = expf(-fabsf(gate));
+            const float sig = (gate >= 0.0f ? 1.0f : e) / (1.0f + e);
+            act[row] = to_bf16(gate * sig * up);
+        }
+        n = 0;
     }
-}
+};
 
 // Argmax epilogue: reduces the tile like finish_tile, stores the logits if
 // the caller wants them, and folds each finished logit into the lane's
@@ -658,17 +713,23 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int i = 0; i < M; ++i) acc[r][i] = 0.0f;
+    Q4Consts k4 = {0u, 0u};
+    if constexpr (FMT == FMT_Q4G32) k4 = Q4Consts::make();
+    SwigluBatch<G, R> swb;   // EPI 1 only
 
     // Consume cursor.
     int64_t tile = t0, j = 0;
 #define QG_CONSUME(slot_)                                                                     \
     do {                                                                                      \
-        consume<FMT, M, R, META_BYTES>(ring[slot_], xs, xsum, KD, U, int(j) * G + g, acc);  \
+        consume<FMT, M, R, META_BYTES>(ring[slot_], xs, xsum, KD, U, int(j) * G + g, k4, acc); \
     } while (0)
 #define QG_ADVANCE()                                                                          \
     do {                                                                                      \
         if (++j == p.J) {                                                                     \
-            if constexpr (EPI == 1) finish_tile_swiglu<G, R>(acc, p, act, tile, g, rho, lane);      \
+            if constexpr (EPI == 1) {                                                         \
+                swb.add(acc, tile, lane);                                                     \
+                if (swb.full()) swb.flush(p, act, tstep, lane, rho);                          \
+            }                                                                                 \
             else if constexpr (EPI == 2) finish_tile_argmax<M, G, R>(acc, p, p.y, tile, g, rho, lane, best); \
             else finish_tile<M, G, R>(acc, p, y, tile, g, rho, lane);                               \
             tile += tstep;                                                                    \
@@ -706,6 +767,9 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
 #undef QG_LOAD_NEXT
 #undef QG_CONSUME
 #undef QG_ADVANCE
+    if constexpr (EPI == 1) {
+        if (swb.n > 0) swb.flush(p, act, tstep, lane, rho);
+    }
     if constexpr (EPI == 2) finish_argmax<M>(best, p, lane, wave);
 }
 
