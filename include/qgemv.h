@@ -316,6 +316,21 @@ uint64_t qg_route_count(const char *variant);
  * the matrix-core kernel for Q4G32, "q4g32_mma_m<m>").
  * Returns QG_OK or the status the call itself would return for that shape. */
 qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char *buf, size_t buf_len);
+/* Overrides how the non-matrix-core kernels (qgemv_q8g64, qgemv_q4g32,
+ * qgemv_q8g128, qgemv_q8pc, the grouped calls and the *_argmax calls) map
+ * tiles to waves, for tests and tuning sweeps.  Every tile is computed the
+ * same way under any mapping, so results are the same bits.
+ *   target_waves  > 0: about this many waves per launch in total (capped at
+ *                 one wave per tile); 0: the per-compute-unit default.
+ *   contig        1: each wave streams a contiguous run of tiles; 0: waves
+ *                 sweep the matrix grid-stride; -1: the default (contiguous
+ *                 for grouped calls, grid-stride otherwise).
+ *   ring_depth    2 or 4: work items kept in flight per wave; 0: default.
+ * Process-wide and sticky until called again with (0, -1, 0); not
+ * synchronized with qgemv_* calls made meanwhile on other host threads.
+ * Returns QG_ERR_INVALID_ARG (and changes nothing) for values outside these
+ * ranges or target_waves above 2^24. */
+qg_status qg_set_launch_override(int64_t target_waves, int32_t contig, int32_t ring_depth);
 
 #ifdef __cplusplus
 }

@@ -387,3 +387,16 @@ def test_q4g32_mma_pack_layout_and_roundtrip():
     assert f(W + 16, X, Y, 1, 16, 256, 256, 16, None) == Q.QG_ERR_ALIGNMENT
     assert f(W, X, Y, 0, 16, 256, 256, 16, None) == Q.QG_OK
     assert Q.variant_name(Q.FMT_Q4G32_MMA, 4, 9216, 2560) == "q4g32_mma_m4"
+
+
+def test_launch_override_validation():
+    # Values outside the documented ranges are rejected; valid ones and the
+    # reset to defaults are accepted (no kernel is launched here).
+    for args in [(-1, -1, 0), (0, 2, 0), (0, -2, 0), (0, -1, 3), (1 << 25, -1, 0)]:
+        with pytest.raises(Q.QGError):
+            Q.set_launch_override(*args)
+    try:
+        Q.set_launch_override(7, 1, 4)
+        Q.set_launch_override(1 << 24, 0, 2)
+    finally:
+        Q.set_launch_override()

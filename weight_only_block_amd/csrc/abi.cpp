@@ -399,6 +399,19 @@ uint64_t qg_route_count(const char* variant)
     return 0;
 }
 
+qg_status qg_set_launch_override(int64_t target_waves, int32_t contig, int32_t ring_depth)
+{
+    if (target_waves < 0 || target_waves > (int64_t(1) << 24) || contig < -1 || contig > 1 ||
+        (ring_depth != 0 && ring_depth != 2 && ring_depth != 4))
+        return QG_ERR_INVALID_ARG;
+    qg::LaunchOverride o;
+    o.target_waves = target_waves;
+    o.contig = contig;
+    o.shape = ring_depth == 2 ? qg::SHAPE_D2_W4 : ring_depth == 4 ? qg::SHAPE_D4_W4 : -1;
+    qg::set_launch_override(o);
+    return QG_OK;
+}
+
 qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char* buf, size_t buf_len)
 {
     if (!buf || buf_len == 0) return QG_ERR_INVALID_ARG;

@@ -71,6 +71,15 @@ struct LaunchArgs {
     hipStream_t stream;
 };
 
+// Process-wide launch-geometry override of the VALU kernels (tests and
+// tuning sweeps; the results are the same bits for every geometry).
+struct LaunchOverride {
+    int64_t target_waves;  // > 0: about this many waves in total
+    int contig;            // 1: contiguous tile runs per wave, 0: grid-stride, -1: default
+    int shape;             // SHAPE_D2_W4 / SHAPE_D4_W4, -1: default
+};
+void set_launch_override(const LaunchOverride& o);
+
 // Bytes of dynamic LDS a launch of this layout needs for m activation rows.
 size_t lds_bytes_for(const Layout& L, int m);
 

@@ -20,6 +20,16 @@ constexpr int64_t kWavesPerCuDenseMulti = 8;
 constexpr int64_t kWavesPerCuGrouped = 8;
 }  // namespace
 
+// Launch-geometry override (qg_set_launch_override): 0 / -1 leave the
+// choice to the environment (QG_TARGET_WAVES, QG_CONTIG, QG_SHAPE, read once,
+// for tuning sweeps) and then to the defaults below.
+static LaunchOverride g_override = {0, -1, -1};
+
+void set_launch_override(const LaunchOverride& o)
+{
+    g_override = o;
+}
+
 // Compute units of the current device, looked up once per device.
 static int64_t compute_units()
 {
@@ -79,9 +89,10 @@ hipError_t launch(const LaunchArgs& a)
     }();
     const int64_t cus = compute_units();
     const int64_t target_waves =
-        env_waves ? env_waves
-                  : cus * (a.grouped ? kWavesPerCuGrouped
-                                     : (a.m > 1 ? kWavesPerCuDenseMulti : kWavesPerCuDense));
+        g_override.target_waves > 0 ? g_override.target_waves
+        : env_waves                 ? env_waves
+                                    : cus * (a.grouped ? kWavesPerCuGrouped
+                                                       : (a.m > 1 ? kWavesPerCuDenseMulti : kWavesPerCuDense));
     int64_t cap = target_waves / slots;
     if (cap < 1) cap = 1;
     // Up to twice the cap, a dense launch is latency-bound rather than
@@ -99,13 +110,16 @@ hipError_t launch(const LaunchArgs& a)
         const char* e = getenv("QG_CONTIG");
         return e ? int(strtol(e, nullptr, 10)) : -1;
     }();
-    const bool contig = env_contig >= 0 ? env_contig != 0 : a.grouped;
+    const bool contig = g_override.contig >= 0 ? g_override.contig != 0
+                      : env_contig >= 0         ? env_contig != 0
+                                                : a.grouped;
     kp.contig_k = contig ? k : 0;
     static const int env_shape = [] {
         const char* e = getenv("QG_SHAPE");   // tuning sweeps only
         return e ? int(strtol(e, nullptr, 10)) : -1;
     }();
     if (env_shape == SHAPE_D2_W4 || env_shape == SHAPE_D4_W4) shape = env_shape;
+    if (g_override.shape == SHAPE_D2_W4 || g_override.shape == SHAPE_D4_W4) shape = g_override.shape;
     const size_t lds = lds_bytes_for(L, a.m);
     const hipStream_t s = a.stream;
     const int64_t w = waves_per_slot;

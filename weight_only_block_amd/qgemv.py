@@ -100,6 +100,7 @@ def lib() -> ctypes.CDLL:
             "qg_route_counts_reset": ([], None),
             "qg_route_count": ([ctypes.c_char_p], ctypes.c_uint64),
             "qg_variant_name": ([ctypes.c_int, i64, i64, i64, ctypes.c_char_p, sz], st),
+            "qg_set_launch_override": ([i64, ctypes.c_int32, ctypes.c_int32], st),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -635,6 +636,11 @@ def variant_name(fmt: int, m: int, N: int, K: int) -> str:
     buf = ctypes.create_string_buffer(64)
     _check(lib().qg_variant_name(fmt, m, N, K, buf, 64), "qg_variant_name")
     return buf.value.decode()
+
+
+def set_launch_override(target_waves: int = 0, contig: int = -1, ring_depth: int = 0) -> None:
+    """qg_set_launch_override; call with no arguments to restore the defaults."""
+    _check(lib().qg_set_launch_override(target_waves, contig, ring_depth), "qg_set_launch_override")
 
 
 def expert_stride(N: int, K: int) -> int:
