@@ -36,12 +36,12 @@ METRIC = "effective weight GB/s and % of HBM peak, m=1 quantized GEMV (µs/call)
 # known size.  Valid only for the kernel sources they were taken on (and,
 # for an entry with "m", for that number of activation rows).
 TRAFFIC = {
-    "lm_head": {"source_digest": "fb00ffa5aee1abdd", "bytes_per_launch": 401967616},
-    "lm_head_q8g128": {"source_digest": "38045f78095a8224", "bytes_per_launch": 395898368},
-    "moe_experts": {"source_digest": "dfe9b09b09e2b7b7", "bytes_per_launch": 31829685},
-    "moe_experts_swiglu": {"source_digest": "c36da2fe70881534", "bytes_per_launch": 47603792},
-    "lm_head_argmax_fused": {"source_digest": "11d94799103a6039", "bytes_per_launch": 401415904},
-    "lm_head_mma": {"source_digest": "508292aa3d6510c4", "bytes_per_launch": 406755328, "m": 8},
+    "lm_head": {"source_digest": "1a235fc2096c95bf", "bytes_per_launch": 403393981},
+    "lm_head_q8g128": {"source_digest": "b9c986b71a66e6b8", "bytes_per_launch": 396782862},
+    "moe_experts": {"source_digest": "c2fe60c4694a9a1b", "bytes_per_launch": 31808840},
+    "moe_experts_swiglu": {"source_digest": "960ffac13ad09421", "bytes_per_launch": 47587822},
+    "lm_head_argmax_fused": {"source_digest": "b9150bc715f14e21", "bytes_per_launch": 402908059},
+    "lm_head_mma": {"source_digest": "1dc13ff2629dc95b", "bytes_per_launch": 409369367, "m": 8},
 }
 
 
@@ -327,6 +327,7 @@ def setup_dense(torch, Q, synth, name, m=1):
 # ----------------------------------------------------------- routed experts
 
 def setup_moe(torch, Q, synth, id_sets=256):
+    id_sets = 1 if HOT else id_sets
     n_exp, n_slots = synth.MOE["n_experts"], synth.MOE["n_slots"]
     wid = synth.WORKLOAD_IDS["moe_experts"]
     bufs, shapes = {}, {}
@@ -381,7 +382,6 @@ def setup_moe_merged(torch, Q, synth, id_sets=256):
     """Routed experts with each expert's gate and up rows stacked into one
     [2*1536][4096] matrix (rows are independent, so the result is the same
     bits as two calls): one grouped launch for gate+up, one for down."""
-    id_sets = 1 if HOT else id_sets
     id_sets = 1 if HOT else id_sets
     n_exp, n_slots = synth.MOE["n_experts"], synth.MOE["n_slots"]
     wid = synth.WORKLOAD_IDS["moe_experts"]
