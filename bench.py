@@ -126,6 +126,40 @@ def time_steps_graph(torch, step, warmup, steps, period):
     return start.elapsed_time(end) * 1e-3
 
 
+def read_stream_reference(torch, Q, bytes_per_launch, launches=300, warmup=50):
+    """The bandwidth of a plain read (qg_read_stream: 16-byte non-temporal
+    loads, as the GEMV kernels use) of the same bytes per launch, rotating
+    over enough buffers that no launch finds its bytes in the last-level
+    cache.  Best of a few wave counts; returns (seconds per launch, waves
+    per CU)."""
+    nb = (int(bytes_per_launch) + 15) // 16 * 16
+    copies = 1 if HOT else max(2, -(-2 * LLC_BYTES // nb))
+    bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fn = Q.lib().qg_read_stream
+    stream = torch.cuda.current_stream().cuda_stream
+    best = None
+    for wpc in (2, 4, 8, 16):
+        args = [(b.data_ptr(), nb, sink.data_ptr(), wpc, stream) for b in bufs]
+        for i in range(warmup):
+            fn(*args[i % copies])
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(launches):
+            if fn(*args[i % copies]) != Q.QG_OK:
+                raise RuntimeError("qg_read_stream failed")
+        end.record()
+        torch.cuda.synchronize()
+        t = start.elapsed_time(end) * 1e-3 / launches
+        if best is None or t < best[0]:
+            best = (t, wpc)
+    del bufs
+    torch.cuda.empty_cache()
+    return best
+
+
 # ------------------------------------------------------------------ lm_head
 
 def setup_lm_head(torch, Q, synth, fmt="q8g64"):
@@ -513,6 +547,8 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-secondary", dest="secondary", action="store_false",
                     help="skip timing the other workload beside the headline")
+    ap.add_argument("--no-read-stream", dest="read_stream", action="store_false",
+                    help="skip timing a plain read of the same bytes per launch")
     args = ap.parse_args()
     global HOT
     HOT = args.hot
@@ -601,6 +637,12 @@ def main():
     if not HOT and entry.get("source_digest") == digest and entry.get("m", args.m) == args.m:
         out["roofline"]["traffic"] = TRAFFIC[args.workload]["bytes_per_launch"]
     out["config"]["kernel_source_digest"] = digest
+    if args.read_stream:
+        bpl = head["alg"] / head["launches"]
+        t, wpc = read_stream_reference(torch, Q, bpl)
+        out["read_stream"] = {"bytes_per_launch": int(bpl), "us_per_launch": round(t * 1e6, 3),
+                              "GBs": round(bpl / t / 1e9, 2), "waves_per_cu": wpc,
+                              "frac": round(achieved / (bpl / t / 1e9), 4)}
     if not args.no_cpu and head["cpu"] is not None:
         import oracle
         threads = max(1, min(16, len(os.sched_getaffinity(0))))
@@ -630,6 +672,11 @@ def main():
                             "us_per_call": round(ps / sec["launches"] * 1e6, 3),
                             "effective_GBs": round(sec["alg"] / ps / 1e9, 2),
                             "pct_hbm_peak": round(100 * sec["alg"] / ps / 1e9 / HBM_PEAK_GBS, 2)}
+        if args.read_stream:
+            bpl = sec["alg"] / sec["launches"]
+            t, wpc = read_stream_reference(torch, Q, bpl)
+            out["secondary"]["read_stream_GBs"] = round(bpl / t / 1e9, 2)
+            out["secondary"]["frac_of_read_stream"] = round(sec["alg"] / ps / 1e9 / (bpl / t / 1e9), 4)
     print(json.dumps(out), flush=True)
 
 

@@ -332,6 +332,26 @@ qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char *buf, s
  * ranges or target_waves above 2^24. */
 qg_status qg_set_launch_override(int64_t target_waves, int32_t contig, int32_t ring_depth);
 
+/* ------------------------------------------------------ measurement hook
+ * A plain read of `bytes` bytes at buf (device, 16-byte aligned, bytes a
+ * nonzero multiple of 16) with the GEMV kernels' access width: 16-byte
+ * non-temporal loads, a wave-wide load one contiguous KiB, each wave
+ * reading 8 KiB chunks (eight loads in flight, lane l taking units l,
+ * l + 64, ... of the chunk) and the waves taking chunks grid-stride.  It is the bandwidth reference that a
+ * weight-streaming call is compared with on the same part (effective weight
+ * bandwidth over the bandwidth of a read of the same bytes; the zLLM post
+ * defines effective bandwidth as bytes over kernel time).
+ * Each lane XOR-folds the 32-bit words of the units it reads (word by word,
+ * then the four words together); a lane whose fold is 0x9E3779B9 writes that
+ * value to *sink (device, 4-byte aligned), so the loads cannot be dropped.
+ * waves_per_cu: waves per compute unit, 1..32, or 0 for 8.  Asynchronous
+ * on hip_stream (NULL = default stream).  QG_ERR_INVALID_ARG for a null
+ * pointer, bytes 0 or not a multiple of 16, or waves_per_cu out of range;
+ * QG_ERR_ALIGNMENT for a misaligned buf or sink; QG_ERR_HIP if the launch
+ * fails.  Nothing is enqueued on error. */
+qg_status qg_read_stream(const void *buf, size_t bytes, uint32_t *sink, int32_t waves_per_cu,
+                         void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

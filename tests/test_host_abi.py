@@ -400,3 +400,16 @@ def test_launch_override_validation():
         Q.set_launch_override(1 << 24, 0, 2)
     finally:
         Q.set_launch_override()
+
+
+def test_read_stream_validation():
+    # Argument checks run before anything touches a device.
+    f = Q.lib().qg_read_stream
+    assert f(None, 16, 64, 0, None) == Q.QG_ERR_INVALID_ARG
+    assert f(256, 16, None, 0, None) == Q.QG_ERR_INVALID_ARG
+    assert f(256, 0, 64, 0, None) == Q.QG_ERR_INVALID_ARG
+    assert f(256, 24, 64, 0, None) == Q.QG_ERR_INVALID_ARG
+    assert f(256, 16, 64, 33, None) == Q.QG_ERR_INVALID_ARG
+    assert f(256, 16, 64, -1, None) == Q.QG_ERR_INVALID_ARG
+    assert f(264, 16, 64, 0, None) == Q.QG_ERR_ALIGNMENT
+    assert f(256, 16, 66, 0, None) == Q.QG_ERR_ALIGNMENT

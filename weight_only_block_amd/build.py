@@ -31,7 +31,8 @@ def _run(cmd):
 
 
 HIP_SOURCES = ["kern_q8g64.hip", "kern_q4g32.hip", "kern_q8g128.hip", "kern_q8pc.hip",
-               "kern_q4g32_swiglu.hip", "kern_argmax_epi.hip", "kern_mma.hip", "argmax.hip", "launch.hip",
+               "kern_q4g32_swiglu.hip", "kern_argmax_epi.hip", "kern_mma.hip", "argmax.hip", "read_stream.hip",
+               "launch.hip",
                "abi.cpp"]
 HOST_SOURCES = ["qpack.cpp"]
 

@@ -15,6 +15,7 @@
 #include "../../include/qgemv.h"
 #include "argmax.h"
 #include "launch.h"
+#include "read_stream.h"
 
 namespace {
 
@@ -397,6 +398,20 @@ uint64_t qg_route_count(const char* variant)
                 if (strcmp(buf, variant) == 0) return g_route[k][m][g].load();
             }
     return 0;
+}
+
+qg_status qg_read_stream(const void* buf, size_t bytes, uint32_t* sink, int32_t waves_per_cu,
+                         void* hip_stream)
+{
+    if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || waves_per_cu < 0 || waves_per_cu > 32)
+        return QG_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(buf) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+        return QG_ERR_ALIGNMENT;
+    (void)hipGetLastError();
+    if (qg::launch_read_stream(buf, int64_t(bytes / 16), sink, waves_per_cu ? waves_per_cu : 8,
+                               static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+        return QG_ERR_HIP;
+    return QG_OK;
 }
 
 qg_status qg_set_launch_override(int64_t target_waves, int32_t contig, int32_t ring_depth)

@@ -101,6 +101,7 @@ def lib() -> ctypes.CDLL:
             "qg_route_count": ([ctypes.c_char_p], ctypes.c_uint64),
             "qg_variant_name": ([ctypes.c_int, i64, i64, i64, ctypes.c_char_p, sz], st),
             "qg_set_launch_override": ([i64, ctypes.c_int32, ctypes.c_int32], st),
+            "qg_read_stream": ([p, sz, p, ctypes.c_int32, p], st),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -636,6 +637,13 @@ def variant_name(fmt: int, m: int, N: int, K: int) -> str:
     buf = ctypes.create_string_buffer(64)
     _check(lib().qg_variant_name(fmt, m, N, K, buf, 64), "qg_variant_name")
     return buf.value.decode()
+
+
+def read_stream(buf, sink, nbytes=None, waves_per_cu: int = 0, stream=None) -> None:
+    """qg_read_stream over the first nbytes (default: all) of device tensor buf."""
+    nbytes = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    _check(lib().qg_read_stream(buf.data_ptr(), nbytes, sink.data_ptr(), waves_per_cu,
+                                _stream_handle(stream)), "qg_read_stream")
 
 
 def set_launch_override(target_waves: int = 0, contig: int = -1, ring_depth: int = 0) -> None:
