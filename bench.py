@@ -662,8 +662,11 @@ def main():
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = n
         del src, dst
-    if args.secondary and args.workload in ("lm_head", "moe_experts"):
-        other = "moe_experts" if args.workload == "lm_head" else "lm_head"
+    # The routed-expert step beside the LM head: gate and up rows stacked into
+    # one grouped call (their fp32 outputs still written separately), then the
+    # grouped down call.
+    if args.secondary and args.workload in ("lm_head", "moe_experts", "moe_experts_merged"):
+        other = "moe_experts_merged" if args.workload == "lm_head" else "lm_head"
         del head
         torch.cuda.empty_cache()
         sec = measure(other)
