@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 LLC_BYTES = 256 << 20          # MI355X last-level (Infinity) cache
 HOT = False                    # --hot: one weight copy / one id set (cache-resident when it fits)
+STACKED = False                # --stacked: projections sharing an activation in one matrix
 METRIC = "effective weight GB/s and % of HBM peak, m=1 quantized GEMV (µs/call)"
 
 
@@ -306,9 +307,25 @@ def cpu_lm_head(oracle, cpu, threads, reps):
 
 # ------------------------------------------------------ small dense configs
 
+# --stacked: projections that read the same activation become one matrix
+# whose rows are the members' rows in order (rows are independent, so each
+# output is the same bits as in its own call; the merged gate_up matrix of
+# vllm.cpp PR #1936 is the pattern).
+STACK_GROUPS = {"qwen3_0.6b": [("q", "k", "v"), ("gate", "up")],
+                "q4_k2560": [("gate", "up")],
+                "w8a16_qwen3_14b_tp4": [("gate", "up")]}
+
+
+def _stack_group(name, label):
+    for g in STACK_GROUPS.get(name, []):
+        if label in g:
+            return g
+    return None
+
+
 def setup_dense(torch, Q, synth, name, m=1):
     """q8_small (1 GEMV), qwen3_0.6b (7 GEMVs), q4_k2560 (3 GEMVs) or
-    w8a16_qwen3_14b_tp4 (5 GEMVs) per step."""
+    w8a16_qwen3_14b_tp4 (5 GEMVs) per step; with --stacked, 4, 2 and 4."""
     wid = synth.WORKLOAD_IDS[name]
     if name == "q8_small":
         mats = [("w", "q8g64", 1024, 1024)]
@@ -323,19 +340,37 @@ def setup_dense(torch, Q, synth, name, m=1):
     else:
         mats = synth.Q4_K2560
         desc = "Q4G32 K=2560 family m=%d: gate/up 2560->9216, down 9216->2560" % m
-    layer, wbytes, io = [], 0, 0
+    gens = []
     for j, (label, fmt, N, K) in enumerate(mats):
         rng = synth.rng_for(wid, j)
         if fmt == "q8g64":
-            packed = Q.qpack_q8g64(*synth.q8g64_weights(rng, N, K))
-            wbytes += synth.bytes_q8g64(N, K)
+            w, nb = synth.q8g64_weights(rng, N, K), synth.bytes_q8g64(N, K)
         elif fmt == "q8pc":
-            packed = Q.qpack_q8pc(*synth.q8pc_weights(rng, N, K))
-            wbytes += synth.bytes_q8pc(N, K)
+            w, nb = synth.q8pc_weights(rng, N, K), synth.bytes_q8pc(N, K)
         else:
-            packed = Q.qpack_q4g32(*synth.q4g32_weights(rng, N, K))
-            wbytes += synth.bytes_q4g32(N, K)
-        x = dev(torch, synth.activations(rng, m, K))
+            w, nb = synth.q4g32_weights(rng, N, K), synth.bytes_q4g32(N, K)
+        gens.append([label, fmt, N, K, w, synth.activations(rng, m, K), nb])
+    if STACKED:
+        merged = []
+        for e in gens:
+            grp = _stack_group(name, e[0])
+            if merged and grp is not None and _stack_group(name, merged[-1][0].split("+")[0]) is grp:
+                prev = merged[-1]
+                prev[0] += "+" + e[0]
+                prev[2] += e[2]
+                prev[4] = tuple(np.concatenate([a, b]) for a, b in zip(prev[4], e[4]))
+                prev[6] += e[6]
+            else:
+                merged.append(list(e))
+        gens = merged
+        mats = [(e[0], e[1], e[2], e[3]) for e in gens]
+        desc += " (stacked: %s)" % ", ".join(e[0] for e in gens)
+    layer, wbytes, io = [], 0, 0
+    packers = {"q8g64": Q.qpack_q8g64, "q8pc": Q.qpack_q8pc, "q4g32": Q.qpack_q4g32}
+    for label, fmt, N, K, w, xh, nb in gens:
+        packed = packers[fmt](*w)
+        wbytes += nb
+        x = dev(torch, xh)
         y = torch.empty((m, N), dtype=torch.float32, device="cuda")
         io += m * (2 * K + 4 * N)
         layer.append((fmt, N, K, packed, x, y))
@@ -538,6 +573,9 @@ def main():
     ap.add_argument("--hot", action="store_true",
                     help="one weight copy and one expert-id set, reused every step: the "
                          "cache-resident (hot) number, reported separately from the default cold one")
+    ap.add_argument("--stacked", action="store_true",
+                    help="qwen3_0.6b, q4_k2560, w8a16_qwen3_14b_tp4: stack the projections that "
+                         "share an activation (q+k+v, gate+up) into one matrix per launch")
     ap.add_argument("--graph", action="store_true",
                     help="replay the timed steps from a captured HIP graph (no host launch cost)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -550,8 +588,9 @@ def main():
     ap.add_argument("--no-read-stream", dest="read_stream", action="store_false",
                     help="skip timing a plain read of the same bytes per launch")
     args = ap.parse_args()
-    global HOT
+    global HOT, STACKED
     HOT = args.hot
+    STACKED = args.stacked
     if args.workload.endswith("_mma") and not 1 <= args.m <= 16:
         print("--m %d: the matrix-core workloads take 1..16 rows" % args.m, file=sys.stderr)
         sys.exit(2)
