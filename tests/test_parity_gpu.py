@@ -179,6 +179,33 @@ def test_moe_grouped_full_size(proj):
     assert_parity(y_gpu, y_ref, a_ref, "moe " + proj)
 
 
+def test_moe_merged_gate_up_full_size():
+    # The routed-expert step the benchmark times beside the LM head: each
+    # expert's gate and up rows stacked into one 3072 x 4096 matrix, 128
+    # experts, 8 routed; the first 1536 outputs of a slot are gate, the rest up.
+    n_experts, n_slots = synth.MOE["n_experts"], synth.MOE["n_slots"]
+    ids = synth.expert_ids(synth.rng_for(4, 1000, 1), n_experts, n_slots)
+    used = set(ids.tolist())
+    gate, N, K = _moe_experts("gate", n_experts, used, 43)
+    up, _, _ = _moe_experts("up", n_experts, used, 44)
+    merged, cache = [], {}
+    for g, u in zip(gate, up):
+        key = (id(g), id(u))
+        if key not in cache:
+            cache[key] = tuple(np.concatenate([a, b]) for a, b in zip(g, u))
+        merged.append(cache[key])
+    buf, stride = _upload_experts(merged, 2 * N, K)
+    x1 = synth.activations(synth.rng_for(4, 2001), 1, K)
+    y = canary((n_slots, 2 * N))
+    Q.qgemv_grouped_q4g32(buf, stride, n_experts, dev(ids), dev(x1), 0, y, 2 * N, 2 * N, K)
+    y_gpu = host(y)
+    xs = np.repeat(x1, n_slots, axis=0)
+    g_ref, g_a = oracle.grouped_q4g32(gate, ids, xs, threads=THREADS)
+    u_ref, u_a = oracle.grouped_q4g32(up, ids, xs, threads=THREADS)
+    assert_parity(y_gpu[:, :N], g_ref, g_a, "merged gate half")
+    assert_parity(y_gpu[:, N:], u_ref, u_a, "merged up half")
+
+
 # ------------------------------------------------------------ shape sweep
 
 @pytest.mark.parametrize("N", [1, 7, 129, 1000])
