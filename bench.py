@@ -37,12 +37,12 @@ METRIC = "effective weight GB/s and % of HBM peak, m=1 quantized GEMV (µs/call)
 # known size.  Valid only for the kernel sources they were taken on (and,
 # for an entry with "m", for that number of activation rows).
 TRAFFIC = {
-    "lm_head": {"source_digest": "1a235fc2096c95bf", "bytes_per_launch": 403393981},
-    "lm_head_q8g128": {"source_digest": "b9c986b71a66e6b8", "bytes_per_launch": 396782862},
-    "moe_experts": {"source_digest": "c2fe60c4694a9a1b", "bytes_per_launch": 31808840},
-    "moe_experts_swiglu": {"source_digest": "960ffac13ad09421", "bytes_per_launch": 47587822},
-    "lm_head_argmax_fused": {"source_digest": "b9150bc715f14e21", "bytes_per_launch": 402908059},
-    "lm_head_mma": {"source_digest": "1dc13ff2629dc95b", "bytes_per_launch": 409369367, "m": 8},
+    "lm_head": {"source_digest": "3bc72cdfeb32a7bb", "bytes_per_launch": 403444491},
+    "lm_head_q8g128": {"source_digest": "f6d5d5213b6a92fd", "bytes_per_launch": 396858764},
+    "moe_experts": {"source_digest": "b4e88a2430bfea11", "bytes_per_launch": 31808840},
+    "moe_experts_swiglu": {"source_digest": "fbcda5a3ebd34bd0", "bytes_per_launch": 47587822},
+    "lm_head_argmax_fused": {"source_digest": "6c893beab5bda0c6", "bytes_per_launch": 402952282},
+    "lm_head_mma": {"source_digest": "3384f6858735019b", "bytes_per_launch": 409586003, "m": 8},
 }
 
 

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "launch.h"
 
 namespace qg {
@@ -33,16 +35,20 @@ void set_launch_override(const LaunchOverride& o)
 // Compute units of the current device, looked up once per device.
 static int64_t compute_units()
 {
-    static int64_t cached[64] = {};
+    // Calls may come from several host threads: the cache is atomic (every
+    // thread that finds it empty stores the same value).
+    static std::atomic<int64_t> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
+    int64_t v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cached[dev] = n;
+        v = n;
+        cached[dev].store(v, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return v;
 }
 
 size_t lds_bytes_for(const Layout& L, int m)

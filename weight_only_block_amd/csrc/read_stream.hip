@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "read_stream.h"
 
 namespace qg {
@@ -53,16 +55,20 @@ __global__ __launch_bounds__(64 * kReadWaves) void read_stream_kernel(const u32x
 
 int64_t device_compute_units()
 {
-    static int64_t cached[64] = {};
+    // Calls may come from several host threads: the cache is atomic (every
+    // thread that finds it empty stores the same value).
+    static std::atomic<int64_t> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
+    int64_t v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cached[dev] = n;
+        v = n;
+        cached[dev].store(v, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return v;
 }
 
 }  // namespace
