@@ -262,19 +262,16 @@ def setup_mma(torch, Q, synth, name, m):
         desc = ("Qwen3-14B TP4 rank-local decode layer, per-output-channel W8A16 on the matrix "
                 "cores m=%d: qkv 5120->1792, o 1280->5120, gate/up 5120->8704, down 4352->5120" % m)
         wid = synth.WORKLOAD_IDS["w8a16_qwen3_14b_tp4"]
+    gens = _generate(synth, name[:-len("_mma")], mats, wid, m)
+    if STACKED and len(gens) < len(mats):
+        mats = [(e[0], e[1], e[2], e[3]) for e in gens]
+        desc += " (stacked: %s)" % ", ".join(e[0] for e in gens)
     layer, wbytes, io = [], 0, 0
-    for j, (label, fmt, N, K) in enumerate(mats):
-        rng = synth.rng_for(wid, j)
-        if fmt == "q8g64":
-            packed = Q.qpack_q8g64_mma(*synth.q8g64_weights(rng, N, K))
-            wbytes += synth.bytes_q8g64(N, K)
-        elif fmt == "q4g32":
-            packed = Q.qpack_q4g32_mma(*synth.q4g32_weights(rng, N, K))
-            wbytes += synth.bytes_q4g32(N, K)
-        else:
-            packed = Q.qpack_q8pc_mma(*synth.q8pc_weights(rng, N, K))
-            wbytes += synth.bytes_q8pc(N, K)
-        x = dev(torch, synth.activations(rng, m, K))
+    packers = {"q8g64": Q.qpack_q8g64_mma, "q4g32": Q.qpack_q4g32_mma, "q8pc": Q.qpack_q8pc_mma}
+    for label, fmt, N, K, w, xh, nb in gens:
+        packed = packers[fmt](*w)
+        wbytes += nb
+        x = dev(torch, xh)
         y = torch.empty((m, N), dtype=torch.float32, device="cuda")
         io += m * (2 * K + 4 * N)
         layer.append((fmt, N, K, packed, x, y))
@@ -323,6 +320,37 @@ def _stack_group(name, label):
     return None
 
 
+def _generate(synth, group_name, mats, wid, m):
+    """Seeded weights and m activation rows per matrix, in layer order; with
+    --stacked, the matrices of a stacking group merged into one (the first
+    member's activation serves the group).  Entries: [label, fmt, N, K,
+    canonical weights, x, algorithmic weight bytes]."""
+    gens = []
+    for j, (label, fmt, N, K) in enumerate(mats):
+        rng = synth.rng_for(wid, j)
+        if fmt == "q8g64":
+            w, nb = synth.q8g64_weights(rng, N, K), synth.bytes_q8g64(N, K)
+        elif fmt == "q8pc":
+            w, nb = synth.q8pc_weights(rng, N, K), synth.bytes_q8pc(N, K)
+        else:
+            w, nb = synth.q4g32_weights(rng, N, K), synth.bytes_q4g32(N, K)
+        gens.append([label, fmt, N, K, w, synth.activations(rng, m, K), nb])
+    if not STACKED:
+        return gens
+    merged = []
+    for e in gens:
+        grp = _stack_group(group_name, e[0])
+        if merged and grp is not None and _stack_group(group_name, merged[-1][0].split("+")[0]) is grp:
+            prev = merged[-1]
+            prev[0] += "+" + e[0]
+            prev[2] += e[2]
+            prev[4] = tuple(np.concatenate([a, b]) for a, b in zip(prev[4], e[4]))
+            prev[6] += e[6]
+        else:
+            merged.append(list(e))
+    return merged
+
+
 def setup_dense(torch, Q, synth, name, m=1):
     """q8_small (1 GEMV), qwen3_0.6b (7 GEMVs), q4_k2560 (3 GEMVs) or
     w8a16_qwen3_14b_tp4 (5 GEMVs) per step; with --stacked, 4, 2 and 4."""
@@ -340,29 +368,8 @@ def setup_dense(torch, Q, synth, name, m=1):
     else:
         mats = synth.Q4_K2560
         desc = "Q4G32 K=2560 family m=%d: gate/up 2560->9216, down 9216->2560" % m
-    gens = []
-    for j, (label, fmt, N, K) in enumerate(mats):
-        rng = synth.rng_for(wid, j)
-        if fmt == "q8g64":
-            w, nb = synth.q8g64_weights(rng, N, K), synth.bytes_q8g64(N, K)
-        elif fmt == "q8pc":
-            w, nb = synth.q8pc_weights(rng, N, K), synth.bytes_q8pc(N, K)
-        else:
-            w, nb = synth.q4g32_weights(rng, N, K), synth.bytes_q4g32(N, K)
-        gens.append([label, fmt, N, K, w, synth.activations(rng, m, K), nb])
+    gens = _generate(synth, name, mats, wid, m)
     if STACKED:
-        merged = []
-        for e in gens:
-            grp = _stack_group(name, e[0])
-            if merged and grp is not None and _stack_group(name, merged[-1][0].split("+")[0]) is grp:
-                prev = merged[-1]
-                prev[0] += "+" + e[0]
-                prev[2] += e[2]
-                prev[4] = tuple(np.concatenate([a, b]) for a, b in zip(prev[4], e[4]))
-                prev[6] += e[6]
-            else:
-                merged.append(list(e))
-        gens = merged
         mats = [(e[0], e[1], e[2], e[3]) for e in gens]
         desc += " (stacked: %s)" % ", ".join(e[0] for e in gens)
     layer, wbytes, io = [], 0, 0
@@ -574,8 +581,9 @@ def main():
                     help="one weight copy and one expert-id set, reused every step: the "
                          "cache-resident (hot) number, reported separately from the default cold one")
     ap.add_argument("--stacked", action="store_true",
-                    help="qwen3_0.6b, q4_k2560, w8a16_qwen3_14b_tp4: stack the projections that "
-                         "share an activation (q+k+v, gate+up) into one matrix per launch")
+                    help="qwen3_0.6b, q4_k2560, w8a16_qwen3_14b_tp4 and their *_mma forms: stack the "
+                         "projections that share an activation (q+k+v, gate+up) into one matrix "
+                         "per launch")
     ap.add_argument("--graph", action="store_true",
                     help="replay the timed steps from a captured HIP graph (no host launch cost)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
