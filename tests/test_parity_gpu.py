@@ -396,6 +396,35 @@ def test_graph_replays_match_eager_calls():
         assert np.array_equal(got_g, host(yge)), "replay %d grouped" % r
 
 
+@pytest.mark.parametrize("fmt,parts,K", [
+    ("q8g64", (2048, 1024, 1024), 1024),     # q, k, v of the 0.6B layer
+    ("q8g64", (3072, 3072), 1024),           # gate, up
+    ("q4g32", (9216, 9216), 2560),
+    ("q8g128", (701, 1299), 2048),           # a part ending inside a tile
+    ("q8pc", (8704, 8704), 5120)])
+def test_stacked_rows_equal_separate_calls_bitwise(fmt, parts, K):
+    # A matrix made of several matrices' rows stacked in order (the stacked
+    # projections of a layer) gives each part's outputs bit for bit, because
+    # every output row is computed the same way in any matrix.
+    gen = {"q8g64": synth.q8g64_weights, "q4g32": synth.q4g32_weights,
+           "q8g128": synth.q8g128_weights, "q8pc": synth.q8pc_weights}[fmt]
+    pack = getattr(Q, "qpack_" + fmt)
+    call = getattr(Q, "qgemv_" + fmt)
+    mats = [gen(synth.rng_for(20, j, K), N, K) for j, N in enumerate(parts)]
+    stacked = tuple(np.concatenate(arrs) for arrs in zip(*mats))
+    x = dev(synth.activations(synth.rng_for(20, 99, K), 2, K))
+    Ns = sum(parts)
+    ys = canary((2, Ns))
+    call(dev(pack(*stacked)), x, ys, Ns, K)
+    ys = host(ys)
+    off = 0
+    for j, (w, N) in enumerate(zip(mats, parts)):
+        y = canary((2, N))
+        call(dev(pack(*w)), x, y, N, K)
+        assert np.array_equal(host(y).view(np.uint32), ys[:, off:off + N].view(np.uint32)), "part %d" % j
+        off += N
+
+
 def test_merged_gate_up_equals_separate_calls_bitwise():
     # Stacking each expert's gate and up rows into one [2N][K] matrix is a row
     # concatenation; every output row is computed the same way, so the merged
