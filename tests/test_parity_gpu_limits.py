@@ -1,4 +1,4 @@
-"""GPU: the largest activations the VALU kernels accept.
+"""GPU: the largest activations and slot counts the VALU kernels accept.
 
 The staged activation rows (bf16 plus one fp32 sum per unit, for m rows) must
 fit in the 159 KiB of dynamic LDS a work-group may use.  For each format and
@@ -6,7 +6,7 @@ row count the test finds the largest K the library accepts (its own check,
 through qg_variant_name), confirms that one more scale group is rejected
 with QG_ERR_UNSUPPORTED, and checks the call at that K against the oracle.
 These launches stage x over many rounds and use more than the default
-64 KiB of dynamic LDS.
+64 KiB of dynamic LDS.  The grouped calls are also run at their 64-slot limit.
 """
 import os
 
@@ -72,3 +72,30 @@ def test_largest_staged_activation(fmt, m, N):
     y_ref, a_ref = getattr(oracle, fmt)(*wts, x, threads=THREADS)
     ok = oracle.within_tolerance(y.cpu().numpy(), y_ref, a_ref, 2e-3)
     assert ok.all(), "%s m=%d N=%d K=%d: %d outputs out of tolerance" % (fmt, m, N, K, (~ok).sum())
+
+
+def test_grouped_calls_at_the_slot_limit():
+    # 64 slots (the most a grouped call takes), expert ids repeating, one x
+    # per slot; the plain grouped call and the SwiGLU call against the oracle.
+    n_experts, n_slots, N, K = 9, 64, 200, 512
+    ids = synth.rng_for(103, 0).integers(0, n_experts, n_slots).astype(np.int32)
+    xs = synth.activations(synth.rng_for(103, 1), n_slots, K)
+    experts = [synth.q4g32_weights(synth.rng_for(103, 2, e), N, K) for e in range(n_experts)]
+    stride = Q.expert_stride(N, K)
+    buf = torch.cat([torch.from_numpy(Q.qpack_q4g32(*e)) for e in experts]).to("cuda")
+    y = torch.full((n_slots, N), float("nan"), dtype=torch.float32, device="cuda")
+    Q.qgemv_grouped_q4g32(buf, stride, n_experts, dev(ids), dev(xs), K, y, N, N, K)
+    torch.cuda.synchronize()
+    y_ref, a_ref = oracle.grouped_q4g32(experts, ids, xs, threads=THREADS)
+    assert oracle.within_tolerance(y.cpu().numpy(), y_ref, a_ref, 2e-3).all()
+
+    ups = [synth.q4g32_weights(synth.rng_for(103, 3, e), N, K) for e in range(n_experts)]
+    gstride = Q.gate_up_expert_stride(N, K)
+    gbuf = torch.cat([torch.from_numpy(Q.qpack_q4g32_gate_up(g, u)) for g, u in zip(experts, ups)]).to("cuda")
+    act = torch.full((n_slots, N), 0x7FAB, dtype=torch.int16, device="cuda")
+    Q.qgemv_grouped_q4g32_swiglu(gbuf, gstride, n_experts, dev(ids), dev(xs), K, act, N, N, K)
+    torch.cuda.synchronize()
+    ref, g, u, a_g, a_u = oracle.grouped_q4g32_swiglu(experts, ups, ids, xs, threads=THREADS)
+    got = (act.cpu().numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    tol = oracle.swiglu_tolerance(ref, g, u, a_g, a_u)
+    assert (np.isfinite(got) & (np.abs(got - ref) <= tol)).all()
