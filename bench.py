@@ -41,6 +41,7 @@ TRAFFIC = {
     "lm_head_q8g128": {"source_digest": "f6d5d5213b6a92fd", "bytes_per_launch": 396858764},
     "moe_experts": {"source_digest": "b4e88a2430bfea11", "bytes_per_launch": 31808840},
     "moe_experts_swiglu": {"source_digest": "fbcda5a3ebd34bd0", "bytes_per_launch": 47587822},
+    "moe_experts_merged": {"source_digest": "b4e88a2430bfea11", "bytes_per_launch": 47600825},
     "lm_head_argmax_fused": {"source_digest": "6c893beab5bda0c6", "bytes_per_launch": 402952282},
     "lm_head_mma": {"source_digest": "3384f6858735019b", "bytes_per_launch": 409586003, "m": 8},
 }
@@ -55,6 +56,7 @@ KERNEL_SOURCES = {
     "lm_head_q8g128": _COMMON_SOURCES + ("kern_q8g128.hip",),
     "moe_experts": _COMMON_SOURCES + ("kern_q4g32.hip",),
     "moe_experts_swiglu": _COMMON_SOURCES + ("kern_q4g32_swiglu.hip", "kern_q4g32.hip"),
+    "moe_experts_merged": _COMMON_SOURCES + ("kern_q4g32.hip",),
     "lm_head_argmax": _COMMON_SOURCES + ("kern_q8g64.hip", "argmax.hip", "argmax.h"),
     "lm_head_argmax_fused": _COMMON_SOURCES + ("kern_argmax_epi.hip", "argmax.h"),
     "lm_head_mma": ("kern_mma.hip", "launch.hip", "layout.h", "launch.h"),
