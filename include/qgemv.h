@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define QG_ABI_VERSION 1
+#define QG_ABI_VERSION 2
 
 typedef enum qg_status {
     QG_OK = 0,

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert Q.lib().qg_abi_version() == 1
+    assert Q.lib().qg_abi_version() == 2
     for s in range(5):
         assert Q.status_string(s)
     assert Q.status_string(99) == "unknown status"
@@ -355,8 +355,9 @@ def test_q4g32_mma_pack_layout_and_roundtrip():
     # Layout of the Q4G32 matrix-core packing, checked against the
     # documented formula: in block (tile t, step j), lane l = 16 qs + rho,
     # dword g holds the codes of row 16 t + rho at k = 128 j + 32 g + 8 qs + e
-    # with e at nibble position (0, 4, 1, 5, 2, 6, 3, 7)[e]; then the meta
-    # dwords scale | min << 16 at [tile][step][row][group].
+    # in canonical byte order (e at nibble position e: byte e // 2, low
+    # nibble for even e); then the meta dwords scale | min << 16 at
+    # [tile][step][row][group].
     N, K = 37, 384
     n_idx = np.arange(N)[:, None]
     k_idx = np.arange(K)[None, :]
@@ -367,7 +368,7 @@ def test_q4g32_mma_pack_layout_and_roundtrip():
     buf = Q.qpack_q4g32_mma(codes, s, mn)
     tiles, J = (N + 15) // 16, K // 128
     assert buf.nbytes == Q.qpack_mma_size("q4g32", N, K) == -(-(tiles * J * 1024 + tiles * J * 256) // 256) * 256
-    pos = (0, 4, 1, 5, 2, 6, 3, 7)
+    pos = tuple(range(8))
     for (t, j, qs, rho, g) in [(0, 0, 0, 0, 0), (1, 2, 3, 5, 1), (2, 1, 2, 4, 3), (0, 2, 1, 15, 2)]:
         n = 16 * t + rho
         word = int(buf[(t * J + j) * 1024 + (16 * qs + rho) * 16 + 4 * g:][:4].view(np.uint32)[0])

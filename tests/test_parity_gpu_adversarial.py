@@ -1,0 +1,327 @@
+"""GPU parity on adversarial inputs: outputs whose sum |w x| is tiny next to
+the magnitudes that pass through the kernel's arithmetic.
+
+The bar is the same per-element one as everywhere else,
+|y_gpu - y_ref| <= 2e-3 * sum_k |w x| (fp64, y_gpu finite), so a row whose
+weights are all exactly zero must come back as exactly zero, and a row with
+one nonzero weight on a 1e-5 activation must come back within 2e-3 of that
+one product, however large the other activations of its 16- or 32-wide unit
+are.  Input classes, at the shapes of the LM head (151936 x 2560) and of the
+routed experts (128 experts, gate/up 1536 x 4096, down 4096 x 1536):
+
+* activations: N(0, 1) with one small value (|x| = 1e-5 .. 1e-2) in every
+  16-wide unit and a few outliers (|x| = 20 .. 60);
+* 8-bit rows: a handful of nonzero codes, all on small activations; exactly
+  one nonzero code; all-zero rows; rows with random finite fp16 scales
+  (subnormals included); ordinary rows as a control;
+* 4-bit groups: constant codes c with a power-of-two scale and min = -c s
+  (every weight exactly zero), the same with one code off by one on a small
+  activation, constant codes with min = fp16(-c s) for an ordinary scale
+  (weights that nearly cancel), groups whose min cancels one code value
+  among random codes, and ordinary groups.
+
+The vllm.cpp pull request #1936 commit log gates its quantized GEMV on the
+CPU oracle under adversarial conditions of this kind (tied amax, all-zero
+rows); these tests apply that gate to the benchmark spec's tolerance.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from weight_only_block_amd import qgemv as Q
+from weight_only_block_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+CANARY_BITS = 0x7FC0DEAD
+THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    Q.lib()
+
+
+def dev(a: np.ndarray) -> "torch.Tensor":
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to("cuda")
+
+
+def canary(shape) -> "torch.Tensor":
+    return torch.full(shape, CANARY_BITS, dtype=torch.int32, device="cuda").view(torch.float32)
+
+
+def host(t) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_parity(y_gpu, y_ref, a_ref, what=""):
+    y_gpu = np.asarray(y_gpu, np.float64)
+    ok = oracle.within_tolerance(y_gpu, y_ref, a_ref, TOL)
+    if not ok.all():
+        bad = np.argwhere(~ok)[:5]
+        details = [(tuple(b), y_gpu[tuple(b)], y_ref[tuple(b)], a_ref[tuple(b)]) for b in bad]
+        raise AssertionError("%s: %d of %d outputs out of tolerance, e.g. %s"
+                             % (what, (~ok).sum(), ok.size, details))
+
+
+# ------------------------------------------------------------- input classes
+
+def adversarial_x(rng, m, K):
+    """bf16 [m][K]: N(0, 1), one small activation per 16-wide unit, outliers.
+    Returns the bits and the small positions (the same in every row)."""
+    x = rng.standard_normal((m, K)).astype(np.float32)
+    small = np.arange(K // 16) * 16 + rng.integers(0, 16, K // 16)
+    x[:, small] = (10.0 ** rng.uniform(-5, -2, (m, small.size))
+                   * rng.choice([-1.0, 1.0], (m, small.size))).astype(np.float32)
+    others = np.setdiff1d(np.arange(K), small)
+    big = rng.choice(others, K // 64, replace=False)
+    x[:, big] = (rng.uniform(20, 60, (m, big.size)) * rng.choice([-1.0, 1.0], (m, big.size))).astype(np.float32)
+    return synth.to_bf16_bits(x), small
+
+
+def random_fp16_scales(rng, shape):
+    """Any finite fp16 value, either sign, subnormals included."""
+    mag = rng.integers(1, 0x7C00, size=shape, dtype=np.uint16)
+    return (mag | (rng.integers(0, 2, size=shape, dtype=np.uint16) << 15)).astype(np.uint16)
+
+
+def sparse_q8(rng, N, K, small, groups):
+    """int8 codes and fp16 scales ([N][K // (K / groups)]) by row class n % 8:
+    0 a handful of nonzero codes on small activations, 1 one nonzero code on
+    a small activation, 2 one nonzero code anywhere, 3 all zero, 4 a handful
+    on small activations with random finite fp16 scales, 5-7 ordinary."""
+    q = rng.integers(-127, 128, size=(N, K), dtype=np.int8)
+    s = synth.to_fp16_bits(rng.uniform(1e-3, 2e-2, size=(N, groups)))
+    cls = np.arange(N) % 8
+    q[cls <= 4] = 0
+    nz = lambda n: (rng.integers(1, 128, n) * rng.choice([-1, 1], n)).astype(np.int8)
+    for c, count in ((0, 6), (1, 1), (4, 6)):
+        rows = np.flatnonzero(cls == c)
+        cols = small[rng.integers(0, small.size, (rows.size, count))]
+        q[rows[:, None], cols] = nz(rows.size * count).reshape(rows.size, count)
+    rows = np.flatnonzero(cls == 2)
+    q[rows, rng.integers(0, K, rows.size)] = nz(rows.size)
+    rows = np.flatnonzero(cls == 4)
+    s[rows] = random_fp16_scales(rng, (rows.size, groups))
+    return q, s
+
+
+def cancelling_q4(rng, N, K, small):
+    """Q4G32 canonical (codes, scales, mins) by row class n % 6:
+    0 every group's weights exactly zero (constant code c, scale 2^-e,
+    min = -c 2^-e), 1 the same with one code off by one on a small
+    activation, 2 constant codes with min = fp16(-c s) for an ordinary s,
+    3 each group one of the classes 0, 1, 2, 4 or ordinary, 4 random codes
+    whose min cancels one code value, 5 ordinary."""
+    G = K // 32
+    c = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    s = rng.uniform(1e-3, 2e-2, size=(N, G))
+    mn = rng.uniform(-0.1, 0.0, size=(N, G))
+    row_cls = np.arange(N) % 6
+    gcls = np.repeat(row_cls[:, None], G, axis=1)
+    gcls = np.where(gcls == 3, rng.choice([0, 1, 2, 4, 5], size=(N, G)), gcls)
+    const = rng.integers(1, 16, size=(N, G))
+    # classes 0 and 1: constant code, power-of-two scale, exact zero weights
+    exact = (gcls == 0) | (gcls == 1)
+    p2 = 2.0 ** -rng.integers(3, 11, size=(N, G))
+    s = np.where(exact, p2, s)
+    # class 2: constant code, ordinary scale, min = fp16(-c s) (RNE below)
+    flat_const = (gcls <= 2)
+    cc = np.repeat(const, 32, axis=1).astype(np.uint8)
+    c = np.where(np.repeat(flat_const, 32, axis=1), cc, c)
+    # class 1: one code off by one at the group's first small position
+    g_of_small = small // 32
+    first = np.full(G, -1)
+    for k in small[::-1]:
+        first[k // 32] = k
+    n1, g1 = np.nonzero(gcls == 1)
+    k1 = first[g1]
+    keep = k1 >= 0
+    n1, g1, k1 = n1[keep], g1[keep], k1[keep]
+    c[n1, k1] = np.where(c[n1, k1] == 15, 14, c[n1, k1] + 1).astype(np.uint8)
+    del g_of_small
+    # class 4: random codes, min cancels one code value
+    c0 = rng.integers(1, 16, size=(N, G))
+    mn = np.where(flat_const, -const * s, mn)
+    mn = np.where(gcls == 4, -c0 * s, mn)
+    s16 = synth.to_fp16_bits(s)
+    mn16 = synth.to_fp16_bits(mn)
+    return synth.pack_nibbles(c), s16, mn16
+
+
+# ------------------------------------------------------------------ LM head
+
+@pytest.mark.parametrize("fmt", ["q8g64", "q8g128"])
+def test_lm_head_sparse_rows_small_activations(fmt):
+    N, K = synth.LM_HEAD[2], synth.LM_HEAD[3]
+    rng = synth.rng_for(70, 0 if fmt == "q8g64" else 1)
+    x, small = adversarial_x(rng, 1, K)
+    group = 64 if fmt == "q8g64" else 128
+    q, s = sparse_q8(rng, N, K, small, K // group)
+    packed = dev(getattr(Q, "qpack_" + fmt)(q, s))
+    y = canary((1, N))
+    getattr(Q, "qgemv_" + fmt)(packed, dev(x), y, N, K)
+    y_gpu = host(y)
+    y_ref, a_ref = getattr(oracle, fmt)(q, s, x, threads=THREADS)
+    assert_parity(y_gpu, y_ref, a_ref, "lm_head " + fmt)
+    zero_rows = np.arange(N) % 8 == 3
+    assert np.all(y_gpu[0, zero_rows] == 0.0), "all-zero rows must give exactly zero"
+
+
+@pytest.mark.parametrize("m", [2, 4])
+def test_lm_head_sparse_rows_multi_row(m):
+    # The VALU path at m > 1 (one weight pass for m activation rows), on a
+    # slice of the LM head's rows (the row classes repeat every 8 rows).
+    N, K = 24576, 2560
+    rng = synth.rng_for(71, m)
+    x, small = adversarial_x(rng, m, K)
+    q, s = sparse_q8(rng, N, K, small, K // 64)
+    y = canary((m, N))
+    Q.qgemv_q8g64(dev(Q.qpack_q8g64(q, s)), dev(x), y, N, K)
+    y_ref, a_ref = oracle.q8g64(q, s, x, threads=THREADS)
+    assert_parity(host(y), y_ref, a_ref, "q8g64 m=%d" % m)
+
+
+@pytest.mark.parametrize("m", [1, 5, 16])
+def test_lm_head_sparse_rows_matrix_cores(m):
+    N, K = 24576, 2560
+    rng = synth.rng_for(72, m)
+    x, small = adversarial_x(rng, m, K)
+    q, s = sparse_q8(rng, N, K, small, K // 64)
+    y = canary((m, N))
+    Q.qgemv_q8g64_mma(dev(Q.qpack_q8g64_mma(q, s)), dev(x), y, N, K)
+    y_ref, a_ref = oracle.q8g64(q, s, x, threads=THREADS)
+    assert_parity(host(y), y_ref, a_ref, "q8g64 matrix cores m=%d" % m)
+
+
+def test_w8a16_sparse_rows_per_channel_scale():
+    # Per-output-channel int8 at the 14B TP4 qkv shape: rows of class 4 get
+    # random finite fp32 scales instead.
+    N, K = 1792, 5120
+    rng = synth.rng_for(73, 0)
+    x, small = adversarial_x(rng, 1, K)
+    q, _ = sparse_q8(rng, N, K, small, 1)
+    s = rng.uniform(1e-3, 2e-2, size=N).astype(np.float32)
+    odd = np.arange(N) % 8 == 4
+    s[odd] = (10.0 ** rng.uniform(-30, 30, odd.sum()) * rng.choice([-1, 1], odd.sum())).astype(np.float32)
+    s = s.view(np.uint32)
+    y = canary((1, N))
+    Q.qgemv_q8pc(dev(Q.qpack_q8pc(q, s)), dev(x), y, N, K)
+    y_ref, a_ref = oracle.q8pc(q, s, x, threads=THREADS)
+    assert_parity(host(y), y_ref, a_ref, "q8pc")
+    ym = canary((1, N))
+    Q.qgemv_q8pc_mma(dev(Q.qpack_q8pc_mma(q, s)), dev(x), ym, N, K)
+    assert_parity(host(ym), y_ref, a_ref, "q8pc matrix cores")
+
+
+# ------------------------------------------------------- routed experts (Q4)
+
+def _experts(proj, used, seed):
+    N, K = synth.MOE[proj]
+    zero = (np.zeros((N, K // 2), np.uint8), np.zeros((N, K // 32), np.uint16),
+            np.zeros((N, K // 32), np.uint16))
+    rng = synth.rng_for(seed, 0)
+    return rng, N, K, zero
+
+
+def _upload(experts, N, K):
+    stride = Q.expert_stride(N, K)
+    buf = torch.zeros(len(experts) * stride, dtype=torch.uint8, device="cuda")
+    for e, ex in enumerate(experts):
+        if ex[0].any() or ex[1].any() or ex[2].any():
+            buf[e * stride:(e + 1) * stride].copy_(torch.from_numpy(Q.qpack_q4g32(*ex)))
+    return buf, stride
+
+
+@pytest.mark.parametrize("proj", ["gate", "down"])
+def test_moe_cancelling_groups(proj):
+    n_experts, n_slots = synth.MOE["n_experts"], synth.MOE["n_slots"]
+    ids = synth.expert_ids(synth.rng_for(74, 1), n_experts, n_slots)
+    ids[0] = n_experts - 1                      # the last expert: 64-bit offset
+    ids = np.array(list(dict.fromkeys(ids.tolist())), np.int32)[:n_slots]
+    rng, N, K, zero = _experts(proj, ids, 75)
+    experts = [zero] * n_experts
+    xs, small = adversarial_x(rng, n_slots, K)
+    for e in ids:
+        experts[e] = cancelling_q4(rng, N, K, small)
+    buf, stride = _upload(experts, N, K)
+    n = len(ids)
+    if proj == "gate":
+        xs = np.repeat(xs[:1], n, axis=0)       # gate/up share the token's x
+        x_stride, xin = 0, xs[:1]
+    else:
+        xs = xs[:n]
+        x_stride, xin = K, xs
+    y = canary((n, N))
+    Q.qgemv_grouped_q4g32(buf, stride, n_experts, dev(ids), dev(xin), x_stride, y, N, N, K)
+    y_gpu = host(y)
+    y_ref, a_ref = oracle.grouped_q4g32(experts, ids, xs, threads=THREADS)
+    assert_parity(y_gpu, y_ref, a_ref, "moe " + proj)
+    zero_rows = np.arange(N) % 6 == 0
+    assert np.all(y_gpu[:, zero_rows] == 0.0), "rows of exactly-zero weights must give zero"
+
+
+def test_moe_swiglu_cancelling_groups():
+    n_experts, n_slots = synth.MOE["n_experts"], synth.MOE["n_slots"]
+    ids = synth.expert_ids(synth.rng_for(74, 2), n_experts, n_slots)
+    rng, N, K, zero = _experts("gate", ids, 76)
+    x, small = adversarial_x(rng, 1, K)
+    gate = [zero] * n_experts
+    up = [zero] * n_experts
+    for e in ids:
+        gate[e] = cancelling_q4(rng, N, K, small)
+        up[e] = cancelling_q4(rng, N, K, small)
+    stride = Q.gate_up_expert_stride(N, K)
+    buf = torch.zeros(n_experts * stride, dtype=torch.uint8, device="cuda")
+    for e in ids:
+        buf[e * stride:(e + 1) * stride].copy_(torch.from_numpy(Q.qpack_q4g32_gate_up(gate[e], up[e])))
+    act = torch.full((n_slots, N), 0x7FBF, dtype=torch.int16, device="cuda")
+    Q.qgemv_grouped_q4g32_swiglu(buf, stride, n_experts, dev(ids), dev(x), 0, act, N, N, K)
+    got = oracle.bf16_to_f64(host(act).view(np.uint16))
+    xs = np.repeat(x, n_slots, axis=0)
+    g, a_g = oracle.grouped_q4g32(gate, ids, xs, threads=THREADS)
+    u, a_u = oracle.grouped_q4g32(up, ids, xs, threads=THREADS)
+    ref = oracle.swiglu(g, u)
+    tol = oracle.swiglu_tolerance(ref, g, u, a_g, a_u)
+    bad = ~(np.abs(got - ref) <= tol)
+    assert not bad.any(), "swiglu: %d outputs out of tolerance" % bad.sum()
+
+
+# ------------------------------------------------------ dense Q4 (K = 2560)
+
+@pytest.mark.parametrize("m", [1, 4])
+@pytest.mark.parametrize("j", [0, 2])
+def test_q4_k2560_cancelling_groups(j, m):
+    label, _, N, K = synth.Q4_K2560[j]
+    rng = synth.rng_for(77, j, m)
+    x, small = adversarial_x(rng, m, K)
+    codes, s, mn = cancelling_q4(rng, N, K, small)
+    y = canary((m, N))
+    Q.qgemv_q4g32(dev(Q.qpack_q4g32(codes, s, mn)), dev(x), y, N, K)
+    y_gpu = host(y)
+    y_ref, a_ref = oracle.q4g32(codes, s, mn, x, threads=THREADS)
+    assert_parity(y_gpu, y_ref, a_ref, "q4 %s m=%d" % (label, m))
+    assert np.all(y_gpu[:, np.arange(N) % 6 == 0] == 0.0)
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_q4_matrix_cores_cancelling_groups(m):
+    label, _, N, K = synth.Q4_K2560[0]
+    rng = synth.rng_for(78, m)
+    x, small = adversarial_x(rng, m, K)
+    codes, s, mn = cancelling_q4(rng, N, K, small)
+    y = canary((m, N))
+    Q.qgemv_q4g32_mma(dev(Q.qpack_q4g32_mma(codes, s, mn)), dev(x), y, N, K)
+    y_gpu = host(y)
+    y_ref, a_ref = oracle.q4g32(codes, s, mn, x, threads=THREADS)
+    assert_parity(y_gpu, y_ref, a_ref, "q4 matrix cores m=%d" % m)
+    assert np.all(y_gpu[:, np.arange(N) % 6 == 0] == 0.0)

@@ -7,18 +7,20 @@
 //
 //  * A (16 x 32): the activation rows (row i = lane mod 16, zero past m),
 //    read from LDS, where x is staged once per work-group.
-//  * B (32 x 16): 16 weight rows, 16 biased codes per lane exactly as one
+//  * B (32 x 16): 16 weight rows, 16 signed codes per lane exactly as one
 //    wave load brings them in (the layout puts row lane mod 16, k-slice
-//    lane div 16 in lane order), widened to bf16 (integers 0..255 are exact).
+//    lane div 16 in lane order), widened to bf16 (every int8 is exact).
 //  * D (16 x 16, fp32): lane l holds D[4*(l div 16) + v][l mod 16].
 //
-// The codes carry a +128 bias, so the MFMA gives D = sum x (q + 128) over a
-// scale group.  A second MFMA with the same A and an all-ones B gives
-// X = sum x over the group in the same arithmetic, so D - 128 X is exactly
-// zero when all codes are zero (scaling B by 128 commutes with rounding).
-// Per group:  acc += s * (D - 128 X)   (s: the row's fp16 group scale, or
-// its fp32 row scale for Q8PC).  Each output is a complete sum when its
-// tile ends, so there is no cross-lane reduction and no atomic.
+// Per scale group:  acc += s * D   (s: the row's fp16 group scale, or its
+// fp32 row scale for Q8PC).  Q4G32 re-centres each 32-group on the integer
+// nearest its zero point (z = clamp(rint(-min / scale), 0, 15), m' =
+// min + scale z), feeds the exact differences c - z as B, and adds the
+// group's activation sum X (a second MFMA against an all-ones B):
+// acc += s * D + m' * X.  No bias is left inside D, so the rounding error
+// of an output stays a few fp32 ulps of sum |w x| (the same argument as the
+// VALU kernels').  Each output is a complete sum when its tile ends, so
+// there is no cross-lane reduction and no atomic.
 //
 // A 16-row tile spans all of K, so a mid-size matrix has few tiles.  With
 // KSPLIT = 4 (16) the four (sixteen) waves of a work-group share each tile,
@@ -43,32 +45,40 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
 
-// Eight biased codes (two dwords, k order) -> eight bf16 in k order.
+// Eight signed codes (two dwords, k order) -> eight bf16 in k order.
 __device__ __forceinline__ bf16x8 widen8(uint32_t lo, uint32_t hi)
 {
     const uint32_t v[2] = {lo, hi};
     u32x4 pr;
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
-        const float f0 = (float)(v[d] & 0xffu);
-        const float f1 = (float)((v[d] >> 8) & 0xffu);
-        const float f2 = (float)((v[d] >> 16) & 0xffu);
-        const float f3 = (float)(v[d] >> 24);
-        // The top half of the fp32 pattern of an integer 0..255 is its bf16.
+        const float f0 = (float)(int8_t)(v[d] & 0xffu);
+        const float f1 = (float)(int8_t)((v[d] >> 8) & 0xffu);
+        const float f2 = (float)(int8_t)((v[d] >> 16) & 0xffu);
+        const float f3 = (float)(int8_t)(v[d] >> 24);
+        // The top half of the fp32 pattern of an integer -128..127 is its bf16.
         pr[2 * d] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
         pr[2 * d + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
     }
     return __builtin_bit_cast(bf16x8, pr);
 }
 
-// Eight Q4 codes (one dword in the matrix-core nibble order, layout.h) ->
-// eight bf16 values 128 + c in k order: the bf16 pattern 0x4300 | c is
-// exactly 128 + c for c = 0..15.
-__device__ __forceinline__ bf16x8 widen_q4(uint32_t u)
+// Eight Q4 codes (one dword, canonical order: byte b holds k = 2b in the
+// low nibble and 2b + 1 in the high nibble) -> eight bf16 values c - z in k
+// order.  zb is z (0..15) in every byte; guarding each byte with bit 7
+// keeps the subtraction from borrowing across bytes, and clearing the guard
+// leaves c - z as a two's-complement byte for the exact widening.
+__device__ __forceinline__ bf16x8 widen_q4(uint32_t u, uint32_t zb)
 {
+    const uint32_t lo = (((u & 0x0F0F0F0Fu) | 0x80808080u) - zb) ^ 0x80808080u;
+    const uint32_t hi = ((((u >> 4) & 0x0F0F0F0Fu) | 0x80808080u) - zb) ^ 0x80808080u;
     u32x4 pr;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) pr[t] = ((u >> (4 * t)) & 0x000F000Fu) | 0x43004300u;
+    for (int b = 0; b < 4; ++b) {
+        const float fe = (float)(int8_t)((lo >> (8 * b)) & 0xffu);
+        const float fo = (float)(int8_t)((hi >> (8 * b)) & 0xffu);
+        pr[b] = __builtin_amdgcn_perm(__float_as_uint(fo), __float_as_uint(fe), 0x07060302u);
+    }
     return __builtin_bit_cast(bf16x8, pr);
 }
 
@@ -86,7 +96,7 @@ __device__ __forceinline__ int xs_chunk(int i, int c, int chunks_per_row)
 }
 
 struct MmaItem {
-    u32x4 c;        // 16 biased 8-bit codes, or 32 Q4 codes (one dword per 32-group)
+    u32x4 c;        // 16 signed 8-bit codes, or 32 Q4 codes (one dword per 32-group)
     uint32_t s;     // fp16 scale (low half) or fp32 row scale bits (8-bit formats)
     u32x4 m4;       // Q4G32: scale | min << 16 of the row's four groups
     u32x4 a0, a1;   // the step's A fragments, when x is read from memory (XG)
@@ -259,13 +269,13 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
     const u32x4 ones4 = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
     const bf16x8 ones = __builtin_bit_cast(bf16x8, ones4);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    f32x4 D = acc, X = acc;
+    f32x4 D = acc;
     int64_t tile = gw, j = j_lo;
 
     auto consume = [&](const MmaItem& it) {
         if constexpr (Q4) {
-            // One MFMA per 32-group: D = sum x (c + 128), X = sum x, then
-            // acc += s (D - 128 X) + min X.
+            // Per 32-group: D = sum x (c - z) and X = sum x (one MFMA each),
+            // then acc += s D + m' X.
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int c = int(j) * 16 + 4 * g + qs;
@@ -273,14 +283,18 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
                 if constexpr (XG) au = g == 0 ? it.a0 : g == 1 ? it.a1 : g == 2 ? it.a2 : it.a3;
                 else au = row_live ? xs[xs_chunk(rho, c, cpr)] : zero4;
                 const bf16x8 a = __builtin_bit_cast(bf16x8, au);
-                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                const f32x4 Dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, widen_q4(it.c[g]), z, 0, 0, 0);
-                const f32x4 Xg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones, z, 0, 0, 0);
                 const float s = half_bits(it.m4[g]);
                 const float mn = half_bits(it.m4[g] >> 16);
+                const float t = -mn * __builtin_amdgcn_rcpf(s);
+                // z = clamp(rint(-min / scale), 0, 15); a NaN ratio gives 0.
+                const float z = t >= 0.5f ? (t < 15.0f ? rintf(t) : 15.0f) : 0.0f;
+                const float mp = fmaf(s, z, mn);
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 Dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    a, widen_q4(it.c[g], __builtin_amdgcn_perm(0u, uint32_t(z), 0u)), zero, 0, 0, 0);
+                const f32x4 Xg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones, zero, 0, 0, 0);
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    acc[v] = fmaf(mn, Xg[v], fmaf(s, fmaf(-128.0f, Xg[v], Dg[v]), acc[v]));
+                for (int v = 0; v < 4; ++v) acc[v] = fmaf(mp, Xg[v], fmaf(s, Dg[v], acc[v]));
             }
         } else {
             const int c0 = int(j) * 8 + 2 * qs;
@@ -296,18 +310,13 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
             const bf16x8 a1 = __builtin_bit_cast(bf16x8, a1u);
             const bf16x8 b0 = widen8(it.c.x, it.c.y);
             const bf16x8 b1 = widen8(it.c.z, it.c.w);
-            if (j % SPG == 0) {
-                D = f32x4{0.f, 0.f, 0.f, 0.f};
-                X = D;
-            }
+            if (j % SPG == 0) D = f32x4{0.f, 0.f, 0.f, 0.f};
             D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, D, 0, 0, 0);
             D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, D, 0, 0, 0);
-            X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, ones, X, 0, 0, 0);
-            X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ones, X, 0, 0, 0);
             if (j % SPG == SPG - 1) {
                 const float s = FMT == FMT_Q8PC ? __uint_as_float(it.s) : half_bits(it.s);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[v] = fmaf(s, fmaf(-128.0f, X[v], D[v]), acc[v]);
+                for (int v = 0; v < 4; ++v) acc[v] = fmaf(s, D[v], acc[v]);
             }
         }
         if (++j == j_hi) {

@@ -11,17 +11,35 @@
 //  * Every lane streams 16-byte units with one global load each; a
 //    wave-wide load is one contiguous 1 KiB block of the packed buffer
 //    (layout.h), read exactly once per call.
-//  * The activation rows are staged once per work-group in LDS together
-//    with fp32 sums of x over each 16/32-element unit.
-//  * Codes become bf16 pairs in registers without a float conversion per
-//    nibble: a 4-bit code c OR-ed into the bf16 pattern 0x4300 is the
-//    number 128 + c, and an int8 code q is stored biased as u = q + 128 and
-//    widened with the byte-to-float conversion.  A v_dot2 bf16 chain then
-//    forms D = sum (c + 128) x over the unit, and the bias comes back out
-//    exactly as D - 128 * X with X = sum x over the unit, accumulated with
-//    the same v_dot2 chain so that an all-zero unit gives exactly zero.
-//  * Per unit:  Q8  acc += s * (D - 128 X)
-//               Q4  acc += s * (D - 128 X) + min * X
+//  * The activation rows are staged once per work-group in LDS, for Q4G32
+//    together with two fp32 sums per 32-wide group: X = sum x and
+//    XA = sum |x|.
+//  * Every output must be within 2e-3 * sum |w x| of the exact sum, for any
+//    inputs (rows of zero weights must give zero, a row whose only nonzero
+//    weight meets a 1e-5 activation must give that one product).
+//      Q8   the signed code q is widened straight from its byte (one
+//           sign-extending byte-to-float conversion; every int8 is exact in
+//           bf16), and v_dot2 bf16 chains form D = sum q x over the 16-code
+//           unit:  acc += s * D.  No bias enters D, so the rounding error is
+//           a few fp32 ulps of sum |w x| by the usual summation bound.
+//      Q4   the fast path turns each nibble pair into the bf16 pair
+//           (128 + c0, 128 + c1) with one and-or (0x4300 | c is 128 + c), so
+//           v_dot2 chains give D = sum (128 + c) x and, per group,
+//             y_g = s (D - 128 X) + min X.
+//           The bias makes the rounding error scale with 128 s XA rather
+//           than with sum |w x|, so every tile carries a certificate: per
+//           row, A = sum |y_g| (a lower bound of sum |w x| up to the error)
+//           and E = sum (|s| + |min| / 256) XA, from which a proven error
+//           bound kappa E follows (see kQ4Kappa).  When kappa E <= T A for
+//           every row of the tile (T is the bar less the accumulation
+//           error), the fast sums meet the bar; otherwise the wave streams
+//           the tile again and recomputes it exactly: each group re-centred
+//           on the integer z nearest its zero point (clamped to 0..15), the
+//           differences c - z widened exactly, and
+//             y_g = s * sum (c - z) x + (min + s z) X,
+//           where |s (c - z)| <= 2 |w| and |min + s z| <= |w| for every
+//           weight of the group, so neither term can cancel.  Ordinary data
+//           never needs the second pass; zero or near-cancelling groups do.
 //  * G lanes share a row; their partial sums meet in a butterfly across
 //    the lane group at the end of the tile.  No atomics: the result is the
 //    same bits on every run.
@@ -42,7 +60,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // (1.0, 1.0)
-constexpr uint32_t kMagicBf16x2 = 0x43004300u;  // (128.0, 128.0)
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
 {
@@ -94,35 +111,37 @@ template <> struct Meta<16> {
     }
 };
 
-// 16 biased int8 codes -> 8 bf16 pairs, in x order (codes 2t, 2t+1 -> pair t).
+// 16 signed int8 codes -> 8 bf16 pairs, in x order (codes 2t, 2t+1 -> pair
+// t).  (float)(int8_t) of a byte is one sign-extending byte-to-float
+// conversion on gfx950 (v_cvt_f32_i32 with a sign-extended byte select).
 __device__ __forceinline__ void q8_pairs(const u32x4& c, uint32_t (&pr)[8])
 {
     const uint32_t v[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        const float f0 = (float)(v[d] & 0xffu);
-        const float f1 = (float)((v[d] >> 8) & 0xffu);
-        const float f2 = (float)((v[d] >> 16) & 0xffu);
-        const float f3 = (float)(v[d] >> 24);
-        // An integer 0..255 has at most 8 significant bits, so the top half
-        // of its fp32 pattern is exactly its bf16 pattern.
+        const float f0 = (float)(int8_t)(v[d] & 0xffu);
+        const float f1 = (float)(int8_t)((v[d] >> 8) & 0xffu);
+        const float f2 = (float)(int8_t)((v[d] >> 16) & 0xffu);
+        const float f3 = (float)(int8_t)(v[d] >> 24);
+        // An integer in [-128, 127] has at most 8 significant bits, so the
+        // top half of its fp32 pattern is exactly its bf16 pattern.
         pr[2 * d] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
         pr[2 * d + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
     }
 }
 
-// The two constants of the 4-bit decode, held in registers for the whole
-// kernel: the nibble-pair mask in a scalar register and the bf16 magic in a
-// vector register.  gfx9 VOP3 encodings take no literal constants, so with
-// both written as literals the compiler splits every (v & mask) | magic into
-// a v_and_b32 and a v_or_b32 (two VOP2 ops with literals); with the mask in
-// an SGPR and the magic in a VGPR it is one v_and_or_b32 (one SGPR operand
-// stays within the single constant-bus read).  Both values come out of asm so
-// the compiler can neither fold them back into literals nor rematerialise
-// them before each use.
+// The two constants of the 4-bit fast decode, held in registers for the
+// whole kernel: the nibble-pair mask in a scalar register and the bf16 magic
+// in a vector register.  gfx9 VOP3 encodings take no literal constants, so
+// with both written as literals the compiler splits every (v & mask) | magic
+// into a v_and_b32 and a v_or_b32 (two VOP2 ops with literals); with the
+// mask in an SGPR and the magic in a VGPR it is one v_and_or_b32 (one SGPR
+// operand stays within the single constant-bus read).  Both values come out
+// of asm so the compiler can neither fold them back into literals nor
+// rematerialise them before each use.
 struct Q4Consts {
     uint32_t mask;    // 0x000F000F, SGPR
-    uint32_t magic;   // kMagicBf16x2, VGPR
+    uint32_t magic;   // 0x43004300 = bf16 (128, 128), VGPR
     __device__ __forceinline__ static Q4Consts make()
     {
         Q4Consts k;
@@ -139,9 +158,11 @@ __device__ __forceinline__ uint32_t and_or(uint32_t v, const Q4Consts& k)
     return r;
 }
 
-// 32 reordered 4-bit codes -> 16 bf16 pairs (128 + c), in x order: pair p of
-// a dword is ((v >> 4p) & 0x000F000F) | 0x43004300, seven VALU ops per dword.
-__device__ __forceinline__ void q4_pairs(const u32x4& c, const Q4Consts& k, uint32_t (&pr)[16])
+// Fast decode: 32 reordered 4-bit codes (layout.h: dword d holds k = 8d + 2p
+// in bits 4p..4p+3 and k = 8d + 2p + 1 in bits 16+4p..19+4p) -> 16 bf16
+// pairs (128 + c), in x order: pair p of a dword is
+// ((v >> 4p) & 0x000F000F) | 0x43004300, seven VALU ops per dword.
+__device__ __forceinline__ void q4_pairs_biased(const u32x4& c, const Q4Consts& k, uint32_t (&pr)[16])
 {
     const uint32_t v[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
@@ -151,15 +172,73 @@ __device__ __forceinline__ void q4_pairs(const u32x4& c, const Q4Consts& k, uint
     }
 }
 
-// x rows -> LDS as bf16 pairs, with X[i][u] = sum of x over unit u formed by
-// the same v_dot2 chain (in the same order) the hot loop uses for D.  Thread
-// t handles units t, t + 256, ... of the flattened [M][U] array.  Its first
-// unit is fetched before anything else the kernel loads (XStage::fetch), so
-// that waiting for it does not also wait for the weight stream: vector
-// memory loads complete in issue order.
+// Zero point of a Q4 group from its meta word (scale in the low half, min
+// in the high half, fp16): z = clamp(rint(-min / scale), 0, 15) (0 when
+// that is not a number, e.g. scale = min = 0) and m' = min + scale z in one
+// rounding.  An approximate reciprocal is enough: the re-centring argument
+// only needs |z + min / scale| <= 1/2 up to a few ulps.
+struct Q4Group {
+    float s, mp;
+    int z;
+};
+
+__device__ __forceinline__ Q4Group q4_group(uint32_t meta)
+{
+    Q4Group g;
+    g.s = half_lo(meta);
+    const float mn = half_hi(meta);
+    const float t = -mn * __builtin_amdgcn_rcpf(g.s);
+    // Comparisons with NaN are false, so a NaN ratio gives z = 0.
+    const float z = t >= 0.5f ? (t < 15.0f ? rintf(t) : 15.0f) : 0.0f;
+    g.mp = fmaf(g.s, z, mn);
+    g.z = int(z);
+    return g;
+}
+
+// Exact decode (the certificate's fallback): the same reordered codes ->
+// 16 bf16 pairs (c - z), in x order.  Integers -15..15 are exact in bf16.
+__device__ __forceinline__ void q4_pairs_centred(const u32x4& c, int z, uint32_t (&pr)[16])
+{
+    const uint32_t v[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const float lo = float(int((v[d] >> (4 * p)) & 0xfu) - z);
+            const float hi = float(int((v[d] >> (16 + 4 * p)) & 0xfu) - z);
+            pr[4 * d + p] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+        }
+    }
+}
+
+// Proven error bound of the Q4 fast path, per group, in units of
+// (|s| + |min| / 256) * XA.  It models each v_dot2 step as erring by at most
+// 3 * 2^-24 of |acc| + |p0| + |p1| (the largest error measured on gfx950
+// over 2^20 random operands was 1.98 * 2^-24 of that sum), and every other
+// fp32 operation as correctly rounded.  D = sum (128 + c) x is two chains
+// of eight v_dot2 steps plus one add: at most 25 * 2^-24 * 143 XA.  X is
+// formed the same way: 25 * 2^-24 XA, times 128 in D - 128 X.  The fma
+// D - 128 X adds 2^-24 * 16 XA.  So |c_hat - sum c x| <= 6790 * 2^-24 XA, and
+// y_g = s c + min X errs by at most 6790 * 2^-24 |s| XA + 26 * 2^-24 |min| XA
+// + 2^-24 |y_g|; 26 / 6790 < 1/256 and the last term is counted with the
+// accumulation error on the host side of the threshold.  The constant below
+// is 6810 * 2^-24, which also covers the fp32 rounding of XA and of E.
+constexpr float kQ4Kappa = 6810.0f / 16777216.0f;
+constexpr float kQ4MinWeight = 1.0f / 256.0f;
+
+// x rows -> LDS as bf16 pairs; for Q4G32 also, per unit (group) u of row
+// i, X = sum x and XA = sum |x| at xsum[2 (i U + u)] and xsum[2 (i U + u) + 1].
+// X is formed by two v_dot2 chains over ones (eight pairs each) and an add,
+// exactly as the hot loop forms D, so that an all-zero group gives
+// D - 128 X = 0 exactly.  The 8-bit formats need no sums.  Thread t handles
+// units t, t + 256, ... of the flattened [M][U] array.  Its first unit is
+// fetched before anything else the kernel loads (XStage::fetch), so that
+// waiting for it does not also wait for the weight stream: vector memory
+// loads complete in issue order.
 template <int FMT, int M, int THREADS>
 struct XStage {
     static constexpr int UD = FMT == FMT_Q4G32 ? 16 : 8;   // dwords per unit
+    static constexpr bool kSums = FMT == FMT_Q4G32;
     uint32_t v[UD];
     int first;                                             // flattened unit index
 
@@ -176,9 +255,6 @@ struct XStage {
     __device__ __forceinline__ void store_unit(uint32_t* xs, float* xsum, int idx, int KD, int U)
     {
         const int i = idx / U, u = idx - i * U;
-        float X = 0.0f;
-#pragma unroll
-        for (int d = 0; d < UD; ++d) X = dot2(v[d], kOnesBf16x2, X);
         u32x4* dst = reinterpret_cast<u32x4*>(xs + i * KD + u * UD);
 #pragma unroll
         for (int q = 0; q < UD / 4; ++q) {
@@ -186,7 +262,20 @@ struct XStage {
             t.x = v[4 * q]; t.y = v[4 * q + 1]; t.z = v[4 * q + 2]; t.w = v[4 * q + 3];
             dst[q] = t;
         }
-        xsum[idx] = X;
+        if constexpr (kSums) {
+            float X0 = 0.0f, X1 = 0.0f, A0 = 0.0f, A1 = 0.0f;
+#pragma unroll
+            for (int d = 0; d < UD / 2; ++d) {
+                X0 = dot2(v[d], kOnesBf16x2, X0);
+                X1 = dot2(v[d + UD / 2], kOnesBf16x2, X1);
+                A0 = dot2(v[d] & 0x7fff7fffu, kOnesBf16x2, A0);
+                A1 = dot2(v[d + UD / 2] & 0x7fff7fffu, kOnesBf16x2, A1);
+            }
+            float2 xa;
+            xa.x = X0 + X1;
+            xa.y = A0 + A1;
+            reinterpret_cast<float2*>(xsum)[idx] = xa;
+        }
     }
 
     __device__ __forceinline__ void fetch(const KernelParams& p, const uint16_t* x, int U)
@@ -233,14 +322,30 @@ struct Item {
     }
 };
 
+// The Q4 fast path's per-row certificate sums (see kQ4Kappa): A = sum |y_g|
+// and E = sum (|s| + |min| / 256) XA over the groups a lane has consumed.
+template <int FMT, int M, int R>
+struct Cert {
+    static constexpr bool kOn = FMT == FMT_Q4G32;
+    float A[kOn ? R : 1][kOn ? M : 1];
+    float E[kOn ? R : 1][kOn ? M : 1];
+    __device__ __forceinline__ void clear()
+    {
+#pragma unroll
+        for (int r = 0; r < (kOn ? R : 1); ++r)
+#pragma unroll
+            for (int i = 0; i < (kOn ? M : 1); ++i) A[r][i] = E[r][i] = 0.0f;
+    }
+};
+
 template <int FMT, int M, int R, int META_BYTES>
 __device__ __forceinline__ void consume(const Item<R, META_BYTES>& it, const uint32_t* xs,
                                         const float* xsum, int KD, int U, int u, const Q4Consts& k4,
-                                        float (&acc)[R][M])
+                                        float (&acc)[R][M], Cert<FMT, M, R>& cert)
 {
     constexpr int UD = FMT == FMT_Q4G32 ? 16 : 8;
     uint32_t xd[M][UD];
-    float X[M];
+    float X[M], XA[M];
 #pragma unroll
     for (int i = 0; i < M; ++i) {
         const u32x4* src = reinterpret_cast<const u32x4*>(xs + i * KD + u * UD);
@@ -250,11 +355,17 @@ __device__ __forceinline__ void consume(const Item<R, META_BYTES>& it, const uin
             xd[i][4 * q] = v.x; xd[i][4 * q + 1] = v.y;
             xd[i][4 * q + 2] = v.z; xd[i][4 * q + 3] = v.w;
         }
-        X[i] = xsum[i * U + u];
+        if constexpr (FMT == FMT_Q4G32) {
+            const float2 xa = reinterpret_cast<const float2*>(xsum)[i * U + u];
+            X[i] = xa.x;
+            XA[i] = xa.y;
+        } else {
+            X[i] = XA[i] = 0.0f;
+        }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        if (FMT != FMT_Q4G32) {
+        if constexpr (FMT != FMT_Q4G32) {
             // Q8G64/Q8G128: fp16 scale of the unit's group; Q8PC: fp32 row scale.
             float s;
             if constexpr (FMT == FMT_Q8PC) s = __uint_as_float(it.m.w[r]);
@@ -266,23 +377,66 @@ __device__ __forceinline__ void consume(const Item<R, META_BYTES>& it, const uin
                 float D = 0.0f;
 #pragma unroll
                 for (int t = 0; t < 8; ++t) D = dot2(pr[t], xd[i][t], D);
-                const float c = fmaf(-128.0f, X[i], D);
-                acc[r][i] = fmaf(s, c, acc[r][i]);
+                acc[r][i] = fmaf(s, D, acc[r][i]);
             }
         } else {
             const float s = half_lo(it.m.w[r]);
             const float mn = half_hi(it.m.w[r]);
+            const float we = fmaf(fabsf(mn), kQ4MinWeight, fabsf(s));
             uint32_t pr[16];
-            q4_pairs(it.c[r], k4, pr);
+            q4_pairs_biased(it.c[r], k4, pr);
 #pragma unroll
             for (int i = 0; i < M; ++i) {
-                float D = 0.0f;
+                // Two chains of eight pairs (the certificate's bound assumes
+                // this shape, and so does the X sum staged with x).
+                float D0 = 0.0f, D1 = 0.0f;
 #pragma unroll
-                for (int t = 0; t < 16; ++t) D = dot2(pr[t], xd[i][t], D);
-                const float c = fmaf(-128.0f, X[i], D);
-                acc[r][i] = fmaf(s, c, acc[r][i]);
-                acc[r][i] = fmaf(mn, X[i], acc[r][i]);
+                for (int t = 0; t < 8; ++t) {
+                    D0 = dot2(pr[t], xd[i][t], D0);
+                    D1 = dot2(pr[t + 8], xd[i][t + 8], D1);
+                }
+                const float c = fmaf(-128.0f, X[i], D0 + D1);
+                const float yg = fmaf(s, c, mn * X[i]);
+                acc[r][i] += yg;
+                cert.A[r][i] += fabsf(yg);
+                cert.E[r][i] = fmaf(we, XA[i], cert.E[r][i]);
             }
+        }
+    }
+}
+
+// The certificate's fallback: one item of a Q4 tile, decoded exactly (each
+// group re-centred on its integer zero point z, see q4_group).
+template <int M, int R, int META_BYTES>
+__device__ __forceinline__ void consume_centred(const Item<R, META_BYTES>& it, const uint32_t* xs,
+                                                const float* xsum, int KD, int U, int u,
+                                                float (&acc)[R][M])
+{
+    uint32_t xd[M][16];
+    float X[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(xs + i * KD + u * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 v = src[q];
+            xd[i][4 * q] = v.x; xd[i][4 * q + 1] = v.y;
+            xd[i][4 * q + 2] = v.z; xd[i][4 * q + 3] = v.w;
+        }
+        X[i] = reinterpret_cast<const float2*>(xsum)[i * U + u].x;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const Q4Group q = q4_group(it.m.w[r]);
+        uint32_t pr[16];
+        q4_pairs_centred(it.c[r], q.z, pr);
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            float D = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) D = dot2(pr[t], xd[i][t], D);
+            acc[r][i] = fmaf(q.s, D, acc[r][i]);
+            acc[r][i] = fmaf(q.mp, X[i], acc[r][i]);
         }
     }
 }
@@ -419,6 +573,45 @@ __device__ __forceinline__ void finish_tile(float (&acc)[R][M], const KernelPara
         const int r = o / M, i = o - (o / M) * M;
         const int64_t row = tile * TR + r * RPS + rho;
         if (holder && row < p.N) y[int64_t(i) * p.ldy + row] = ts.v[k];
+    }
+}
+
+// End of a Q4 tile: reduces the certificate sums of every row the tile
+// holds and reports whether each row's fast sums are proven to meet the bar
+// (kQ4Kappa * E <= T * A; false for NaN).  The answer is the same in every
+// lane of the wave (a ballot), so the caller branches uniformly.
+template <int M, int G, int R>
+__device__ __forceinline__ bool q4_tile_certified(Cert<FMT_Q4G32, M, R>& cert, float T, int g)
+{
+    using TS = TileSums<M, G, R>;
+    TS ta, te;
+    reduce_tile<M, G, R>(cert.A, ta);
+    reduce_tile<M, G, R>(cert.E, te);
+    bool bad = false;
+    if (TS::holder(g)) {
+#pragma unroll
+        for (int k = 0; k < TS::V2; ++k) bad = bad || !(kQ4Kappa * te.v[k] <= T * ta.v[k]);
+    }
+    return __builtin_amdgcn_ballot_w64(bad) == 0;
+}
+
+// The certificate's fallback: the tile's J items are streamed again, one at
+// a time, and its sums recomputed exactly (consume_centred).  Items are
+// addressed as in the main stream, so every load stays inside the matrix.
+template <int M, int G, int R, int META_BYTES>
+__device__ __forceinline__ void q4_recompute_tile(float (&acc)[R][M], const KernelParams& p,
+                                                  const uint8_t* code_lane, const uint8_t* meta_lane,
+                                                  int64_t tile, const uint32_t* xs, const float* xsum,
+                                                  int KD, int U, int g)
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < M; ++i) acc[r][i] = 0.0f;
+    for (int64_t jj = 0; jj < p.J; ++jj) {
+        Item<R, META_BYTES> it;
+        it.load(code_lane, meta_lane, tile * p.J + jj, tile, p);
+        consume_centred<M, R, META_BYTES>(it, xs, xsum, KD, U, int(jj) * G + g, acc);
     }
 }
 
@@ -598,7 +791,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     const int KD = p.K >> 1;
     const int U = p.K / (FMT == FMT_Q4G32 ? 32 : 16);
     uint32_t* xs = lds;
-    float* xsum = reinterpret_cast<float*>(lds + M * KD);
+    float* xsum = reinterpret_cast<float*>(lds + M * KD);   // Q4G32 only
 
     const int slot = GROUPED ? int(blockIdx.y) : 0;
     const int64_t W = int64_t(gridDim.x) * kWaves;
@@ -716,16 +909,23 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     Q4Consts k4 = {0u, 0u};
     if constexpr (FMT == FMT_Q4G32) k4 = Q4Consts::make();
     SwigluBatch<G, R> swb;   // EPI 1 only
+    Cert<FMT, M, R> cert;    // Q4G32 only
+    cert.clear();
 
     // Consume cursor.
     int64_t tile = t0, j = 0;
 #define QG_CONSUME(slot_)                                                                     \
     do {                                                                                      \
-        consume<FMT, M, R, META_BYTES>(ring[slot_], xs, xsum, KD, U, int(j) * G + g, k4, acc); \
+        consume<FMT, M, R, META_BYTES>(ring[slot_], xs, xsum, KD, U, int(j) * G + g, k4, acc, cert); \
     } while (0)
 #define QG_ADVANCE()                                                                          \
     do {                                                                                      \
         if (++j == p.J) {                                                                     \
+            if constexpr (FMT == FMT_Q4G32) {                                                 \
+                if (__builtin_expect(!q4_tile_certified<M, G, R>(cert, p.cert_t, g), 0))      \
+                    q4_recompute_tile<M, G, R, META_BYTES>(acc, p, code_lane, meta_lane, tile, xs, \
+                                                           xsum, KD, U, g);                   \
+            }                                                                                 \
             if constexpr (EPI == 1) {                                                         \
                 swb.add(acc, tile, lane);                                                     \
                 if (swb.full()) swb.flush(p, act, tstep, lane, rho);                          \

@@ -41,7 +41,22 @@ struct KernelParams {
     int32_t* idx_out;          // argmax epilogue: chosen index per activation row
     unsigned long long* keys;  // argmax epilogue: one key per row (zero between calls)
     unsigned int* counter;     // argmax epilogue: finished work-groups (zero between calls)
+    float cert_t;              // Q4G32: certificate threshold T (q4_cert_threshold)
 };
+
+// Threshold T of the Q4G32 fast path's certificate (kernel_body.h,
+// kQ4Kappa): a row's fast sum is accepted when kappa * E <= T * A.  The
+// bar is |y - y_exact| <= 2e-3 * sum |w x|; sum |w x| >= A - (fast error),
+// and adding the J per-lane partial sums and the log2(64) reduction levels
+// costs at most (J + 7) * 2^-24 * A more (the same for forming A itself).
+// So kappa E + (J + 7) u A <= 2e-3 (A (1 - (J + 7) u) - kappa E) is enough,
+// which holds when kappa E <= A (2e-3 - 2.01 (J + 7) u) / 1.002; 1e-6 is
+// taken off for the fp32 evaluation of the comparison.
+inline float q4_cert_threshold(int64_t J)
+{
+    const double u = 1.0 / 16777216.0;
+    return float((2e-3 - 2.01 * double(J + 7) * u) / 1.002 - 1e-6);
+}
 
 // Launch shape: ring depth 2 or 4 items; work-groups are 4 waves.
 enum Shape { SHAPE_D2_W4 = 0, SHAPE_D4_W4 = 1 };

@@ -53,7 +53,10 @@ static int64_t compute_units()
 
 size_t lds_bytes_for(const Layout& L, int m)
 {
-    return size_t(m) * size_t(L.K / 2 + L.U) * 4;
+    // The bf16 rows of x, plus two fp32 activation sums (sum x, sum |x|)
+    // per 32-group for Q4G32 (the 8-bit formats need none).
+    const int64_t sums = L.fmt == FMT_Q4G32 ? 2 * L.U : 0;
+    return size_t(m) * size_t(L.K / 2 + sums) * 4;
 }
 
 hipError_t launch(const LaunchArgs& a)
@@ -83,6 +86,7 @@ hipError_t launch(const LaunchArgs& a)
     kp.idx_out = a.idx_out;
     kp.keys = static_cast<unsigned long long*>(a.argmax_workspace);
     kp.counter = a.argmax_workspace ? reinterpret_cast<unsigned int*>(kp.keys + a.m) : nullptr;
+    kp.cert_t = q4_cert_threshold(L.J);
     const int slots = a.grouped ? a.n_slots : 1;
     // About target_waves waves in total (QG_TARGET_WAVES overrides it, for
     // tuning sweeps), never more waves than tiles; k tiles per wave, then the

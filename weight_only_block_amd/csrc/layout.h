@@ -3,10 +3,12 @@
 // qpack_*_size() and an opaque buffer.
 //
 // A 16-byte "unit" is what one lane loads with one 16-byte global load:
-//   Q8G64, Q8G128, Q8PC: 16 consecutive int8 codes of one row, stored biased
-//          as q+128 (4 units make a 64-wide group, 8 a 128-wide group)
+//   Q8G64, Q8G128, Q8PC: 16 consecutive signed int8 codes of one row, as
+//          they are (4 units make a 64-wide group, 8 a 128-wide group)
 //   Q4G32: the 32 codes of one 32-wide group of one row, nibbles reordered
 //          so that each 16-bit half of a dword pairs with one bf16 pair of x
+//          (dword d holds k = 8d .. 8d + 7: k = 8d + 2p in bits 4p .. 4p + 3,
+//          k = 8d + 2p + 1 in bits 16 + 4p .. 19 + 4p)
 // A row has U = K/16 (8-bit codes) or K/32 (Q4) units.  G lanes share a row
 // (G is a power of two dividing U, at least the units per scale group), so
 // one 64-lane load covers 64/G rows.  A tile is R such row slots,
@@ -23,8 +25,7 @@
 //     Q4G32:  for each lane l: R dwords (scale | min << 16), one per r
 //     Q8PC:   no per-step meta; after a tile's steps, its TR fp32 row scales
 //             ordered [rho][r], so lane l's R scales are contiguous
-// Rows past N in the last tile are padding: zero scales and min, code bytes
-// that decode to zero.  Every weight byte is stored exactly once; the
+// Rows past N in the last tile are padding: zero codes, scales and mins.  Every weight byte is stored exactly once; the
 // padding is at most TR-1 rows.
 #pragma once
 #include <stdint.h>
@@ -122,7 +123,7 @@ static inline bool make_gate_up_layout(int64_t N, int64_t K, Layout* L, int64_t*
 // feeds the 16x16x32 bf16 MFMA (m = 1..16 activation rows share the B-side
 // weights).  A tile is 16 rows; a step covers 64 consecutive K.  Item
 // (tile t, step j) is one 1 KiB block at (t*J + j)*1024 in which lane l
-// holds the 16 biased codes (q + 128) of row t*16 + (l mod 16) at
+// holds the 16 signed codes of row t*16 + (l mod 16) at
 // k = 64j + 16*(l div 16) .. +15: the MFMA's B operand (lane l supplies
 // column l mod 16, k-slice l div 16) with no shuffling.  Meta after all
 // code blocks:
@@ -130,15 +131,14 @@ static inline bool make_gate_up_layout(int64_t N, int64_t K, Layout* L, int64_t*
 //   Q8G128: [tile][128-group][16 rows] fp16 scales
 //   Q8PC:   [tile][16 rows] fp32 row scales
 // K must be a multiple of 64 (128 for Q8G128).  Rows past N are padding
-// (code 0x80, scale 0).  Every weight byte is stored once.
+// (code 0, scale 0).  Every weight byte is stored once.
 //
 // Q4G32 uses the same tiles with 128-wide steps, so that an item is still
 // 1 KiB: lane l holds four dwords, dword g being the eight codes of row
-// t*16 + (l mod 16) at k = 128j + 32g + 8*(l div 16) + e (e = 0..7), one
-// nibble each, in the nibble order e = 0, 2, 4, 6, 1, 3, 5, 7.  Masking
-// the dword (and its shifts by 4, 8, 12) with 0x000F000F then yields the
-// bf16 pairs (e0, e1), (e2, e3), (e4, e5), (e6, e7): the B operand of one
-// MFMA, which thus covers exactly one 32-group.  Meta after all code
+// t*16 + (l mod 16) at k = 128j + 32g + 8*(l div 16) + e (e = 0..7) as
+// their four canonical bytes (e = 2b in the low nibble of byte b, 2b + 1 in
+// the high nibble): the B operand of one MFMA (in k order once widened),
+// which thus covers exactly one 32-group.  Meta after all code
 // blocks: [tile][step][16 rows][4 groups] dwords, scale (fp16) in the low
 // half and min (fp16) in the high half.  K must be a multiple of 128.
 // Rows past N are padding (code 0, scale 0, min 0).

@@ -86,7 +86,7 @@ inline int64_t meta_off_pc(const qg::Layout& L, int64_t t, int r, int rho)
     return meta_base(L, t, L.J) + (int64_t(rho) * L.R + r) * 4;
 }
 
-// Packs any 8-bit-code format: codes biased to q+128, then the format's scales.
+// Packs any 8-bit-code format: the signed codes as they are, then the format's scales.
 // scales: fp16 [N][K/group] for the grouped formats, fp32 bit patterns [N] for Q8PC.
 qg_status pack_q8(int fmt, const int8_t* q, const void* scales, int64_t N, int64_t K, void* out,
                   size_t out_bytes)
@@ -96,9 +96,8 @@ qg_status pack_q8(int fmt, const int8_t* q, const void* scales, int64_t N, int64
     if (!qg::make_layout(fmt, N, K, &L)) return QG_ERR_INVALID_ARG;
     if (out_bytes < size_t(L.total_bytes)) return QG_ERR_INVALID_ARG;
     uint8_t* o = static_cast<uint8_t*>(out);
-    // Padding rows: code byte 0x80 (q = 0 after the +128 bias), scale 0.
-    memset(o, 0x80, size_t(L.code_bytes));
-    memset(o + L.code_bytes, 0, size_t(L.total_bytes - L.code_bytes));
+    // Padding rows: code 0, scale 0.
+    memset(o, 0, size_t(L.total_bytes));
     const int lanes_per_group = fmt == qg::FMT_Q8G128 ? 8 : 4;
     const int64_t groups = K / L.group;
     const uint16_t* s16 = static_cast<const uint16_t*>(scales);
@@ -113,7 +112,7 @@ qg_status pack_q8(int fmt, const int8_t* q, const void* scales, int64_t N, int64
                     const int64_t u = j * L.G + g;
                     const int8_t* src = q + n * K + u * 16;
                     uint8_t* dst = o + code_off(L, t, j, r, lane);
-                    for (int b = 0; b < 16; ++b) dst[b] = uint8_t(int(src[b]) + 128);
+                    memcpy(dst, src, 16);
                     if (fmt == qg::FMT_Q8PC) {
                         if (j == 0 && g == 0) memcpy(o + meta_off_pc(L, t, r, rho), &s32[n], 4);
                     } else if (g % lanes_per_group == 0) {
@@ -146,7 +145,7 @@ qg_status unpack_q8(int fmt, const void* packed, size_t packed_bytes, int64_t N,
                     if (n >= N) continue;
                     const int64_t u = j * L.G + g;
                     const uint8_t* src = p + code_off(L, t, j, r, lane);
-                    for (int b = 0; b < 16; ++b) q[n * K + u * 16 + b] = int8_t(int(src[b]) - 128);
+                    memcpy(q + n * K + u * 16, src, 16);
                     if (fmt == qg::FMT_Q8PC) {
                         if (j == 0 && g == 0) memcpy(&s32[n], p + meta_off_pc(L, t, r, rho), 4);
                     } else if (g % lanes_per_group == 0) {
@@ -235,8 +234,7 @@ qg_status pack_q8_mma(int fmt, const int8_t* q, const void* scales, int64_t N, i
     if (!qg::make_mma_layout(fmt, N, K, &L)) return QG_ERR_INVALID_ARG;
     if (out_bytes < size_t(L.total_bytes)) return QG_ERR_INVALID_ARG;
     uint8_t* o = static_cast<uint8_t*>(out);
-    memset(o, 0x80, size_t(L.code_bytes));
-    memset(o + L.code_bytes, 0, size_t(L.total_bytes - L.code_bytes));
+    memset(o, 0, size_t(L.total_bytes));   // padding rows: code 0, scale 0
     const uint16_t* s16 = static_cast<const uint16_t*>(scales);
     const uint32_t* s32 = static_cast<const uint32_t*>(scales);
     for (int64_t t = 0; t < L.tiles; ++t)
@@ -248,7 +246,7 @@ qg_status pack_q8_mma(int fmt, const int8_t* q, const void* scales, int64_t N, i
                     const int lane = qs * 16 + rho;
                     const int8_t* src = q + n * K + 64 * j + 16 * qs;
                     uint8_t* dst = o + (t * L.J + j) * 1024 + lane * 16;
-                    for (int b = 0; b < 16; ++b) dst[b] = uint8_t(int(src[b]) + 128);
+                    memcpy(dst, src, 16);
                 }
             uint8_t* meta = o + L.code_bytes + t * L.meta_tile_bytes;
             if (fmt == qg::FMT_Q8PC) {
@@ -278,7 +276,7 @@ qg_status unpack_q8_mma(int fmt, const void* packed, size_t packed_bytes, int64_
             for (int64_t j = 0; j < L.J; ++j)
                 for (int qs = 0; qs < 4; ++qs) {
                     const uint8_t* src = p + (t * L.J + j) * 1024 + (qs * 16 + rho) * 16;
-                    for (int b = 0; b < 16; ++b) q[n * K + 64 * j + 16 * qs + b] = int8_t(int(src[b]) - 128);
+                    memcpy(q + n * K + 64 * j + 16 * qs, src, 16);
                 }
             const uint8_t* meta = p + L.code_bytes + t * L.meta_tile_bytes;
             if (fmt == qg::FMT_Q8PC) {
@@ -292,9 +290,9 @@ qg_status unpack_q8_mma(int fmt, const void* packed, size_t packed_bytes, int64_
 }
 
 // Q4G32 in the matrix-core layout (layout.h): codes [N][K/2] canonical
-// (even k in the low nibble), scale and min fp16 [N][K/32].
-constexpr int kQ4MmaNibble[8] = {0, 4, 1, 5, 2, 6, 3, 7};   // position of e in the dword
-
+// (even k in the low nibble), scale and min fp16 [N][K/32].  Dword g of
+// lane (qs, rho) is the four canonical bytes of row rho's codes at
+// k = 128 j + 32 g + 8 qs .. + 7.
 qg_status pack_q4_mma(const uint8_t* codes, const uint16_t* scale, const uint16_t* minv, int64_t N,
                       int64_t K, void* out, size_t out_bytes)
 {
@@ -312,15 +310,8 @@ qg_status pack_q4_mma(const uint8_t* codes, const uint16_t* scale, const uint16_
             for (int64_t j = 0; j < L.J; ++j) {
                 for (int qs = 0; qs < 4; ++qs) {
                     uint8_t* dst = o + (t * L.J + j) * 1024 + (qs * 16 + rho) * 16;
-                    for (int g = 0; g < 4; ++g) {
-                        uint32_t word = 0;
-                        for (int e = 0; e < 8; ++e) {
-                            const int64_t k = 128 * j + 32 * g + 8 * qs + e;
-                            const uint32_t c = (codes[n * (K / 2) + k / 2] >> (4 * (k & 1))) & 0xFu;
-                            word |= c << (4 * kQ4MmaNibble[e]);
-                        }
-                        memcpy(dst + 4 * g, &word, 4);
-                    }
+                    for (int g = 0; g < 4; ++g)
+                        memcpy(dst + 4 * g, codes + n * (K / 2) + (128 * j + 32 * g + 8 * qs) / 2, 4);
                 }
                 uint8_t* meta = o + L.code_bytes + t * L.meta_tile_bytes + (j * qg::kMmaRows + rho) * 16;
                 for (int g = 0; g < 4; ++g) {
@@ -342,7 +333,6 @@ qg_status unpack_q4_mma(const void* packed, size_t packed_bytes, int64_t N, int6
     if (packed_bytes < size_t(L.total_bytes)) return QG_ERR_INVALID_ARG;
     const uint8_t* p = static_cast<const uint8_t*>(packed);
     const int64_t G = K / 32;
-    memset(codes, 0, size_t(N * (K / 2)));
     for (int64_t t = 0; t < L.tiles; ++t)
         for (int rho = 0; rho < qg::kMmaRows; ++rho) {
             const int64_t n = t * qg::kMmaRows + rho;
@@ -350,15 +340,8 @@ qg_status unpack_q4_mma(const void* packed, size_t packed_bytes, int64_t N, int6
             for (int64_t j = 0; j < L.J; ++j) {
                 for (int qs = 0; qs < 4; ++qs) {
                     const uint8_t* src = p + (t * L.J + j) * 1024 + (qs * 16 + rho) * 16;
-                    for (int g = 0; g < 4; ++g) {
-                        uint32_t word;
-                        memcpy(&word, src + 4 * g, 4);
-                        for (int e = 0; e < 8; ++e) {
-                            const int64_t k = 128 * j + 32 * g + 8 * qs + e;
-                            const uint8_t c = uint8_t((word >> (4 * kQ4MmaNibble[e])) & 0xFu);
-                            codes[n * (K / 2) + k / 2] |= uint8_t(c << (4 * (k & 1)));
-                        }
-                    }
+                    for (int g = 0; g < 4; ++g)
+                        memcpy(codes + n * (K / 2) + (128 * j + 32 * g + 8 * qs) / 2, src + 4 * g, 4);
                 }
                 const uint8_t* meta = p + L.code_bytes + t * L.meta_tile_bytes + (j * qg::kMmaRows + rho) * 16;
                 for (int g = 0; g < 4; ++g) {
