@@ -301,6 +301,22 @@ qg_status qgemv_q8g128_argmax(const void *w_packed, const uint16_t *x_bf16, floa
                               int64_t ldy, void *workspace, size_t workspace_bytes,
                               void *hip_stream);
 
+/* Allocation-free LM head with the fused greedy choice, for callers that
+ * cannot allocate or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): qgemv_q8g64_argmax
+ * without the workspace arguments.  The keys and counter live in a small
+ * device array owned by the library (256 bytes per GPU, held until the
+ * process ends); the first call on a device looks up that GPU's copy and
+ * enqueues one small kernel that zeroes it, and every completed call leaves
+ * it zeroed again.  Nothing is allocated or freed.  Calls that overlap in
+ * time on one GPU share the array and race: issue them on one stream (or
+ * otherwise serialize them).  m = 1..4 (the array holds the workspace of at
+ * most 4 rows; QG_ERR_UNSUPPORTED beyond); other arguments, results and
+ * errors as qgemv_q8g64_argmax; QG_ERR_HIP if the array cannot be found. */
+qg_status qgemv_q8g64_argmax_noalloc(const void *w_packed, const uint16_t *x_bf16, float *logits,
+                                     int32_t *idx_out, int64_t m, int64_t N, int64_t K, int64_t ldx,
+                                     int64_t ldy, void *hip_stream);
+
 /* ------------------------------------------------------------- test hooks
  * Every successful qgemv_* call bumps the counter of the kernel variant it
  * launched.  Variant names: "<fmt>[_grouped[_swiglu]|_argmax]_m<m>_g<G>_r<R>"

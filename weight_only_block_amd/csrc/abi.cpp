@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/qgemv.h"
 #include "argmax.h"
@@ -132,22 +133,35 @@ qg_status run_mma(int fmt, int kind, const void* w_packed, const uint16_t* x, fl
     return QG_OK;
 }
 
+// The checks of a dense call (m >= 1) that do not involve the argmax
+// workspace; with idx_out the argmax epilogue (y may then be null).
+qg_status validate_dense(int fmt, const void* w_packed, const uint16_t* x, const float* y,
+                         const int32_t* idx_out, int64_t m, int64_t N, int64_t K, int64_t ldx,
+                         int64_t ldy, qg::Layout* L)
+{
+    const bool argmax = idx_out != nullptr;
+    if (!w_packed || !x || (!y && !argmax)) return QG_ERR_INVALID_ARG;
+    const qg_status st = check_shape(fmt, m, N, K, L);
+    if (st != QG_OK) return st;
+    if (ldx < K || (y && ldy < N)) return QG_ERR_INVALID_ARG;
+    if (!aligned(w_packed, 256) || !aligned(x, 4) || (y && !aligned(y, 4))) return QG_ERR_ALIGNMENT;
+    if (argmax && !aligned(idx_out, 4)) return QG_ERR_ALIGNMENT;
+    if (m > 1 && (ldx % 2) != 0) return QG_ERR_ALIGNMENT;
+    return QG_OK;
+}
+
 qg_status run_dense(int fmt, const void* w_packed, const uint16_t* x, float* y, int64_t m,
                     int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* stream,
                     int32_t* idx_out = nullptr, void* workspace = nullptr, size_t workspace_bytes = 0)
 {
     const bool argmax = idx_out != nullptr;
-    if (!w_packed || !x || (!y && !argmax)) return QG_ERR_INVALID_ARG;
     if (argmax && !workspace) return QG_ERR_INVALID_ARG;
-    if (m == 0) return QG_OK;  // an empty batch: nothing to compute
+    if (m == 0 && w_packed && x && (y || argmax)) return QG_OK;  // an empty batch: nothing to compute
     qg::Layout L;
-    const qg_status st = check_shape(fmt, m, N, K, &L);
+    const qg_status st = validate_dense(fmt, w_packed, x, y, idx_out, m, N, K, ldx, ldy, &L);
     if (st != QG_OK) return st;
-    if (ldx < K || (y && ldy < N)) return QG_ERR_INVALID_ARG;
     if (argmax && workspace_bytes < qg::argmax_workspace_bytes(m)) return QG_ERR_INVALID_ARG;
-    if (!aligned(w_packed, 256) || !aligned(x, 4) || (y && !aligned(y, 4))) return QG_ERR_ALIGNMENT;
-    if (argmax && (!aligned(idx_out, 4) || !aligned(workspace, 8))) return QG_ERR_ALIGNMENT;
-    if (m > 1 && (ldx % 2) != 0) return QG_ERR_ALIGNMENT;
+    if (argmax && !aligned(workspace, 8)) return QG_ERR_ALIGNMENT;
     qg::LaunchArgs a;
     a.layout = L;
     a.grouped = false;
@@ -175,6 +189,52 @@ qg_status run_dense(int fmt, const void* w_packed, const uint16_t* x, float* y, 
     if (qg::launch(a) != hipSuccess) return QG_ERR_HIP;
     const int kind = argmax ? (fmt == qg::FMT_Q8G64 ? 6 : 7) : kind_of(fmt);
     g_route[kind][m - 1][log2i(L.G)].fetch_add(1, std::memory_order_relaxed);
+    return QG_OK;
+}
+
+// --------------------------------------------------------------------------
+// Library-owned argmax scratch, for the allocation-free LM-head call
+// (qgemv_q8g64_argmax_noalloc): the fused argmax's keys and finished-work-
+// group counter (qg::argmax_workspace_bytes(m) <= 48 bytes for m <= 4).
+// One copy per GPU, held until the process ends.  Every completed call
+// leaves the bytes it used at zero (its last work-group clears them), and
+// the first call on a device zeroes the whole array with a fill kernel
+// before anything reads it, so every call starts from zeros.  Calls that
+// overlap in time on one GPU share the array and race.
+constexpr size_t kScratchBytes = 256;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ void scratch_zero(unsigned char* p, size_t n)
+{
+    for (size_t i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+
+// Device address of this GPU's `scratch` (the host-side name is only a
+// stand-in for it), looked up once per device with that device current; the
+// first lookup also enqueues the zero fill on the caller's stream.
+qg_status scratch_for_current_device(hipStream_t stream, void** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QG_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return QG_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return QG_ERR_HIP;
+        }
+        (void)hipGetLastError();
+        hipLaunchKernelGGL(scratch_zero, dim3(1), dim3(256), 0, stream,
+                           static_cast<unsigned char*>(ptr), kScratchBytes);
+        if (hipGetLastError() != hipSuccess) return QG_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
     return QG_OK;
 }
 
@@ -332,6 +392,26 @@ qg_status qgemv_q8g128_argmax(const void* w_packed, const uint16_t* x_bf16, floa
     if (!idx_out) return QG_ERR_INVALID_ARG;
     return run_dense(qg::FMT_Q8G128, w_packed, x_bf16, logits, m, N, K, ldx, ldy, hip_stream,
                      idx_out, workspace, workspace_bytes);
+}
+
+qg_status qgemv_q8g64_argmax_noalloc(const void* w_packed, const uint16_t* x_bf16, float* logits,
+                                     int32_t* idx_out, int64_t m, int64_t N, int64_t K, int64_t ldx,
+                                     int64_t ldy, void* hip_stream)
+{
+    // Everything the call itself would reject is rejected first, before the
+    // scratch is touched; the scratch holds the workspace of up to 4 rows.
+    if (!idx_out || !w_packed || !x_bf16) return QG_ERR_INVALID_ARG;
+    if (m == 0) return QG_OK;
+    if (m < 1 || m > 4 || qg::argmax_workspace_bytes(m) > kScratchBytes) return QG_ERR_UNSUPPORTED;
+    qg::Layout L;
+    const qg_status st = validate_dense(qg::FMT_Q8G64, w_packed, x_bf16, logits, idx_out, m, N, K, ldx,
+                                        ldy, &L);
+    if (st != QG_OK) return st;
+    void* ws = nullptr;
+    const qg_status sst = scratch_for_current_device(static_cast<hipStream_t>(hip_stream), &ws);
+    if (sst != QG_OK) return sst;
+    return run_dense(qg::FMT_Q8G64, w_packed, x_bf16, logits, m, N, K, ldx, ldy, hip_stream, idx_out, ws,
+                     kScratchBytes);
 }
 
 qg_status qgemv_q8g64_mma(const void* w_packed, const uint16_t* x_bf16, float* y, int64_t m,

@@ -96,6 +96,7 @@ def lib() -> ctypes.CDLL:
             "qgemv_q4g32_mma": ([p, p, p, i64, i64, i64, i64, i64, p], st),
             "qgemv_q8g64_argmax": ([p, p, p, p, i64, i64, i64, i64, i64, p, sz, p], st),
             "qgemv_q8g128_argmax": ([p, p, p, p, i64, i64, i64, i64, i64, p, sz, p], st),
+            "qgemv_q8g64_argmax_noalloc": ([p, p, p, p, i64, i64, i64, i64, i64, p], st),
             "qg_argmax_f32": ([p, i64, i64, i64, p, p, sz, p], st),
             "qg_route_counts_reset": ([], None),
             "qg_route_count": ([ctypes.c_char_p], ctypes.c_uint64),
@@ -510,6 +511,24 @@ def qgemv_q8g64_argmax(w_packed, x, logits, idx_out, workspace, N: int, K: int, 
                                                       K, m, ldx, ldy, stream))
     if check:
         _check(st, "qgemv_q8g64_argmax")
+    return st
+
+
+def qgemv_q8g64_argmax_noalloc(w_packed, x, logits, idx_out, N: int, K: int, m=None, ldx=None,
+                               ldy=None, stream=None, check=True):
+    """As qgemv_q8g64_argmax with the library's own per-GPU scratch in place
+    of a workspace (m = 1..4; calls that overlap on one GPU race)."""
+    if m is None:
+        m = 1 if x.dim() == 1 else x.shape[0]
+    if ldx is None:
+        ldx = x.stride(0) if x.dim() == 2 else K
+    if ldy is None:
+        ldy = logits.stride(0) if logits is not None and logits.dim() == 2 else N
+    st = lib().qgemv_q8g64_argmax_noalloc(w_packed.data_ptr(), x.data_ptr(),
+                                          None if logits is None else logits.data_ptr(),
+                                          idx_out.data_ptr(), m, N, K, ldx, ldy, _stream_handle(stream))
+    if check:
+        _check(st, "qgemv_q8g64_argmax_noalloc")
     return st
 
 
