@@ -222,12 +222,14 @@ __device__ __forceinline__ void q4_pairs_centred(const u32x4& c, int z, uint32_t
 // y_g = s c + min X errs by at most 6790 * 2^-24 |s| XA + 26 * 2^-24 |min| XA
 // + 2^-24 |y_g|; 26 / 6790 < 1/256 and the last term is counted with the
 // accumulation error on the host side of the threshold.  The constant below
-// is 6810 * 2^-24, which also covers the fp32 rounding of XA and of E.
+// is 6810 * 2^-24, which also covers the fp32 rounding of XA and of the
+// certificate's own terms.
 constexpr float kQ4Kappa = 6810.0f / 16777216.0f;
 constexpr float kQ4MinWeight = 1.0f / 256.0f;
 
 // x rows -> LDS as bf16 pairs; for Q4G32 also, per unit (group) u of row
-// i, X = sum x and XA = sum |x| at xsum[2 (i U + u)] and xsum[2 (i U + u) + 1].
+// i, X = sum x at xsum[2 (i U + u)] and kappa * sum |x| (kQ4Kappa) at
+// xsum[2 (i U + u) + 1].
 // X is formed by two v_dot2 chains over ones (eight pairs each) and an add,
 // exactly as the hot loop forms D, so that an all-zero group gives
 // D - 128 X = 0 exactly.  The 8-bit formats need no sums.  Thread t handles
@@ -273,7 +275,7 @@ struct XStage {
             }
             float2 xa;
             xa.x = X0 + X1;
-            xa.y = A0 + A1;
+            xa.y = kQ4Kappa * (A0 + A1);   // kappa * sum |x|, for the certificate
             reinterpret_cast<float2*>(xsum)[idx] = xa;
         }
     }
@@ -322,26 +324,28 @@ struct Item {
     }
 };
 
-// The Q4 fast path's per-row certificate sums (see kQ4Kappa): A = sum |y_g|
-// and E = sum (|s| + |min| / 256) XA over the groups a lane has consumed.
+// The Q4 fast path's per-row certificate (see kQ4Kappa), one sum per row:
+// C = sum over the groups a lane has consumed of
+//     T |y_g| - kappa (|s| + |min| / 256) XA,
+// with kappa folded into the staged XA.  The row's fast sum is proven to
+// meet the bar when its C >= 0.
 template <int FMT, int M, int R>
 struct Cert {
     static constexpr bool kOn = FMT == FMT_Q4G32;
-    float A[kOn ? R : 1][kOn ? M : 1];
-    float E[kOn ? R : 1][kOn ? M : 1];
+    float C[kOn ? R : 1][kOn ? M : 1];
     __device__ __forceinline__ void clear()
     {
 #pragma unroll
         for (int r = 0; r < (kOn ? R : 1); ++r)
 #pragma unroll
-            for (int i = 0; i < (kOn ? M : 1); ++i) A[r][i] = E[r][i] = 0.0f;
+            for (int i = 0; i < (kOn ? M : 1); ++i) C[r][i] = 0.0f;
     }
 };
 
 template <int FMT, int M, int R, int META_BYTES>
 __device__ __forceinline__ void consume(const Item<R, META_BYTES>& it, const uint32_t* xs,
                                         const float* xsum, int KD, int U, int u, const Q4Consts& k4,
-                                        float (&acc)[R][M], Cert<FMT, M, R>& cert)
+                                        float T, float (&acc)[R][M], Cert<FMT, M, R>& cert)
 {
     constexpr int UD = FMT == FMT_Q4G32 ? 16 : 8;
     uint32_t xd[M][UD];
@@ -398,8 +402,8 @@ __device__ __forceinline__ void consume(const Item<R, META_BYTES>& it, const uin
                 const float c = fmaf(-128.0f, X[i], D0 + D1);
                 const float yg = fmaf(s, c, mn * X[i]);
                 acc[r][i] += yg;
-                cert.A[r][i] += fabsf(yg);
-                cert.E[r][i] = fmaf(we, XA[i], cert.E[r][i]);
+                cert.C[r][i] = fmaf(T, fabsf(yg), cert.C[r][i]);
+                cert.C[r][i] = fmaf(-we, XA[i], cert.C[r][i]);
             }
         }
     }
@@ -576,21 +580,20 @@ __device__ __forceinline__ void finish_tile(float (&acc)[R][M], const KernelPara
     }
 }
 
-// End of a Q4 tile: reduces the certificate sums of every row the tile
-// holds and reports whether each row's fast sums are proven to meet the bar
-// (kQ4Kappa * E <= T * A; false for NaN).  The answer is the same in every
-// lane of the wave (a ballot), so the caller branches uniformly.
+// End of a Q4 tile: reduces the certificate sum of every row the tile holds
+// and reports whether each row's fast sums are proven to meet the bar
+// (C >= 0; false for NaN).  The answer is the same in every lane of the
+// wave (a ballot), so the caller branches uniformly.
 template <int M, int G, int R>
-__device__ __forceinline__ bool q4_tile_certified(Cert<FMT_Q4G32, M, R>& cert, float T, int g)
+__device__ __forceinline__ bool q4_tile_certified(Cert<FMT_Q4G32, M, R>& cert, int g)
 {
     using TS = TileSums<M, G, R>;
-    TS ta, te;
-    reduce_tile<M, G, R>(cert.A, ta);
-    reduce_tile<M, G, R>(cert.E, te);
+    TS tc;
+    reduce_tile<M, G, R>(cert.C, tc);
     bool bad = false;
     if (TS::holder(g)) {
 #pragma unroll
-        for (int k = 0; k < TS::V2; ++k) bad = bad || !(kQ4Kappa * te.v[k] <= T * ta.v[k]);
+        for (int k = 0; k < TS::V2; ++k) bad = bad || !(tc.v[k] >= 0.0f);
     }
     return __builtin_amdgcn_ballot_w64(bad) == 0;
 }
@@ -916,13 +919,13 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     int64_t tile = t0, j = 0;
 #define QG_CONSUME(slot_)                                                                     \
     do {                                                                                      \
-        consume<FMT, M, R, META_BYTES>(ring[slot_], xs, xsum, KD, U, int(j) * G + g, k4, acc, cert); \
+        consume<FMT, M, R, META_BYTES>(ring[slot_], xs, xsum, KD, U, int(j) * G + g, k4, p.cert_t, acc, cert); \
     } while (0)
 #define QG_ADVANCE()                                                                          \
     do {                                                                                      \
         if (++j == p.J) {                                                                     \
             if constexpr (FMT == FMT_Q4G32) {                                                 \
-                if (__builtin_expect(!q4_tile_certified<M, G, R>(cert, p.cert_t, g), 0))      \
+                if (__builtin_expect(!q4_tile_certified<M, G, R>(cert, g), 0))                \
                     q4_recompute_tile<M, G, R, META_BYTES>(acc, p, code_lane, meta_lane, tile, xs, \
                                                            xsum, KD, U, g);                   \
             }                                                                                 \

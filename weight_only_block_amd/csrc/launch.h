@@ -45,17 +45,21 @@ struct KernelParams {
 };
 
 // Threshold T of the Q4G32 fast path's certificate (kernel_body.h,
-// kQ4Kappa): a row's fast sum is accepted when kappa * E <= T * A.  The
-// bar is |y - y_exact| <= 2e-3 * sum |w x|; sum |w x| >= A - (fast error),
-// and adding the J per-lane partial sums and the log2(64) reduction levels
-// costs at most (J + 7) * 2^-24 * A more (the same for forming A itself).
-// So kappa E + (J + 7) u A <= 2e-3 (A (1 - (J + 7) u) - kappa E) is enough,
-// which holds when kappa E <= A (2e-3 - 2.01 (J + 7) u) / 1.002; 1e-6 is
-// taken off for the fp32 evaluation of the comparison.
+// kQ4Kappa): a row's fast sum is accepted when
+//     C = sum_g (T |y_g| - kappa (|s| + |min| / 256) XA_g) >= 0.
+// The bar is |y - y_exact| <= 2e-3 * sum |w x|; sum |w x| >= A - kappa E
+// with A = sum |y_g| and E the sum of the kappa terms' factors, and adding
+// the J per-lane partial sums and the log2(64) reduction levels costs at
+// most (J + 7) * 2^-24 * A more (the same for forming A).  So kappa E +
+// (J + 7) u A <= 2e-3 (A (1 - (J + 7) u) - kappa E) is enough, which holds
+// when kappa E <= A (2e-3 - 2.01 (J + 7) u) / 1.002.  C itself is summed in
+// fp32 over the same J + 7 steps, so T is reduced by a further relative
+// 4 (J + 7) u, and by 1e-6 for the rounding of each term.
 inline float q4_cert_threshold(int64_t J)
 {
     const double u = 1.0 / 16777216.0;
-    return float((2e-3 - 2.01 * double(J + 7) * u) / 1.002 - 1e-6);
+    const double t = (2e-3 - 2.01 * double(J + 7) * u) / 1.002;
+    return float(t * (1.0 - 4.0 * double(J + 7) * u) - 1e-6);
 }
 
 // Launch shape: ring depth 2 or 4 items; work-groups are 4 waves.
