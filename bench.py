@@ -87,28 +87,45 @@ def dev(torch, a):
     return torch.from_numpy(a).to("cuda")
 
 
-def time_steps(torch, step, warmup, steps):
+ROUNDS = 5
+
+
+def _round_edges(steps, rounds):
+    """Step indices that split K timed steps into `rounds` consecutive rounds."""
+    rounds = max(1, min(rounds, steps))
+    return [steps * r // rounds for r in range(rounds + 1)]
+
+
+def time_steps(torch, step, warmup, steps, rounds=ROUNDS):
     """W untimed steps, then exactly K timed steps bracketed by synchronize
-    and HIP events on torch's current stream (the stream the kernels use)."""
+    and HIP events on torch's current stream (the stream the kernels use).
+    The K steps are split into consecutive rounds, each between its own pair
+    of events (no synchronize in between), so the same run also gives the
+    per-round times.  Returns (total seconds, [seconds per step of each
+    round])."""
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(steps):
-        step(warmup + i)
-    end.record()
+    edges = _round_edges(steps, rounds)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in edges]
+    ev[0].record()
+    for r in range(len(edges) - 1):
+        for i in range(edges[r], edges[r + 1]):
+            step(warmup + i)
+        ev[r + 1].record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) * 1e-3       # seconds
+    per_round = [ev[r].elapsed_time(ev[r + 1]) * 1e-3 / (edges[r + 1] - edges[r])
+                 for r in range(len(edges) - 1)]
+    return ev[0].elapsed_time(ev[-1]) * 1e-3, per_round
 
 
-def time_steps_graph(torch, step, warmup, steps, period):
+def time_steps_graph(torch, step, warmup, steps, period, rounds=ROUNDS):
     """As time_steps, but the launches of P consecutive steps are captured
     once into a HIP graph that is replayed K/P times: host launch cost leaves
     the timed region, the GPU work is the same.  P is the largest divisor of
     K up to 2000 (replaying small graphs costs more than it saves), and the
-    captured steps keep the workload's rotation of weights and ids."""
+    captured steps keep the workload's rotation of weights and ids.  Rounds
+    are whole replays, so fewer than `rounds` when K/P is small."""
     P = max(d for d in range(1, min(steps, 2000) + 1) if steps % d == 0)
     for i in range(warmup):
         step(i)
@@ -119,14 +136,17 @@ def time_steps_graph(torch, step, warmup, steps, period):
             step(i)
     g.replay()                      # one untimed replay
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps // P):
-        g.replay()
-    end.record()
+    edges = _round_edges(steps // P, rounds)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in edges]
+    ev[0].record()
+    for r in range(len(edges) - 1):
+        for _ in range(edges[r], edges[r + 1]):
+            g.replay()
+        ev[r + 1].record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) * 1e-3
+    per_round = [ev[r].elapsed_time(ev[r + 1]) * 1e-3 / ((edges[r + 1] - edges[r]) * P)
+                 for r in range(len(edges) - 1)]
+    return ev[0].elapsed_time(ev[-1]) * 1e-3, per_round
 
 
 def read_stream_reference(torch, Q, bytes_per_launch, launches=300, warmup=50):
@@ -302,6 +322,18 @@ def cpu_lm_head(oracle, cpu, threads, reps):
         fn(cpu["q"], cpu["s"], cpu["x"], threads=threads)
         times.append(time.perf_counter() - t0)
     return float(np.median(times)), "one full lm_head call (151936 x 2560, m=1), median of %d" % reps
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ------------------------------------------------------ small dense configs
@@ -646,10 +678,11 @@ def main():
             step, alg, wbytes, launches, info, cpu = setup_dense(torch, Q, synth, name, args.m)
         log("setup %s: %.1f s" % (name, time.time() - t0))
         if args.graph:
-            secs = time_steps_graph(torch, step, args.warmup, args.steps, info.get("period", 1))
+            secs, rounds = time_steps_graph(torch, step, args.warmup, args.steps, info.get("period", 1))
         else:
-            secs = time_steps(torch, step, args.warmup, args.steps)
-        return dict(secs=secs, alg=alg, wbytes=wbytes, launches=launches, info=info, cpu=cpu)
+            secs, rounds = time_steps(torch, step, args.warmup, args.steps)
+        return dict(secs=secs, rounds=rounds, alg=alg, wbytes=wbytes, launches=launches, info=info,
+                    cpu=cpu)
 
     head = measure(args.workload)
     secs, steps = head["secs"], args.steps
@@ -681,6 +714,17 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
     }
+    # The timed steps in consecutive rounds (each between its own events):
+    # the median round and the spread between the fastest and slowest.
+    round_us = [t / head["launches"] * 1e6 for t in head["rounds"]]
+    out["rounds"] = {"count": len(round_us), "steps_per_round": args.steps // max(1, len(round_us)),
+                     "us_per_call": [round(u, 3) for u in round_us],
+                     "median_us_per_call": round(float(np.median(round_us)), 3),
+                     "min_us_per_call": round(min(round_us), 3),
+                     "max_us_per_call": round(max(round_us), 3),
+                     "median_pct_hbm_peak": round(100.0 * head["alg"] / head["launches"]
+                                                  / (float(np.median(round_us)) * 1e-6) / 1e9
+                                                  / HBM_PEAK_GBS, 2)}
     digest = kernel_source_digest(args.workload)
     entry = TRAFFIC.get(args.workload, {})
     if not HOT and entry.get("source_digest") == digest and entry.get("m", args.m) == args.m:
@@ -693,15 +737,24 @@ def main():
                               "GBs": round(bpl / t / 1e9, 2), "waves_per_cu": wpc,
                               "frac": round(achieved / (bpl / t / 1e9), 4)}
     if not args.no_cpu and head["cpu"] is not None:
+        # The oracle as the parity tests run it, on the host: (i) one thread,
+        # (ii) output rows split over the host cores it may use (at most 16,
+        # the host's CPU share per GPU).
         import oracle
-        threads = max(1, min(16, len(os.sched_getaffinity(0))))
-        if args.workload in ("lm_head", "lm_head_q8g128"):
-            t, sample = cpu_lm_head(oracle, head["cpu"], threads, args.cpu_reps)
-        else:
-            t, sample = cpu_moe(oracle, head["cpu"], threads, args.cpu_reps, synth)
-        out["cpu_baseline"] = {"value": round(head["alg"] / t / 1e9, 4), "unit": "GB/s",
+        affinity = len(os.sched_getaffinity(0))
+        threads = max(1, min(16, affinity))
+        run = cpu_lm_head if args.workload in ("lm_head", "lm_head_q8g128") else (
+            lambda o, c, t, r: cpu_moe(o, c, t, r, synth))
+        t1, sample1 = run(oracle, head["cpu"], 1, args.cpu_reps)
+        tp, sample = run(oracle, head["cpu"], threads, args.cpu_reps)
+        out["cpu_baseline"] = {"value": round(head["alg"] / tp / 1e9, 4), "unit": "GB/s",
                                "cores": threads, "kind": "oracle", "sample": sample,
-                               "seconds_per_step": round(t, 4)}
+                               "seconds_per_step": round(tp, 4),
+                               "single_thread": {"value": round(head["alg"] / t1 / 1e9, 4),
+                                                 "unit": "GB/s", "cores": 1, "sample": sample1,
+                                                 "seconds_per_step": round(t1, 4)},
+                               "affinity_cores": affinity, "cores_cap": 16,
+                               "cpu_model": cpu_model()}
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
@@ -720,10 +773,13 @@ def main():
         torch.cuda.empty_cache()
         sec = measure(other)
         ps = sec["secs"] / steps
+        sec_round_us = [t / sec["launches"] * 1e6 for t in sec["rounds"]]
         out["secondary"] = {"workload": sec["info"]["workload"], "launches_per_step": sec["launches"],
                             "us_per_call": round(ps / sec["launches"] * 1e6, 3),
                             "effective_GBs": round(sec["alg"] / ps / 1e9, 2),
-                            "pct_hbm_peak": round(100 * sec["alg"] / ps / 1e9 / HBM_PEAK_GBS, 2)}
+                            "pct_hbm_peak": round(100 * sec["alg"] / ps / 1e9 / HBM_PEAK_GBS, 2),
+                            "rounds_us_per_call": [round(u, 3) for u in sec_round_us],
+                            "median_us_per_call": round(float(np.median(sec_round_us)), 3)}
         if args.read_stream:
             bpl = sec["alg"] / sec["launches"]
             t, wpc = read_stream_reference(torch, Q, bpl)

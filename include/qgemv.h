@@ -52,8 +52,18 @@
 extern "C" {
 #endif
 
+/* Version of this interface and of the packed layouts: a buffer packed by
+ * qpack_* is valid input only for a library of the same version.  Version 2
+ * stores 8-bit codes unbiased (signed, as given). */
 #define QG_ABI_VERSION 2
 
+/* Result of every call that can fail.  Errors are returned, never thrown and
+ * never answered by running some other path: the explicit Status / Result
+ * propagation of the MetaInfer-cpp (Qwen3 C++ Reference Runtime) README,
+ * milestone "M1 Core 与 Backend", whose HIP backend returns Unsupported
+ * instead of falling back to the CPU.  Validation (shape, stride, alignment,
+ * byte range) happens on the host before anything is enqueued, after that
+ * section's validated TensorView. */
 typedef enum qg_status {
     QG_OK = 0,
     QG_ERR_INVALID_ARG = 1,  /* null pointer, bad size, stride or buffer length */
@@ -62,15 +72,21 @@ typedef enum qg_status {
     QG_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
 } qg_status;
 
-/* Human-readable name of a status code; never NULL. */
-const char *qg_status_string(int status);
+/* Human-readable name of a status code (the same "M1 Core 与 Backend"
+ * convention); "unknown status" for a value outside the enum; never NULL. */
+const char *qg_status_string(qg_status status);
 
 /* QG_ABI_VERSION of the built library. */
 int qg_abi_version(void);
 
 /* ------------------------------------------------------------------ packing
  * qpack_* re-tile canonical weights, once per matrix, into the layout the
- * kernels stream with 16-byte loads per lane.  Row order and the grouping
+ * kernels stream with 16-byte loads per lane.  The layout is fixed once, at
+ * load time (the WeightArchive of the MetaInfer-cpp README, milestone "M2
+ * Model Inputs 与 Weight Loading", materialises weights once in 256-byte
+ * aligned storage), and only whole rows move (the commit log of vllm.cpp
+ * pull request #1936 notes that row permutation is safe for block formats,
+ * while column permutation crosses groups).  Row order and the grouping
  * along K are kept; the packed buffer is opaque and its size depends only
  * on (N, K).  K must be a whole number of groups (64 for Q8G64, 128 for
  * Q8G128, 32 for Q4G32, 16 for Q8PC) and 1 <= N, K < 2^31.
@@ -318,13 +334,19 @@ qg_status qgemv_q8g64_argmax_noalloc(const void *w_packed, const uint16_t *x_bf1
                                      int64_t ldy, void *hip_stream);
 
 /* ------------------------------------------------------------- test hooks
- * Every successful qgemv_* call bumps the counter of the kernel variant it
- * launched.  Variant names: "<fmt>[_grouped[_swiglu]|_argmax]_m<m>_g<G>_r<R>"
+ * Host-side route counters, after the routing witnesses of the vllm.cpp pull
+ * request #1936 commit log (process-global counters bumped once per dispatch
+ * on exactly the branch taken, with a reset hook, so that tests can assert
+ * which kernel ran).  Every successful qgemv_* call bumps the counter of the
+ * kernel variant it launched.  Variant names: "<fmt>[_grouped[_swiglu]|_argmax]_m<m>_g<G>_r<R>"
  * with fmt one of q8g64, q4g32, q8g128, q8pc, e.g. "q8g64_m1_g32_r2".
  * qg_route_count returns 0 for unknown names. */
 void     qg_route_counts_reset(void);
 uint64_t qg_route_count(const char *variant);
 /* Writes the name of the variant qgemv_* would launch for (fmt, m, N, K)
+ * (one distinct kernel symbol per variant, so that a profile never averages
+ * two of them under one name: the symbol-collision lesson of the vllm.cpp
+ * pull request #1936 commit log)
  * into buf (fmt 0 = Q8G64, 1 = Q4G32, 2 = grouped Q4G32, 3 = Q8G128,
  * 4 = Q8PC, 5 = grouped Q4G32 with SwiGLU, N = gate rows, 6 = Q8G64 with
  * the argmax epilogue, 7 = Q8G128 with the argmax epilogue, 8/9/10 = the
@@ -332,7 +354,10 @@ uint64_t qg_route_count(const char *variant);
  * the matrix-core kernel for Q4G32, "q4g32_mma_m<m>").
  * Returns QG_OK or the status the call itself would return for that shape. */
 qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char *buf, size_t buf_len);
-/* Overrides how the non-matrix-core kernels (qgemv_q8g64, qgemv_q4g32,
+/* Launch-geometry override for the per-shape launch sweeps of the vllm.cpp
+ * pull request #1936 commit log (tile and work-group counts swept per shape,
+ * a choice adopted only on measured evidence).
+ * Overrides how the non-matrix-core kernels (qgemv_q8g64, qgemv_q4g32,
  * qgemv_q8g128, qgemv_q8pc, the grouped calls and the *_argmax calls) map
  * tiles to waves, for tests and tuning sweeps.  Every tile is computed the
  * same way under any mapping, so results are the same bits.

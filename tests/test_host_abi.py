@@ -212,14 +212,18 @@ def test_variant_names_follow_layout():
     assert Q.route_count("no_such_variant") == 0
 
 
-def test_bound_calls_keep_their_buffers_alive():
+def test_bound_calls_keep_their_buffers_alive(monkeypatch):
     # A prepared call passes raw device addresses; it must own the tensors
     # behind them, or torch may release the memory (graph capture empties
-    # torch's cache) while the call can still be replayed.
+    # torch's cache) while the call can still be replayed.  (Small host
+    # tensors stand in for device ones here, so the binding's tensor checks
+    # are switched off; the calls are never issued.)
     import gc
     import weakref
 
     import torch
+    monkeypatch.setattr(Q, "_on_gpu", lambda *a, **k: None)
+    monkeypatch.setattr(Q, "_need", lambda *a, **k: None)
     w = torch.zeros(4096, dtype=torch.uint8)
     x = torch.zeros(64, dtype=torch.int16)
     y = torch.zeros(16, dtype=torch.float32)
@@ -414,3 +418,48 @@ def test_read_stream_validation():
     assert f(256, 16, 64, -1, None) == Q.QG_ERR_INVALID_ARG
     assert f(264, 16, 64, 0, None) == Q.QG_ERR_ALIGNMENT
     assert f(256, 16, 66, 0, None) == Q.QG_ERR_ALIGNMENT
+
+
+def test_binding_checks_tensors_before_calling_the_library():
+    # The torch-facing wrappers reject a wrong element type, a tensor too
+    # short for the shape and a tensor that is not on a GPU, with
+    # QG_ERR_INVALID_ARG, before any pointer reaches the C ABI (no GPU
+    # needed: the checks run on the host and nothing is launched).
+    torch = pytest.importorskip("torch")
+    N, K, m = 64, 128, 2
+    w = torch.zeros(Q.qpack_q8g64_size(N, K), dtype=torch.uint8)
+    x = torch.zeros((m, K), dtype=torch.bfloat16)
+    y = torch.zeros((m, N), dtype=torch.float32)
+
+    def rejects(fn, *a, **kw):
+        with pytest.raises(Q.QGError) as e:
+            fn(*a, **kw)
+        assert e.value.status == Q.QG_ERR_INVALID_ARG
+        return str(e.value)
+
+    assert "dtype" in rejects(Q.qgemv_q8g64, w, x.float(), y, N, K)
+    assert "dtype" in rejects(Q.qgemv_q8g64, w, x, y.double(), N, K)
+    assert "dtype" in rejects(Q.qgemv_q8g64, w.to(torch.int32), x, y, N, K)
+    assert "elements" in rejects(Q.qgemv_q8g64, w[:-1], x, y, N, K)
+    assert "elements" in rejects(Q.qgemv_q8g64, w, x[:, :K - 2], y, N, K, m=m, ldx=K)
+    assert "elements" in rejects(Q.qgemv_q8g64, w, x, y[:1], N, K, m=m, ldy=N)
+    assert "GPU" in rejects(Q.qgemv_q8g64, w, x, y, N, K)
+    # routed experts: int64 ids (torch's default integer type) are refused
+    Ne, Ke, E = 32, 64, 3
+    stride = Q.expert_stride(Ne, Ke)
+    we = torch.zeros(E * stride, dtype=torch.uint8)
+    ids = torch.zeros(2, dtype=torch.int64)
+    xe = torch.zeros((2, Ke), dtype=torch.int16)
+    ye = torch.zeros((2, Ne), dtype=torch.float32)
+    assert "dtype" in rejects(Q.qgemv_grouped_q4g32, we, stride, E, ids, xe, Ke, ye, Ne, Ne, Ke)
+    ids32 = ids.to(torch.int32)
+    assert "elements" in rejects(Q.qgemv_grouped_q4g32, we[:-256], stride, E, ids32, xe, Ke, ye, Ne, Ne, Ke)
+    assert "elements" in rejects(Q.qgemv_grouped_q4g32, we, stride, E, ids32, xe[:1], Ke, ye, Ne, Ne, Ke)
+    assert "GPU" in rejects(Q.qgemv_grouped_q4g32, we, stride, E, ids32, xe, Ke, ye, Ne, Ne, Ke)
+    # argmax: the logits must cover m rows of N at stride ldx
+    lg = torch.zeros((2, 100), dtype=torch.float32)
+    idx = torch.zeros(2, dtype=torch.int32)
+    ws = torch.zeros(Q.argmax_workspace_size(2), dtype=torch.uint8)
+    assert "elements" in rejects(Q.argmax_f32, lg[:1], idx, ws, N=100, m=2, ldx=100)
+    assert "dtype" in rejects(Q.argmax_f32, lg, idx.long(), ws, N=100, m=2)
+    assert "GPU" in rejects(Q.argmax_f32, lg, idx, ws, N=100, m=2)

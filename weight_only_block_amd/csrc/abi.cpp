@@ -242,7 +242,7 @@ qg_status scratch_for_current_device(hipStream_t stream, void** out)
 
 extern "C" {
 
-const char* qg_status_string(int status)
+const char* qg_status_string(qg_status status)
 {
     switch (status) {
     case QG_OK: return "ok";

@@ -40,7 +40,10 @@ _lib = None
 class QGError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = int(status)
-        super().__init__("%s failed: %s (status %d)" % (where, status_string(status), status))
+        names = {QG_OK: "ok", QG_ERR_INVALID_ARG: "invalid argument", QG_ERR_UNSUPPORTED: "unsupported",
+                 QG_ERR_ALIGNMENT: "misaligned pointer or stride", QG_ERR_HIP: "HIP runtime error"}
+        super().__init__("%s failed: %s (status %d)" % (where, names.get(self.status, "unknown status"),
+                                                        status))
 
 
 def lib() -> ctypes.CDLL:
@@ -123,6 +126,76 @@ def _check(status: int, where: str) -> None:
 
 def _np_ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ------------------------------------------------- device-argument checks
+# The C ABI sees only pointers, so a tensor on the wrong device, of the wrong
+# element type or too short for the shape would be read or written out of
+# bounds on the GPU.  Every torch-facing call below checks its tensors here
+# first and raises QGError(QG_ERR_INVALID_ARG) instead of calling the library.
+
+_W_DTYPES = ("uint8", "int8")
+_X_DTYPES = ("bfloat16", "int16", "uint16")
+_F32 = ("float32",)
+_I32 = ("int32",)
+
+
+def _extent(t) -> int:
+    """Elements the view t spans from t.data_ptr(): one past its last element
+    (for a row-strided view of m rows of K, (m - 1) * stride + K)."""
+    if t.numel() == 0:
+        return 0
+    return 1 + sum((n - 1) * st for n, st in zip(t.shape, t.stride()))
+
+
+def _need(t, where: str, what: str, dtypes, elems: int) -> None:
+    """Element type and extent of one tensor (the device is checked by _on_gpu)."""
+    dt = str(t.dtype).replace("torch.", "")
+    if dt not in dtypes:
+        raise QGError(QG_ERR_INVALID_ARG, "%s: %s has dtype %s, needs %s" % (where, what, dt, "/".join(dtypes)))
+    if elems > 0 and _extent(t) < elems:
+        raise QGError(QG_ERR_INVALID_ARG, "%s: %s holds %d elements from its start, the call reads or "
+                      "writes %d" % (where, what, _extent(t), elems))
+
+
+def _on_gpu(where: str, **tensors) -> None:
+    for what, t in tensors.items():
+        if t is not None and t.device.type != "cuda":
+            raise QGError(QG_ERR_INVALID_ARG, "%s: %s is not a GPU tensor" % (where, what))
+
+
+_PACKED_SIZE = {
+    "qgemv_q8g64": "qpack_q8g64_size", "qgemv_q4g32": "qpack_q4g32_size",
+    "qgemv_q8g128": "qpack_q8g128_size", "qgemv_q8pc": "qpack_q8pc_size",
+    "qgemv_q8g64_mma": "qpack_q8g64_mma_size", "qgemv_q8g128_mma": "qpack_q8g128_mma_size",
+    "qgemv_q8pc_mma": "qpack_q8pc_mma_size", "qgemv_q4g32_mma": "qpack_q4g32_mma_size",
+    "qgemv_q8g64_argmax": "qpack_q8g64_size", "qgemv_q8g128_argmax": "qpack_q8g128_size",
+    "qgemv_q8g64_argmax_noalloc": "qpack_q8g64_size",
+}
+
+
+def _check_dense(fn_name, w_packed, x, y, m, N, K, ldx, ldy, idx_out=None):
+    if m <= 0:
+        return
+    size = int(getattr(lib(), _PACKED_SIZE[fn_name])(N, K)) if N > 0 and K > 0 else 0
+    _need(w_packed, fn_name, "w_packed", _W_DTYPES, size)
+    _need(x, fn_name, "x", _X_DTYPES, (m - 1) * ldx + K)
+    if y is not None:
+        _need(y, fn_name, "y", _F32, (m - 1) * ldy + N)
+    if idx_out is not None:
+        _need(idx_out, fn_name, "idx_out", _I32, m)
+    _on_gpu(fn_name, w_packed=w_packed, x=x, y=y, idx_out=idx_out)
+
+
+def _check_grouped(fn_name, w, stride, n_experts, ids, n_slots, x, x_slot_stride, out, out_slot_stride,
+                   N, K, out_dtypes, packed_size):
+    if n_slots <= 0:
+        return
+    _need(w, fn_name, "w_experts", _W_DTYPES, (n_experts - 1) * stride + packed_size if n_experts > 0 else 0)
+    _need(ids, fn_name, "expert_ids", _I32, n_slots)
+    _need(x, fn_name, "x", _X_DTYPES, (n_slots - 1) * x_slot_stride + K)
+    _need(out, fn_name, "y" if out_dtypes == _F32 else "act", out_dtypes, (n_slots - 1) * out_slot_stride + N)
+    _on_gpu(fn_name, w_experts=w, expert_ids=ids, x=x, out=out)
 
 
 def _stream_handle(stream):
@@ -365,6 +438,7 @@ def _dense(fn_name, w_packed, x, y, N, K, m=None, ldx=None, ldy=None, stream=Non
         ldx = x.stride(0) if x.dim() == 2 else K
     if ldy is None:
         ldy = y.stride(0) if y.dim() == 2 else N
+    _check_dense(fn_name, w_packed, x, y, m, N, K, ldx, ldy)
     st = getattr(lib(), fn_name)(w_packed.data_ptr(), x.data_ptr(), y.data_ptr(), m, N, K, ldx, ldy,
                                  _stream_handle(stream))
     if check:
@@ -435,6 +509,8 @@ def qgemv_grouped_q4g32(w_experts, expert_stride_bytes: int, n_experts: int, exp
     expert_stride_bytes; expert_ids: device int32 tensor [n_slots]."""
     if n_slots is None:
         n_slots = expert_ids.numel()
+    _check_grouped("qgemv_grouped_q4g32", w_experts, expert_stride_bytes, n_experts, expert_ids, n_slots,
+                   x, x_slot_stride, y, y_slot_stride, N, K, _F32, qpack_q4g32_size(N, K))
     st = lib().qgemv_grouped_q4g32(w_experts.data_ptr(), expert_stride_bytes, n_experts,
                                    expert_ids.data_ptr(), n_slots, x.data_ptr(), x_slot_stride,
                                    y.data_ptr(), y_slot_stride, N, K, _stream_handle(stream))
@@ -454,6 +530,9 @@ def qgemv_grouped_q4g32_swiglu(w_gate_up, expert_stride_bytes: int, n_experts: i
     qpack_q4g32_gate_up at expert_stride_bytes; act: device 16-bit tensor."""
     if n_slots is None:
         n_slots = expert_ids.numel()
+    _check_grouped("qgemv_grouped_q4g32_swiglu", w_gate_up, expert_stride_bytes, n_experts, expert_ids,
+                   n_slots, x, x_slot_stride, act, act_slot_stride, N, K, _X_DTYPES,
+                   qpack_q4g32_gate_up_size(N, K))
     st = lib().qgemv_grouped_q4g32_swiglu(w_gate_up.data_ptr(), expert_stride_bytes, n_experts,
                                           expert_ids.data_ptr(), n_slots, x.data_ptr(),
                                           x_slot_stride, act.data_ptr(), act_slot_stride, N, K,
@@ -481,6 +560,7 @@ def argmax_f32(x, idx_out, workspace, N=None, m=None, ldx=None, stream=None, che
     if ldx is None:
         ldx = x.stride(0) if x.dim() == 2 else N
     nbytes = workspace.numel() * workspace.element_size()
+    _check_argmax(x, idx_out, workspace, m, N, ldx)
     st = lib().qg_argmax_f32(x.data_ptr(), m, N, ldx, idx_out.data_ptr(), workspace.data_ptr(),
                              nbytes, _stream_handle(stream))
     if check:
@@ -488,13 +568,24 @@ def argmax_f32(x, idx_out, workspace, N=None, m=None, ldx=None, stream=None, che
     return st
 
 
-def _argmax_gemv_args(w_packed, x, logits, idx_out, workspace, N, K, m, ldx, ldy, stream):
+def _check_argmax(x, idx_out, workspace, m, N, ldx):
+    if m <= 0:
+        return
+    _need(x, "qg_argmax_f32", "x", _F32, (m - 1) * ldx + N)
+    _need(idx_out, "qg_argmax_f32", "idx_out", _I32, m)
+    _on_gpu("qg_argmax_f32", x=x, idx_out=idx_out, workspace=workspace)
+
+
+def _argmax_gemv_args(w_packed, x, logits, idx_out, workspace, N, K, m, ldx, ldy, stream,
+                      fn_name="qgemv_q8g64_argmax"):
     if m is None:
         m = 1 if x.dim() == 1 else x.shape[0]
     if ldx is None:
         ldx = x.stride(0) if x.dim() == 2 else K
     if ldy is None:
         ldy = logits.stride(0) if logits is not None and logits.dim() == 2 else N
+    _check_dense(fn_name, w_packed, x, logits, m, N, K, ldx, ldy, idx_out)
+    _on_gpu(fn_name, workspace=workspace)
     nbytes = workspace.numel() * workspace.element_size()
     return (w_packed.data_ptr(), x.data_ptr(), None if logits is None else logits.data_ptr(),
             idx_out.data_ptr(), m, N, K, ldx, ldy, workspace.data_ptr(), nbytes,
@@ -524,6 +615,7 @@ def qgemv_q8g64_argmax_noalloc(w_packed, x, logits, idx_out, N: int, K: int, m=N
         ldx = x.stride(0) if x.dim() == 2 else K
     if ldy is None:
         ldy = logits.stride(0) if logits is not None and logits.dim() == 2 else N
+    _check_dense("qgemv_q8g64_argmax_noalloc", w_packed, x, logits, m, N, K, ldx, ldy, idx_out)
     st = lib().qgemv_q8g64_argmax_noalloc(w_packed.data_ptr(), x.data_ptr(),
                                           None if logits is None else logits.data_ptr(),
                                           idx_out.data_ptr(), m, N, K, ldx, ldy, _stream_handle(stream))
@@ -536,7 +628,7 @@ def qgemv_q8g128_argmax(w_packed, x, logits, idx_out, workspace, N: int, K: int,
                         ldy=None, stream=None, check=True):
     """As qgemv_q8g64_argmax for Q8G128 weights."""
     st = lib().qgemv_q8g128_argmax(*_argmax_gemv_args(w_packed, x, logits, idx_out, workspace, N,
-                                                       K, m, ldx, ldy, stream))
+                                                       K, m, ldx, ldy, stream, "qgemv_q8g128_argmax"))
     if check:
         _check(st, "qgemv_q8g128_argmax")
     return st
@@ -590,6 +682,7 @@ def bound_q8pc(w_packed, x, y, N: int, K: int, m: int = 1, ldx=None, ldy=None, s
 def _bind(fn_name, w_packed, x, y, N, K, m, ldx, ldy, stream):
     ldx = K if ldx is None else ldx
     ldy = N if ldy is None else ldy
+    _check_dense(fn_name, w_packed, x, y, m, N, K, ldx, ldy)
     args = (w_packed.data_ptr(), x.data_ptr(), y.data_ptr(), m, N, K, ldx, ldy,
             _stream_handle(stream))
     return BoundCall(getattr(lib(), fn_name), args, fn_name, (w_packed, x, y))
@@ -601,6 +694,8 @@ def bound_grouped_q4g32(w_experts, expert_stride_bytes: int, n_experts: int, exp
     """As bound_q8g64 for qgemv_grouped_q4g32."""
     if n_slots is None:
         n_slots = expert_ids.numel()
+    _check_grouped("qgemv_grouped_q4g32", w_experts, expert_stride_bytes, n_experts, expert_ids, n_slots,
+                   x, x_slot_stride, y, y_slot_stride, N, K, _F32, qpack_q4g32_size(N, K))
     args = (w_experts.data_ptr(), expert_stride_bytes, n_experts, expert_ids.data_ptr(), n_slots,
             x.data_ptr(), x_slot_stride, y.data_ptr(), y_slot_stride, N, K, _stream_handle(stream))
     return BoundCall(lib().qgemv_grouped_q4g32, args, "qgemv_grouped_q4g32",
@@ -613,6 +708,9 @@ def bound_grouped_q4g32_swiglu(w_gate_up, expert_stride_bytes: int, n_experts: i
     """As bound_q8g64 for qgemv_grouped_q4g32_swiglu."""
     if n_slots is None:
         n_slots = expert_ids.numel()
+    _check_grouped("qgemv_grouped_q4g32_swiglu", w_gate_up, expert_stride_bytes, n_experts, expert_ids,
+                   n_slots, x, x_slot_stride, act, act_slot_stride, N, K, _X_DTYPES,
+                   qpack_q4g32_gate_up_size(N, K))
     args = (w_gate_up.data_ptr(), expert_stride_bytes, n_experts, expert_ids.data_ptr(), n_slots,
             x.data_ptr(), x_slot_stride, act.data_ptr(), act_slot_stride, N, K,
             _stream_handle(stream))
@@ -624,6 +722,7 @@ def bound_argmax_f32(x, idx_out, workspace, N: int, m: int = 1, ldx=None, stream
     """As bound_q8g64 for qg_argmax_f32."""
     ldx = N if ldx is None else ldx
     nbytes = workspace.numel() * workspace.element_size()
+    _check_argmax(x, idx_out, workspace, m, N, ldx)
     args = (x.data_ptr(), m, N, ldx, idx_out.data_ptr(), workspace.data_ptr(), nbytes,
             _stream_handle(stream))
     return BoundCall(lib().qg_argmax_f32, args, "qg_argmax_f32", (x, idx_out, workspace))
