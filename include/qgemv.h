@@ -69,7 +69,12 @@ typedef enum qg_status {
     QG_ERR_INVALID_ARG = 1,  /* null pointer, bad size, stride or buffer length */
     QG_ERR_UNSUPPORTED = 2,  /* valid request outside what is built (m > 4, ...) */
     QG_ERR_ALIGNMENT = 3,    /* a pointer or stride breaks an alignment rule */
-    QG_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
+    QG_ERR_HIP = 4,          /* the HIP runtime reported an error at launch */
+    /* Reserved, never returned: they make every int a valid qg_status value
+     * (C++ leaves an enum holding a value outside its range undefined, and
+     * a status read from elsewhere may hold anything). */
+    QG_STATUS_RESERVED_MIN_ = -2147483647 - 1,
+    QG_STATUS_RESERVED_MAX_ = 2147483647
 } qg_status;
 
 /* Human-readable name of a status code (the same "M1 Core 与 Backend"

@@ -46,10 +46,23 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+def build_sanitized(out_path: str, clang: str = "/opt/rocm/llvm/bin/clang") -> str:
+    """oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer, linked
+    against clang's shared ASan runtime (for the host-sanitizer CPU tests,
+    which load it through ORACLE_LIBRARY)."""
+    cmd = [clang, "-O1", "-g", "-fPIC", "-shared", "-std=c99", "-fno-fast-math",
+           "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-shared-libasan",
+           "-o", out_path, _SRC, "-lm"]
+    subprocess.check_call(cmd)
+    return out_path
+
+
 def _load():
     global _lib
     if _lib is None:
-        lib = ctypes.CDLL(build())
+        # ORACLE_LIBRARY names another build of oracle.c (the host-sanitizer
+        # build of the CPU tests).
+        lib = ctypes.CDLL(os.environ.get("ORACLE_LIBRARY") or build())
         p = ctypes.c_void_p
         i64 = ctypes.c_int64
         lib.oracle_q8g64.argtypes = [p, p, i64, i64, p, i64, i64, i64, i64, p, p, i64]

@@ -37,28 +37,45 @@ HIP_SOURCES = ["kern_q8g64.hip", "kern_q4g32.hip", "kern_q8g128.hip", "kern_q8pc
 HOST_SOURCES = ["qpack.cpp"]
 
 
-def build(verbose: bool = True) -> str:
+# Host-sanitizer build (CPU tests only): AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host code (the packer, the C ABI's
+# validation, the launch sizing), linked against clang's shared ASan
+# runtime; the gfx950 device code is built as usual.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-shared-libasan"]
+
+
+def build(verbose: bool = True, out_dir: str = None, sanitize: bool = False) -> str:
     """Compiles every source (the per-format kernel units in parallel) and
-    links libqgemv.so."""
+    links libqgemv.so (into the package, or into out_dir).  sanitize=True
+    makes the host-sanitizer build; every source then goes through hipcc so
+    that one ASan runtime serves the whole library."""
     from concurrent.futures import ThreadPoolExecutor
 
-    os.makedirs(BUILD, exist_ok=True)
+    obj_dir = os.path.join(out_dir, "obj") if out_dir else BUILD
+    lib_path = os.path.join(out_dir, "libqgemv.so") if out_dir else LIB
+    os.makedirs(obj_dir, exist_ok=True)
     jobs = []
-    for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    hip_flags = HIP_FLAGS + (SANITIZE_HOST if sanitize else [])
+    for src in HIP_SOURCES + (HOST_SOURCES if sanitize else []):
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        jobs.append((obj, [HIPCC] + HIP_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]))
-    for src in HOST_SOURCES:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        jobs.append((obj, ["g++"] + HOST_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]))
+        jobs.append((obj, [HIPCC] + hip_flags + lang + ["-c", os.path.join(CSRC, src), "-o", obj]))
+    if not sanitize:
+        for src in HOST_SOURCES:
+            obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
+            jobs.append((obj, ["g++"] + HOST_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]))
+    run = _run if verbose else (lambda cmd: subprocess.check_call(cmd, stdout=subprocess.DEVNULL,
+                                                                  stderr=subprocess.DEVNULL))
     workers = max(1, min(len(jobs), len(os.sched_getaffinity(0))))
     with ThreadPoolExecutor(workers) as ex:
-        list(ex.map(lambda job: _run(job[1]), jobs))
+        list(ex.map(lambda job: run(job[1]), jobs))
     objs = [obj for obj, _ in jobs]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = lib_path + ".tmp%d" % os.getpid()
+    run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + (SANITIZE_HOST if sanitize else [])
+        + ["-o", tmp] + objs)
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -13,7 +13,9 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libqgemv.so")
+# QG_LIBRARY names another build of the same library (the host-sanitizer
+# build of the CPU tests); by default the in-tree libqgemv.so.
+LIB_PATH = os.environ.get("QG_LIBRARY") or os.path.join(_PKG, "libqgemv.so")
 
 QG_OK = 0
 QG_ERR_INVALID_ARG = 1
