@@ -596,6 +596,55 @@ def cpu_moe(oracle, cpu, threads, reps, synth):
 
 # --------------------------------------------------------------------- main
 
+def measure_setup(args, torch, Q, synth, name=None):
+    """The workload's step function and its byte counts."""
+    name = name or args.workload
+    if name in ("lm_head_mma", "w8a16_qwen3_14b_tp4_mma", "q4_k2560_mma"):
+        return setup_mma(torch, Q, synth, name, args.m)
+    if name == "lm_head_argmax_fused":
+        return setup_lm_head_argmax_fused(torch, Q, synth)
+    if name == "lm_head_argmax":
+        return setup_lm_head_argmax(torch, Q, synth)
+    if name in ("lm_head", "lm_head_q8g128"):
+        return setup_lm_head(torch, Q, synth, "q8g64" if name == "lm_head" else "q8g128")
+    if name == "moe_experts":
+        return setup_moe(torch, Q, synth)
+    if name == "moe_experts_merged":
+        return setup_moe_merged(torch, Q, synth)
+    if name == "moe_experts_swiglu":
+        return setup_moe_swiglu(torch, Q, synth)
+    return setup_dense(torch, Q, synth, name, args.m)
+
+
+def ab_pairs(args, step, torch):
+    """Interleaved A/B pairs (the adoption rule of the vllm.cpp pull request
+    #1936 commit log: a variant is taken only if it wins at least 4 of 5
+    pairs).  The library reads QG_FORCE_VARIANT at every call, so switching
+    it between rounds switches the launch geometry with everything else
+    held fixed.  Returns per-pair us/step of each arm and B's wins."""
+    a_spec, b_spec = args.ab
+    a_t, b_t = [], []
+
+    def run(spec, offset):
+        if spec:
+            os.environ["QG_FORCE_VARIANT"] = spec
+        else:
+            os.environ.pop("QG_FORCE_VARIANT", None)
+        secs, _ = time_steps(torch, step, args.warmup, args.steps, rounds=1)
+        return secs / args.steps * 1e6
+
+    for p in range(args.pairs):
+        order = [(a_spec, a_t), (b_spec, b_t)] if p % 2 == 0 else [(b_spec, b_t), (a_spec, a_t)]
+        for spec, out in order:
+            out.append(run(spec, p))
+    os.environ.pop("QG_FORCE_VARIANT", None)
+    wins = sum(1 for a, b in zip(a_t, b_t) if b < a)
+    return {"ab": {"workload": args.workload, "m": args.m, "a": a_spec, "b": b_spec,
+                   "a_us_per_step": [round(t, 3) for t in a_t], "b_us_per_step": [round(t, 3) for t in b_t],
+                   "a_median": round(float(np.median(a_t)), 3), "b_median": round(float(np.median(b_t)), 3),
+                   "b_wins": wins, "pairs": args.pairs}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -629,6 +678,14 @@ def main():
                     help="skip timing the other workload beside the headline")
     ap.add_argument("--no-read-stream", dest="read_stream", action="store_false",
                     help="skip timing a plain read of the same bytes per launch")
+    ap.add_argument("--ab", nargs=2, metavar=("A", "B"),
+                    help="interleaved A/B pairs instead of the benchmark line: A and B are "
+                         "QG_FORCE_VARIANT values ('' = the library's own choice); each pair times "
+                         "--steps steps of A then of B (the order alternates between pairs), "
+                         "--pairs times, in one process on one set of inputs")
+    ap.add_argument("--pairs", type=int, default=5)
+    ap.add_argument("--sweep", nargs="+", metavar="SPEC",
+                    help="--ab '' SPEC for each SPEC in turn on one set of inputs (one JSON line each)")
     args = ap.parse_args()
     global HOT, STACKED
     HOT = args.hot
@@ -659,23 +716,7 @@ def main():
 
     def measure(name):
         t0 = time.time()
-        if name in ("lm_head_mma", "w8a16_qwen3_14b_tp4_mma", "q4_k2560_mma"):
-            step, alg, wbytes, launches, info, cpu = setup_mma(torch, Q, synth, name, args.m)
-        elif name == "lm_head_argmax_fused":
-            step, alg, wbytes, launches, info, cpu = setup_lm_head_argmax_fused(torch, Q, synth)
-        elif name == "lm_head_argmax":
-            step, alg, wbytes, launches, info, cpu = setup_lm_head_argmax(torch, Q, synth)
-        elif name in ("lm_head", "lm_head_q8g128"):
-            step, alg, wbytes, launches, info, cpu = setup_lm_head(
-                torch, Q, synth, "q8g64" if name == "lm_head" else "q8g128")
-        elif name == "moe_experts":
-            step, alg, wbytes, launches, info, cpu = setup_moe(torch, Q, synth)
-        elif name == "moe_experts_merged":
-            step, alg, wbytes, launches, info, cpu = setup_moe_merged(torch, Q, synth)
-        elif name == "moe_experts_swiglu":
-            step, alg, wbytes, launches, info, cpu = setup_moe_swiglu(torch, Q, synth)
-        else:
-            step, alg, wbytes, launches, info, cpu = setup_dense(torch, Q, synth, name, args.m)
+        step, alg, wbytes, launches, info, cpu = measure_setup(args, torch, Q, synth, name)
         log("setup %s: %.1f s" % (name, time.time() - t0))
         if args.graph:
             secs, rounds = time_steps_graph(torch, step, args.warmup, args.steps, info.get("period", 1))
@@ -683,6 +724,13 @@ def main():
             secs, rounds = time_steps(torch, step, args.warmup, args.steps)
         return dict(secs=secs, rounds=rounds, alg=alg, wbytes=wbytes, launches=launches, info=info,
                     cpu=cpu)
+
+    if args.ab or args.sweep:
+        step = measure_setup(args, torch, Q, synth)[0]
+        for pair in ([args.ab] if args.ab else [("", spec) for spec in args.sweep]):
+            args.ab = list(pair)
+            print(json.dumps(ab_pairs(args, step, torch)), flush=True)
+        return
 
     head = measure(args.workload)
     secs, steps = head["secs"], args.steps

@@ -371,9 +371,17 @@ qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char *buf, s
  *   contig        1: each wave streams a contiguous run of tiles; 0: waves
  *                 sweep the matrix grid-stride; -1: the default (contiguous
  *                 for grouped calls, grid-stride otherwise).
- *   ring_depth    2 or 4: work items kept in flight per wave; 0: default.
- * Process-wide and sticky until called again with (0, -1, 0); not
- * synchronized with qgemv_* calls made meanwhile on other host threads.
+ *   ring_depth    2 or 4: work items kept in flight per wave, with the
+ *                 activation rows staged in LDS; 1: each lane holds its own
+ *                 units of x in registers and the ring holds one tile (for
+ *                 m = 1 and layouts of 2, 3 or 5 steps per tile and at least
+ *                 16 lanes per row; elsewhere the default); 0: default.
+ * Process-wide and sticky until called again with (0, -1, 0).  The three
+ * values are stored together atomically: a call on another host thread uses
+ * either the old or the new geometry.  The environment variable
+ * QG_FORCE_VARIANT ("waves=N,wpcu=N,contig=0|1,ring=2|4|xr", any subset),
+ * read at every call, does the same with lower precedence; both take
+ * precedence over the library's per-shape policy.
  * Returns QG_ERR_INVALID_ARG (and changes nothing) for values outside these
  * ranges or target_waves above 2^24. */
 qg_status qg_set_launch_override(int64_t target_waves, int32_t contig, int32_t ring_depth);

@@ -242,8 +242,16 @@ def _upload(experts, N, K):
     return buf, stride
 
 
+@pytest.fixture
+def ring(request):
+    Q.set_launch_override(0, -1, request.param)
+    yield request.param
+    Q.set_launch_override()
+
+
+@pytest.mark.parametrize("ring", [0, 1], indirect=True, ids=["default", "x_in_registers"])
 @pytest.mark.parametrize("proj", ["gate", "down"])
-def test_moe_cancelling_groups(proj):
+def test_moe_cancelling_groups(proj, ring):
     n_experts, n_slots = synth.MOE["n_experts"], synth.MOE["n_slots"]
     ids = synth.expert_ids(synth.rng_for(74, 1), n_experts, n_slots)
     ids[0] = n_experts - 1                      # the last expert: 64-bit offset
@@ -270,7 +278,8 @@ def test_moe_cancelling_groups(proj):
     assert np.all(y_gpu[:, zero_rows] == 0.0), "rows of exactly-zero weights must give zero"
 
 
-def test_moe_swiglu_cancelling_groups():
+@pytest.mark.parametrize("ring", [0, 1], indirect=True, ids=["default", "x_in_registers"])
+def test_moe_swiglu_cancelling_groups(ring):
     n_experts, n_slots = synth.MOE["n_experts"], synth.MOE["n_slots"]
     ids = synth.expert_ids(synth.rng_for(74, 2), n_experts, n_slots)
     rng, N, K, zero = _experts("gate", ids, 76)

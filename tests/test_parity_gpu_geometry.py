@@ -1,7 +1,9 @@
 """GPU: the VALU kernels give the same bits under every launch geometry.
 
 qg_set_launch_override changes how tiles map to waves (total wave count,
-contiguous runs or a grid-stride sweep, ring depth 2 or 4).  Each tile is
+contiguous runs or a grid-stride sweep, ring depth 2 or 4, or x held in
+registers with a ring of one tile), and QG_FORCE_VARIANT does the same per
+call.  Each tile is
 computed the same way under any mapping, so every output must equal the
 default launch's bit for bit; the default itself is checked against the
 oracle.  Few waves give each wave hundreds of tiles, which drives the
@@ -24,8 +26,12 @@ THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 CANARY16 = 0x7FAB
 
 # (target_waves, contig, ring_depth); the first entry is the default.
+# ring_depth 1 holds x in registers (where the layout allows it).
 GEOMETRIES = [(0, -1, 0), (1, 1, 2), (1, 0, 4), (3, 0, 4), (7, 1, 4), (64, 0, 2), (4096, 1, 2),
-              (4096, 0, 4)]
+              (4096, 0, 4), (0, -1, 1), (1, 1, 1), (7, 0, 1), (4096, 1, 1)]
+# The same choices through QG_FORCE_VARIANT, which the library reads at every
+# call (the override above must be at its default for it to apply).
+FORCED = ["ring=xr", "waves=5,contig=0,ring=xr", "wpcu=2,contig=1,ring=4", "waves=3,ring=2", "policy=0"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -61,6 +67,12 @@ def over_geometries(run):
         Q.set_launch_override(*geo)
         results.append((geo, run()))
     Q.set_launch_override()
+    for spec in FORCED:
+        os.environ["QG_FORCE_VARIANT"] = spec
+        try:
+            results.append((spec, run()))
+        finally:
+            del os.environ["QG_FORCE_VARIANT"]
     base = results[0][1]
     for geo, r in results[1:]:
         diff = np.argwhere(r != base)

@@ -125,6 +125,8 @@ qg_status run_mma(int fmt, int kind, const void* w_packed, const uint16_t* x, fl
     kp.tiles = L.tiles;
     kp.code_bytes = L.code_bytes;
     kp.meta_tile_bytes = L.meta_tile_bytes;
+    kp.tiles_q = kp.tiles_r = 0;   // set per launch shape
+    kp.inv_cpr = 1.0f / float(K / 8);
     (void)hipGetLastError();
     if (qg::launch_mma_sized(fmt, kp, size_t(m) * size_t(K) * 2, static_cast<hipStream_t>(stream)) !=
         hipSuccess)
@@ -497,12 +499,16 @@ qg_status qg_read_stream(const void* buf, size_t bytes, uint32_t* sink, int32_t 
 qg_status qg_set_launch_override(int64_t target_waves, int32_t contig, int32_t ring_depth)
 {
     if (target_waves < 0 || target_waves > (int64_t(1) << 24) || contig < -1 || contig > 1 ||
-        (ring_depth != 0 && ring_depth != 2 && ring_depth != 4))
+        (ring_depth != 0 && ring_depth != 1 && ring_depth != 2 && ring_depth != 4))
         return QG_ERR_INVALID_ARG;
     qg::LaunchOverride o;
+    o.use_policy = 1;
     o.target_waves = target_waves;
     o.contig = contig;
-    o.shape = ring_depth == 2 ? qg::SHAPE_D2_W4 : ring_depth == 4 ? qg::SHAPE_D4_W4 : -1;
+    o.shape = ring_depth == 2   ? qg::SHAPE_D2_W4
+              : ring_depth == 4 ? qg::SHAPE_D4_W4
+              : ring_depth == 1 ? qg::SHAPE_XR
+                                : -1;
     qg::set_launch_override(o);
     return QG_OK;
 }

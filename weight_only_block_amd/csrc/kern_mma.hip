@@ -153,7 +153,8 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
         j_lo = G * wave / KSPLIT * SPG;
         j_hi = G * (wave + 1) / KSPLIT * SPG;
     }
-    const int64_t my_tiles = gw < p.tiles ? (p.tiles - 1 - gw) / W + 1 : 0;
+    // tiles = q W + r (from the host): no division on the way to the first load.
+    const int64_t my_tiles = p.tiles_q + (gw < p.tiles_r ? 1 : 0);
     const int64_t n_items = my_tiles * (j_hi - j_lo);
 
     const uint8_t* code_lane = p.w + lane * 16;
@@ -216,13 +217,21 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
     // batches also wait for the ring.  Chunks are XOR-swizzled in LDS.
     constexpr int kXBatch = 8;
     const int x_total = XG ? 0 : m * cpr;
+    // Row of a flattened chunk index (< m * cpr, far below 2^20): a float
+    // reciprocal and one correction instead of an emulated integer division.
+    auto row_of_chunk = [&](int idx) {
+        int q = int(float(idx) * p.inv_cpr);
+        if (q * cpr > idx) --q;
+        else if ((q + 1) * cpr <= idx) ++q;
+        return q;
+    };
     u32x4 xv[kXBatch];
     auto x_load = [&](int base) {
 #pragma unroll
         for (int b = 0; b < kXBatch; ++b) {
             const int idx = base + b * kThreads + int(threadIdx.x);
             if (idx < x_total) {
-                const int i = idx / cpr, c = idx - i * cpr;
+                const int i = row_of_chunk(idx), c = idx - i * cpr;
                 xv[b] = load_x16(p.x + int64_t(i) * p.ldx + c * 8);
             }
         }
@@ -232,7 +241,7 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
         for (int b = 0; b < kXBatch; ++b) {
             const int idx = base + b * kThreads + int(threadIdx.x);
             if (idx < x_total) {
-                const int i = idx / cpr, c = idx - i * cpr;
+                const int i = row_of_chunk(idx), c = idx - i * cpr;
                 xs[xs_chunk(i, c, cpr)] = xv[b];
             }
         }
@@ -395,7 +404,13 @@ hipError_t launch_fmt(const MmaParams& kp, int64_t waves, size_t lds, hipStream_
     if (attr != hipSuccess && lds > 64 * 1024) return attr;
     constexpr int threads = mma_threads<KSPLIT>();
     const int64_t wpg = threads / 64;
-    hipLaunchKernelGGL(kern, dim3(unsigned((waves + wpg - 1) / wpg)), dim3(threads), lds, s, kp);
+    const unsigned blocks = unsigned((waves + wpg - 1) / wpg);
+    // Tile streams: one per wave, or one per work-group with a K split.
+    MmaParams k = kp;
+    const int64_t W = KSPLIT == 1 ? int64_t(blocks) * wpg : int64_t(blocks);
+    k.tiles_q = kp.tiles / W;
+    k.tiles_r = kp.tiles % W;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), lds, s, k);
     return hipGetLastError();
 }
 

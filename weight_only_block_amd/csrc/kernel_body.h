@@ -227,6 +227,18 @@ __device__ __forceinline__ void q4_pairs_centred(const u32x4& c, int z, uint32_t
 constexpr float kQ4Kappa = 6810.0f / 16777216.0f;
 constexpr float kQ4MinWeight = 1.0f / 256.0f;
 
+// q = n / d for 0 <= n < 2^20 and d >= 1, from a float reciprocal of d
+// (inv_d = 1.0f / d, from the host) and one correction step: the product is
+// within one of the quotient, and a runtime integer division would be a long
+// emulated sequence.
+__device__ __forceinline__ int div_small(int n, int d, float inv_d)
+{
+    int q = int(float(n) * inv_d);
+    if (q * d > n) --q;
+    else if ((q + 1) * d <= n) ++q;
+    return q;
+}
+
 // x rows -> LDS as bf16 pairs; for Q4G32 also, per unit (group) u of row
 // i, X = sum x at xsum[2 (i U + u)] and kappa * sum |x| (kQ4Kappa) at
 // xsum[2 (i U + u) + 1].
@@ -247,16 +259,17 @@ struct XStage {
     __device__ __forceinline__ void load_unit(const KernelParams& p, const uint16_t* x, int idx, int U)
     {
         // 4-byte loads: x rows only need 4-byte alignment, and x is read
-        // once per work-group (from L2 after the first work-group).
-        const int i = idx / U, u = idx - i * U;
+        // once per work-group (from L2 after the first work-group).  With one
+        // row, idx is the unit.
+        const int i = M == 1 ? 0 : div_small(idx, U, p.inv_U), u = idx - i * U;
         const uint32_t* src = reinterpret_cast<const uint32_t*>(x + int64_t(i) * p.ldx + u * (2 * UD));
 #pragma unroll
         for (int d = 0; d < UD; ++d) v[d] = src[d];
     }
 
-    __device__ __forceinline__ void store_unit(uint32_t* xs, float* xsum, int idx, int KD, int U)
+    __device__ __forceinline__ void store_unit(uint32_t* xs, float* xsum, int idx, int KD, int U, float inv_U)
     {
-        const int i = idx / U, u = idx - i * U;
+        const int i = M == 1 ? 0 : div_small(idx, U, inv_U), u = idx - i * U;
         u32x4* dst = reinterpret_cast<u32x4*>(xs + i * KD + u * UD);
 #pragma unroll
         for (int q = 0; q < UD / 4; ++q) {
@@ -290,9 +303,9 @@ struct XStage {
     }
 
     // Stores the unit fetched first.
-    __device__ __forceinline__ void finish_first(uint32_t* xs, float* xsum, int KD, int U)
+    __device__ __forceinline__ void finish_first(uint32_t* xs, float* xsum, int KD, int U, float inv_U)
     {
-        if (first < M * U) store_unit(xs, xsum, first, KD, U);
+        if (first < M * U) store_unit(xs, xsum, first, KD, U, inv_U);
     }
 
     // Loads and stores the units past the first (only when M*U > threads).
@@ -301,7 +314,65 @@ struct XStage {
     {
         for (int idx = first + THREADS; idx < M * U; idx += THREADS) {
             load_unit(p, x, idx, U);
-            store_unit(xs, xsum, idx, KD, U);
+            store_unit(xs, xsum, idx, KD, U, p.inv_U);
+        }
+    }
+};
+
+// x held in registers instead of LDS (launches whose rows have few units
+// per lane: J = U / G steps per tile).  Lane g of a row group uses only the
+// units j G + g, j < J, of each activation row, in every tile it streams, so
+// it loads those J units once, straight from memory (L2 after the first
+// wave), and no work-group staging, barrier or LDS read is needed.  The
+// Q4G32 sums X and kappa * sum |x| are formed exactly as XStage forms them.
+template <int FMT, int M, int J>
+struct XRegs {
+    static constexpr int UD = FMT == FMT_Q4G32 ? 16 : 8;   // dwords per unit
+    uint32_t v[J][M][UD];
+    float X[J][M], XA[J][M];                               // Q4G32 only
+
+    __device__ __forceinline__ void load(const KernelParams& p, const uint16_t* x, int g, int G)
+    {
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int i = 0; i < M; ++i) {
+                const uint16_t* src = x + int64_t(i) * p.ldx + (j * G + g) * (2 * UD);
+                if (p.x_vec16) {
+                    // 16-byte loads where x, its row stride and its slot
+                    // stride allow them (the same in every lane).
+#pragma unroll
+                    for (int q = 0; q < UD / 4; ++q) {
+                        const u32x4 t = *reinterpret_cast<const u32x4*>(src + 8 * q);
+                        v[j][i][4 * q] = t.x; v[j][i][4 * q + 1] = t.y;
+                        v[j][i][4 * q + 2] = t.z; v[j][i][4 * q + 3] = t.w;
+                    }
+                } else {
+                    const uint32_t* s4 = reinterpret_cast<const uint32_t*>(src);
+#pragma unroll
+                    for (int d = 0; d < UD; ++d) v[j][i][d] = s4[d];
+                }
+            }
+    }
+
+    __device__ __forceinline__ void sums()
+    {
+        if constexpr (FMT == FMT_Q4G32) {
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+#pragma unroll
+                for (int i = 0; i < M; ++i) {
+                    float X0 = 0.0f, X1 = 0.0f, A0 = 0.0f, A1 = 0.0f;
+#pragma unroll
+                    for (int d = 0; d < UD / 2; ++d) {
+                        X0 = dot2(v[j][i][d], kOnesBf16x2, X0);
+                        X1 = dot2(v[j][i][d + UD / 2], kOnesBf16x2, X1);
+                        A0 = dot2(v[j][i][d] & 0x7fff7fffu, kOnesBf16x2, A0);
+                        A1 = dot2(v[j][i][d + UD / 2] & 0x7fff7fffu, kOnesBf16x2, A1);
+                    }
+                    X[j][i] = X0 + X1;
+                    XA[j][i] = kQ4Kappa * (A0 + A1);
+                }
         }
     }
 };
@@ -342,31 +413,13 @@ struct Cert {
     }
 };
 
-template <int FMT, int M, int R, int META_BYTES>
-__device__ __forceinline__ void consume(const Item<R, META_BYTES>& it, const uint32_t* xs,
-                                        const float* xsum, int KD, int U, int u, const Q4Consts& k4,
-                                        float T, float (&acc)[R][M], Cert<FMT, M, R>& cert)
+// One item against one unit of each activation row: xd holds the unit's x
+// pairs, X and XA its Q4 sums (X = sum x, XA = kappa * sum |x|).
+template <int FMT, int M, int R, int META_BYTES, int UD>
+__device__ __forceinline__ void consume_x(const Item<R, META_BYTES>& it, const uint32_t (&xd)[M][UD],
+                                          const float (&X)[M], const float (&XA)[M], const Q4Consts& k4,
+                                          float T, float (&acc)[R][M], Cert<FMT, M, R>& cert)
 {
-    constexpr int UD = FMT == FMT_Q4G32 ? 16 : 8;
-    uint32_t xd[M][UD];
-    float X[M], XA[M];
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(xs + i * KD + u * UD);
-#pragma unroll
-        for (int q = 0; q < UD / 4; ++q) {
-            const u32x4 v = src[q];
-            xd[i][4 * q] = v.x; xd[i][4 * q + 1] = v.y;
-            xd[i][4 * q + 2] = v.z; xd[i][4 * q + 3] = v.w;
-        }
-        if constexpr (FMT == FMT_Q4G32) {
-            const float2 xa = reinterpret_cast<const float2*>(xsum)[i * U + u];
-            X[i] = xa.x;
-            XA[i] = xa.y;
-        } else {
-            X[i] = XA[i] = 0.0f;
-        }
-    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         if constexpr (FMT != FMT_Q4G32) {
@@ -409,8 +462,58 @@ __device__ __forceinline__ void consume(const Item<R, META_BYTES>& it, const uin
     }
 }
 
+// The same with the unit's x read from the work-group's LDS copy.
+template <int FMT, int M, int R, int META_BYTES>
+__device__ __forceinline__ void consume(const Item<R, META_BYTES>& it, const uint32_t* xs,
+                                        const float* xsum, int KD, int U, int u, const Q4Consts& k4,
+                                        float T, float (&acc)[R][M], Cert<FMT, M, R>& cert)
+{
+    constexpr int UD = FMT == FMT_Q4G32 ? 16 : 8;
+    uint32_t xd[M][UD];
+    float X[M], XA[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(xs + i * KD + u * UD);
+#pragma unroll
+        for (int q = 0; q < UD / 4; ++q) {
+            const u32x4 v = src[q];
+            xd[i][4 * q] = v.x; xd[i][4 * q + 1] = v.y;
+            xd[i][4 * q + 2] = v.z; xd[i][4 * q + 3] = v.w;
+        }
+        if constexpr (FMT == FMT_Q4G32) {
+            const float2 xa = reinterpret_cast<const float2*>(xsum)[i * U + u];
+            X[i] = xa.x;
+            XA[i] = xa.y;
+        } else {
+            X[i] = XA[i] = 0.0f;
+        }
+    }
+    consume_x<FMT, M, R, META_BYTES, UD>(it, xd, X, XA, k4, T, acc, cert);
+}
+
 // The certificate's fallback: one item of a Q4 tile, decoded exactly (each
-// group re-centred on its integer zero point z, see q4_group).
+// group re-centred on its integer zero point z, see q4_group), against x
+// pairs xd and sums X of one unit per activation row.
+template <int M, int R, int META_BYTES>
+__device__ __forceinline__ void consume_centred_x(const Item<R, META_BYTES>& it, const uint32_t (&xd)[M][16],
+                                                  const float (&X)[M], float (&acc)[R][M])
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const Q4Group q = q4_group(it.m.w[r]);
+        uint32_t pr[16];
+        q4_pairs_centred(it.c[r], q.z, pr);
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            float D = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) D = dot2(pr[t], xd[i][t], D);
+            acc[r][i] = fmaf(q.s, D, acc[r][i]);
+            acc[r][i] = fmaf(q.mp, X[i], acc[r][i]);
+        }
+    }
+}
+
 template <int M, int R, int META_BYTES>
 __device__ __forceinline__ void consume_centred(const Item<R, META_BYTES>& it, const uint32_t* xs,
                                                 const float* xsum, int KD, int U, int u,
@@ -429,20 +532,7 @@ __device__ __forceinline__ void consume_centred(const Item<R, META_BYTES>& it, c
         }
         X[i] = reinterpret_cast<const float2*>(xsum)[i * U + u].x;
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const Q4Group q = q4_group(it.m.w[r]);
-        uint32_t pr[16];
-        q4_pairs_centred(it.c[r], q.z, pr);
-#pragma unroll
-        for (int i = 0; i < M; ++i) {
-            float D = 0.0f;
-#pragma unroll
-            for (int t = 0; t < 16; ++t) D = dot2(pr[t], xd[i][t], D);
-            acc[r][i] = fmaf(q.s, D, acc[r][i]);
-            acc[r][i] = fmaf(q.mp, X[i], acc[r][i]);
-        }
-    }
+    consume_centred_x<M, R, META_BYTES>(it, xd, X, acc);
 }
 
 __device__ __forceinline__ float dpp_add(float v, int ctrl_sel)
@@ -618,6 +708,24 @@ __device__ __forceinline__ void q4_recompute_tile(float (&acc)[R][M], const Kern
     }
 }
 
+// The same with x held in registers (J steps per tile, known at compile time).
+template <int M, int R, int META_BYTES, int J>
+__device__ __forceinline__ void q4_recompute_tile_xr(float (&acc)[R][M], const KernelParams& p,
+                                                     const uint8_t* code_lane, const uint8_t* meta_lane,
+                                                     int64_t tile, const XRegs<FMT_Q4G32, M, J>& xr)
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < M; ++i) acc[r][i] = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) {
+        Item<R, META_BYTES> it;
+        it.load(code_lane, meta_lane, tile * J + jj, tile, p);
+        consume_centred_x<M, R, META_BYTES>(it, xr.v[jj], xr.X[jj], acc);
+    }
+}
+
 // fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t to_bf16(float v)
 {
@@ -770,9 +878,13 @@ __device__ __forceinline__ void finish_argmax(uint64_t (&best)[M], const KernelP
 // EPI 0 stores fp32 sums; EPI 1 is the SwiGLU epilogue over gate/up pairs
 // (grouped Q4G32, m = 1 only); EPI 2 is the greedy argmax epilogue (dense,
 // logits store optional).
-template <int FMT, int M, int G, int R, int DEPTH, int WAVES, bool GROUPED, int EPI>
+template <int FMT, int M, int G, int R, int DEPTH, int WAVES, bool GROUPED, int EPI, int XRJ>
 __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
 {
+    // XRJ > 0: x in registers (XRegs) for rows of exactly XRJ steps per tile;
+    // the ring then holds whole tiles, so each slot always holds the same
+    // step and indexes x at compile time.
+    static_assert(XRJ == 0 || DEPTH % XRJ == 0, "with x in registers the ring holds whole tiles");
     constexpr int kWaves = WAVES;
     constexpr int kThreads = 64 * WAVES;
     extern __shared__ __align__(16) uint32_t lds[];
@@ -807,9 +919,12 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
         tstep = 1;
         my_tiles = t0 < p.tiles ? (p.tiles - t0 < p.contig_k ? p.tiles - t0 : p.contig_k) : 0;
     } else {
+        // Tiles gw, gw + W, ... below p.tiles: the host passes tiles = q W + r
+        // for this grid, so the count needs no division here (a 64-bit
+        // division is a long emulated sequence on the way to the first load).
         t0 = gw;
         tstep = W;
-        my_tiles = gw < p.tiles ? (p.tiles - 1 - gw) / W + 1 : 0;
+        my_tiles = p.tiles_q + (gw < p.tiles_r ? 1 : 0);
     }
     static_assert(EPI != 1 || (FMT == FMT_Q4G32 && M == 1 && GROUPED && R == 2),
                   "the SwiGLU epilogue is built for grouped Q4G32 gate/up pairs");
@@ -823,7 +938,9 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     // weight ring is issued, so the x loads go out while the id is in
     // flight instead of waiting behind it.
     XStage<FMT, M, kThreads> xstage;
-    xstage.fetch(p, x, U);
+    XRegs<FMT, M, (XRJ > 0 ? XRJ : 1)> xr;
+    if constexpr (XRJ > 0) xr.load(p, x, g, G);
+    else xstage.fetch(p, x, U);
 
     const uint8_t* w = p.w;
     bool bad_expert = false;
@@ -869,19 +986,27 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
             }                                                                                 \
         }                                                                                     \
     } while (0)
-    if (M * U <= kThreads) {
-        // One x unit per thread at most: it was fetched first; finish staging
-        // it while the weights are in flight.
+    if constexpr (XRJ > 0) {
+        // The lane's own x units were loaded first; their sums wait for x
+        // alone while the weights are in flight.  No barrier: nothing is
+        // shared through LDS.
         QG_FILL_RING();
-        xstage.finish_first(xs, xsum, KD, U);
+        xr.sums();
     } else {
-        // Long activations: stage all of x, then start the weight stream.
-        xstage.finish_first(xs, xsum, KD, U);
-        xstage.finish_rest(p, x, xs, xsum, KD, U);
-        QG_FILL_RING();
+        if (M * U <= kThreads) {
+            // One x unit per thread at most: it was fetched first; finish
+            // staging it while the weights are in flight.
+            QG_FILL_RING();
+            xstage.finish_first(xs, xsum, KD, U, p.inv_U);
+        } else {
+            // Long activations: stage all of x, then start the weight stream.
+            xstage.finish_first(xs, xsum, KD, U, p.inv_U);
+            xstage.finish_rest(p, x, xs, xsum, KD, U);
+            QG_FILL_RING();
+        }
+        __syncthreads();
     }
 #undef QG_FILL_RING
-    __syncthreads();
     if (GROUPED && bad_expert) {
         for (int64_t n = 0, t = t0; n < my_tiles; ++n, t += tstep) {
             if constexpr (EPI == 1) {
@@ -919,15 +1044,26 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     int64_t tile = t0, j = 0;
 #define QG_CONSUME(slot_)                                                                     \
     do {                                                                                      \
-        consume<FMT, M, R, META_BYTES>(ring[slot_], xs, xsum, KD, U, int(j) * G + g, k4, p.cert_t, acc, cert); \
+        if constexpr (XRJ > 0)                                                                \
+            consume_x<FMT, M, R, META_BYTES, XRegs<FMT, M, 1>::UD>(                           \
+                ring[slot_], xr.v[(slot_) % XRJ], xr.X[(slot_) % XRJ], xr.XA[(slot_) % XRJ], k4, \
+                p.cert_t, acc, cert);                                                         \
+        else                                                                                  \
+            consume<FMT, M, R, META_BYTES>(ring[slot_], xs, xsum, KD, U, int(j) * G + g, k4,  \
+                                           p.cert_t, acc, cert);                              \
     } while (0)
 #define QG_ADVANCE()                                                                          \
     do {                                                                                      \
         if (++j == p.J) {                                                                     \
             if constexpr (FMT == FMT_Q4G32) {                                                 \
-                if (__builtin_expect(!q4_tile_certified<M, G, R>(cert, g), 0))                \
-                    q4_recompute_tile<M, G, R, META_BYTES>(acc, p, code_lane, meta_lane, tile, xs, \
-                                                           xsum, KD, U, g);                   \
+                if (__builtin_expect(!q4_tile_certified<M, G, R>(cert, g), 0)) {              \
+                    if constexpr (XRJ > 0)                                                    \
+                        q4_recompute_tile_xr<M, R, META_BYTES, (XRJ > 0 ? XRJ : 1)>(          \
+                            acc, p, code_lane, meta_lane, tile, xr);                          \
+                    else                                                                      \
+                        q4_recompute_tile<M, G, R, META_BYTES>(acc, p, code_lane, meta_lane,  \
+                                                               tile, xs, xsum, KD, U, g);     \
+                }                                                                             \
             }                                                                                 \
             if constexpr (EPI == 1) {                                                         \
                 swb.add(acc, tile, lane);                                                     \
@@ -978,11 +1114,11 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
 
 // Launch shape (launch.h): ring depth 2 or 4; work-groups are 4 waves.
 
-template <int FMT, int M, int G, int DEPTH, int WAVES, bool GROUPED, int EPI>
+template <int FMT, int M, int G, int DEPTH, int WAVES, bool GROUPED, int EPI, int XRJ = 0>
 hipError_t launch_variant(const KernelParams& kp, int64_t waves, int slots, size_t lds_bytes,
                           hipStream_t stream)
 {
-    auto kern = qgemv_stream<FMT, M, G, kRowSlots, DEPTH, WAVES, GROUPED, EPI>;
+    auto kern = qgemv_stream<FMT, M, G, kRowSlots, DEPTH, WAVES, GROUPED, EPI, XRJ>;
     // Raise the dynamic-LDS limit once per kernel (static LDS is within the
     // reserve).  A failure is not left behind as the launch's error; it only
     // matters to launches that need more than the default 64 KiB.
@@ -995,7 +1131,13 @@ hipError_t launch_variant(const KernelParams& kp, int64_t waves, int slots, size
     }();
     if (attr != hipSuccess && lds_bytes > 64 * 1024) return attr;
     const dim3 grid(unsigned((waves + WAVES - 1) / WAVES), unsigned(slots));
-    hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), lds_bytes, stream, kp);
+    // The grid-stride share of each wave: tiles = q W + r for the W waves
+    // of a slot (the kernel adds 1 for waves below r).
+    KernelParams k = kp;
+    const int64_t W = int64_t(grid.x) * WAVES;
+    k.tiles_q = kp.tiles / W;
+    k.tiles_r = kp.tiles % W;
+    hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), lds_bytes, stream, k);
     return hipGetLastError();
 }
 
@@ -1006,8 +1148,24 @@ hipError_t launch_shape(int shape, const KernelParams& kp, int64_t waves, int sl
     switch (shape) {
     case SHAPE_D2_W4: return launch_variant<FMT, M, G, 2, 4, GROUPED, EPI>(kp, waves, slots, lds, s);
     case SHAPE_D4_W4: return launch_variant<FMT, M, G, 4, 4, GROUPED, EPI>(kp, waves, slots, lds, s);
-    default: return hipErrorInvalidValue;
+    default: break;
     }
+    // x in registers: built for one activation row, lane groups of 16..64
+    // lanes and 2, 3 or 5 steps per tile (the ring holds one tile).
+    if constexpr (M == 1 && G >= 16) {
+        switch (shape) {
+        case SHAPE_XR:
+            switch (kp.J) {
+            case 2: return launch_variant<FMT, M, G, 2, 4, GROUPED, EPI, 2>(kp, waves, slots, 0, s);
+            case 3: return launch_variant<FMT, M, G, 3, 4, GROUPED, EPI, 3>(kp, waves, slots, 0, s);
+            case 5: return launch_variant<FMT, M, G, 5, 4, GROUPED, EPI, 5>(kp, waves, slots, 0, s);
+            default: break;
+            }
+            break;
+        default: break;
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int FMT, int M, bool GROUPED, int EPI>

@@ -31,6 +31,7 @@ struct KernelParams {
     int64_t y_slot_stride;     // elements between slot outputs
     int64_t J;                 // steps per tile
     int64_t tiles;
+    int64_t tiles_q, tiles_r;  // grid-stride mapping: tiles = tiles_q * waves + tiles_r
     int64_t code_bytes;        // offset of the meta blocks
     int64_t meta_step_bytes;
     int64_t meta_tile_bytes;   // per-tile meta after the steps' meta (Q8PC row scales)
@@ -42,6 +43,8 @@ struct KernelParams {
     unsigned long long* keys;  // argmax epilogue: one key per row (zero between calls)
     unsigned int* counter;     // argmax epilogue: finished work-groups (zero between calls)
     float cert_t;              // Q4G32: certificate threshold T (q4_cert_threshold)
+    int32_t x_vec16;           // x in registers: x, ldx and x_slot_stride allow 16-byte loads
+    float inv_U;               // 1.0f / (units per row), for the staging's row index
 };
 
 // Threshold T of the Q4G32 fast path's certificate (kernel_body.h,
@@ -62,8 +65,16 @@ inline float q4_cert_threshold(int64_t J)
     return float(t * (1.0 - 4.0 * double(J + 7) * u) - 1e-6);
 }
 
-// Launch shape: ring depth 2 or 4 items; work-groups are 4 waves.
-enum Shape { SHAPE_D2_W4 = 0, SHAPE_D4_W4 = 1 };
+// Launch shape: ring depth 2 or 4 items with x staged in LDS; or x held in
+// registers with a ring of one tile (J = 2, 3 or 5 steps, m = 1, G >= 16).
+// Work-groups are 4 waves.
+enum Shape { SHAPE_D2_W4 = 0, SHAPE_D4_W4 = 1, SHAPE_XR = 2 };
+
+// Whether a layout can take the x-in-registers kernel (m activation rows).
+inline bool xr_supported(const Layout& L, int m)
+{
+    return m == 1 && L.G >= 16 && (L.J == 2 || L.J == 3 || L.J == 5);
+}
 
 struct LaunchArgs {
     Layout layout;
@@ -95,7 +106,8 @@ struct LaunchArgs {
 struct LaunchOverride {
     int64_t target_waves;  // > 0: about this many waves in total
     int contig;            // 1: contiguous tile runs per wave, 0: grid-stride, -1: default
-    int shape;             // SHAPE_D2_W4 / SHAPE_D4_W4, -1: default
+    int shape;             // SHAPE_D2_W4 / SHAPE_D4_W4 / SHAPE_XR, -1: default
+    int use_policy = 1;    // 0: leave out the exact-shape policy (QG_FORCE_VARIANT only)
 };
 void set_launch_override(const LaunchOverride& o);
 
@@ -125,6 +137,8 @@ struct MmaParams {
     int32_t m;
     int32_t N;
     int64_t K, J, tiles, code_bytes, meta_tile_bytes;
+    int64_t tiles_q, tiles_r;  // tiles = tiles_q * W + tiles_r for the launch's W tile streams
+    float inv_cpr;             // 1.0f / (16-byte chunks per activation row), for the staging
 };
 // ksplit: 1 (each wave streams whole tiles), 4 or 16 (the waves of a
 // work-group share each tile's K).  xg (with ksplit 4): x is read from

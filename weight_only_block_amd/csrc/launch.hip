@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <string.h>
+
 #include <atomic>
 
 #include "launch.h"
@@ -22,14 +24,131 @@ constexpr int64_t kWavesPerCuDenseMulti = 8;
 constexpr int64_t kWavesPerCuGrouped = 8;
 }  // namespace
 
-// Launch-geometry override (qg_set_launch_override): 0 / -1 leave the
-// choice to the environment (QG_TARGET_WAVES, QG_CONTIG, QG_SHAPE, read once,
-// for tuning sweeps) and then to the defaults below.
-static LaunchOverride g_override = {0, -1, -1};
+// Launch-geometry override (qg_set_launch_override), process-wide.  The
+// three fields are packed into one atomic word, so a call made while
+// another thread changes the override sees either the old or the new
+// geometry, never a mix: target_waves in bits 0..39, contig + 1 in bits
+// 40..41, shape + 1 in bits 42..44.
+static std::atomic<uint64_t> g_override_word{(uint64_t(0) << 40) | (uint64_t(0) << 42)};
 
 void set_launch_override(const LaunchOverride& o)
 {
-    g_override = o;
+    const uint64_t w = (uint64_t(o.target_waves) & ((uint64_t(1) << 40) - 1)) |
+                       (uint64_t(o.contig + 1) << 40) | (uint64_t(o.shape + 1) << 42);
+    g_override_word.store(w, std::memory_order_relaxed);
+}
+
+static LaunchOverride current_override()
+{
+    const uint64_t w = g_override_word.load(std::memory_order_relaxed);
+    LaunchOverride o;
+    o.target_waves = int64_t(w & ((uint64_t(1) << 40) - 1));
+    o.contig = int((w >> 40) & 3) - 1;
+    o.shape = int((w >> 42) & 7) - 1;
+    o.use_policy = 1;
+    return o;
+}
+
+// QG_FORCE_VARIANT, read at every call (so that an A/B run and graph
+// capture in one process pick up a change at the next call, as the per-call
+// environment knobs of the vllm.cpp pull request #1936 commit log): a comma
+// list of waves=<total waves>, wpcu=<waves per compute unit>, contig=0|1 and
+// ring=2|4|xr (xr: x in registers, where the layout allows it), optionally
+// restricted to one shape with n=<N>, k=<K> and m=<m> (calls of other
+// shapes are then not forced), and policy=0 to leave out the exact-shape
+// policy below (for A/B runs of the policy itself).  Unknown keys and bad
+// values are ignored; an unset or empty variable forces nothing.
+static LaunchOverride forced_variant(int64_t cus, int64_t N, int64_t K, int m)
+{
+    LaunchOverride o = {0, -1, -1, 1};
+    const char* e = getenv("QG_FORCE_VARIANT");
+    if (!e) return o;
+    bool other_shape = false;
+    o.use_policy = 1;
+    while (*e) {
+        const char* eq = strchr(e, '=');
+        if (!eq) break;
+        const char* end = strchr(eq, ',');
+        const size_t klen = size_t(eq - e);
+        char* stop = nullptr;
+        const long v = strtol(eq + 1, &stop, 10);
+        const bool num = stop != eq + 1 && (stop == end || (!end && *stop == 0));
+        if (klen == 5 && !strncmp(e, "waves", 5) && num && v > 0 && v <= (1L << 24)) o.target_waves = v;
+        else if (klen == 4 && !strncmp(e, "wpcu", 4) && num && v > 0 && v <= 64) o.target_waves = v * cus;
+        else if (klen == 6 && !strncmp(e, "contig", 6) && num && (v == 0 || v == 1)) o.contig = int(v);
+        else if (klen == 1 && e[0] == 'n' && num && v != N) other_shape = true;
+        else if (klen == 1 && e[0] == 'k' && num && v != K) other_shape = true;
+        else if (klen == 1 && e[0] == 'm' && num && v != m) other_shape = true;
+        else if (klen == 6 && !strncmp(e, "policy", 6) && num && (v == 0 || v == 1)) o.use_policy = int(v);
+        else if (klen == 4 && !strncmp(e, "ring", 4)) {
+            if (num && v == 2) o.shape = SHAPE_D2_W4;
+            else if (num && v == 4) o.shape = SHAPE_D4_W4;
+            else if (!strncmp(eq + 1, "xr", 2) && (eq[3] == ',' || eq[3] == 0)) o.shape = SHAPE_XR;
+        }
+        if (!end) break;
+        e = end + 1;
+    }
+    if (other_shape) return LaunchOverride{0, -1, -1, 1};
+    return o;
+}
+
+// Exact-shape launch policy: geometries that measured faster than the
+// defaults below for one (format, m, N, K, grouped) shape, each admitted by
+// interleaved A/B pairs (the evidence is recorded with the measurements);
+// every other shape takes the defaults.  This is the per-shape, measured
+// operator policy of the MetaInfer-cpp README (milestone M6.5-E,
+// MeasuredOperatorPolicy), for launch geometry.
+struct ShapePolicy {
+    int fmt, m;
+    int64_t N, K;
+    bool grouped;
+    int64_t waves_per_cu;   // 0: default
+    int contig;             // -1: default
+    int shape;              // -1: default
+};
+// Entries were admitted on MI355X by interleaved pairs in one process
+// (bench.py --sweep, 500 steps per arm, five pairs): at least 4 of 5 pairs
+// won and a median gain of at least 0.5%.  Medians are us per step of the
+// workload the shape belongs to, default -> entry.
+static const ShapePolicy kPolicy[] = {
+    // Q4G32 K=2560 family, m = 1: ring 2 + contiguous 21.45 -> 20.36 (5/5)
+    {FMT_Q4G32, 1, 9216, 2560, false, 0, 1, SHAPE_D2_W4},
+    // contiguous 21.44 -> 21.20 (5/5)
+    {FMT_Q4G32, 1, 2560, 9216, false, 0, 1, -1},
+    // m = 4: ring 2 34.60 -> 34.22 (5/5)
+    {FMT_Q4G32, 4, 9216, 2560, false, 0, -1, SHAPE_D2_W4},
+    // Qwen3-14B TP4 W8A16 layer, m = 1: contiguous 37.69 -> 37.50 (5/5)
+    {FMT_Q8PC, 1, 1792, 5120, false, 0, 1, -1},
+    // contiguous 37.67 -> 37.48 (5/5)
+    {FMT_Q8PC, 1, 5120, 1280, false, 0, 1, -1},
+    // x in registers + contiguous 37.74 -> 37.49 (5/5)
+    {FMT_Q8PC, 1, 8704, 5120, false, 0, 1, SHAPE_XR},
+    // contiguous 37.71 -> 37.58 (5/5)
+    {FMT_Q8PC, 1, 5120, 4352, false, 0, 1, -1},
+    // m = 4: ring 2 53.80 -> 53.40 (5/5) and 53.80 -> 52.50 (5/5)
+    {FMT_Q8PC, 4, 1792, 5120, false, 0, -1, SHAPE_D2_W4},
+    {FMT_Q8PC, 4, 8704, 5120, false, 0, -1, SHAPE_D2_W4},
+    // Qwen3-0.6B-shaped layer: x in registers 30.55 -> 30.35 (4/5),
+    // ring 2 30.33 -> 30.13 (4/5), x in registers 30.38 -> 30.19 (4/5)
+    {FMT_Q8G64, 1, 1024, 2048, false, 0, -1, SHAPE_XR},
+    {FMT_Q8G64, 1, 3072, 1024, false, 0, -1, SHAPE_D2_W4},
+    {FMT_Q8G64, 1, 1024, 3072, false, 0, -1, SHAPE_XR},
+    // Routed experts (8 of 128): x in registers, three-call flow 24.50 ->
+    // 24.02 (gate/up, 5/5) and 24.45 -> 24.19 (down, 5/5); merged flow
+    // (down) 20.80 -> 20.58 (5/5), merged gate+up 20.75 -> 20.62 (4/5)
+    {FMT_Q4G32, 1, 1536, 4096, true, 0, -1, SHAPE_XR},
+    {FMT_Q4G32, 1, 4096, 1536, true, 0, -1, SHAPE_XR},
+    {FMT_Q4G32, 1, 3072, 4096, true, 0, -1, SHAPE_XR},
+    {-1, 0, 0, 0, false, 0, -1, -1},   // (end)
+};
+
+static const ShapePolicy* policy_for(int fmt, int m, int64_t N, int64_t K, bool grouped)
+{
+    for (const ShapePolicy& e : kPolicy) {
+        if (e.fmt < 0) break;
+        if (e.fmt == fmt && e.m == m && e.N == N && e.K == K && e.grouped == grouped) return &e;
+    }
+    return nullptr;
 }
 
 // Compute units of the current device, looked up once per device.
@@ -87,22 +206,36 @@ hipError_t launch(const LaunchArgs& a)
     kp.keys = static_cast<unsigned long long*>(a.argmax_workspace);
     kp.counter = a.argmax_workspace ? reinterpret_cast<unsigned int*>(kp.keys + a.m) : nullptr;
     kp.cert_t = q4_cert_threshold(L.J);
+    kp.inv_U = 1.0f / float(L.U);
     const int slots = a.grouped ? a.n_slots : 1;
-    // About target_waves waves in total (QG_TARGET_WAVES overrides it, for
-    // tuning sweeps), never more waves than tiles; k tiles per wave, then the
-    // fewest waves that cover the tiles with k each, so all waves get k tiles
-    // (a few k-1), never k for some and k/2 for others.
+    // Geometry, first match wins: qg_set_launch_override, QG_FORCE_VARIANT,
+    // the exact-shape policy, then the defaults (with QG_TARGET_WAVES,
+    // QG_CONTIG and QG_SHAPE, read once, over the default wave count,
+    // mapping and ring).
+    const int64_t cus = compute_units();
+    const LaunchOverride api = current_override();
+    const LaunchOverride env = forced_variant(cus, a.swiglu ? a.n_out : L.N, L.K, a.m);
+    // The swiglu pair layout is a Q4G32 layout of Nv rows; its shapes are
+    // looked up with N = the gate rows, as the call names them.
+    const ShapePolicy* pol =
+        env.use_policy ? policy_for(a.swiglu ? 5 : L.fmt, a.m, a.swiglu ? a.n_out : L.N, L.K, a.grouped)
+                       : nullptr;
+    // About target_waves waves in total, never more waves than tiles; k
+    // tiles per wave, then the fewest waves that cover the tiles with k
+    // each, so all waves get k tiles (a few k-1), never k for some and k/2
+    // for others.
     static const int64_t env_waves = [] {
         const char* e = getenv("QG_TARGET_WAVES");
         const long v = e ? strtol(e, nullptr, 10) : 0;
         return v > 0 ? int64_t(v) : int64_t(0);
     }();
-    const int64_t cus = compute_units();
-    const int64_t target_waves =
-        g_override.target_waves > 0 ? g_override.target_waves
-        : env_waves                 ? env_waves
-                                    : cus * (a.grouped ? kWavesPerCuGrouped
-                                                       : (a.m > 1 ? kWavesPerCuDenseMulti : kWavesPerCuDense));
+    int64_t target_waves =
+        env_waves ? env_waves
+                  : cus * (a.grouped ? kWavesPerCuGrouped
+                                     : (a.m > 1 ? kWavesPerCuDenseMulti : kWavesPerCuDense));
+    if (pol && pol->waves_per_cu > 0) target_waves = cus * pol->waves_per_cu;
+    if (env.target_waves > 0) target_waves = env.target_waves;
+    if (api.target_waves > 0) target_waves = api.target_waves;
     int64_t cap = target_waves / slots;
     if (cap < 1) cap = 1;
     // Up to twice the cap, a dense launch is latency-bound rather than
@@ -120,16 +253,26 @@ hipError_t launch(const LaunchArgs& a)
         const char* e = getenv("QG_CONTIG");
         return e ? int(strtol(e, nullptr, 10)) : -1;
     }();
-    const bool contig = g_override.contig >= 0 ? g_override.contig != 0
-                      : env_contig >= 0         ? env_contig != 0
-                                                : a.grouped;
+    bool contig = env_contig >= 0 ? env_contig != 0 : a.grouped;
+    if (pol && pol->contig >= 0) contig = pol->contig != 0;
+    if (env.contig >= 0) contig = env.contig != 0;
+    if (api.contig >= 0) contig = api.contig != 0;
     kp.contig_k = contig ? k : 0;
     static const int env_shape = [] {
         const char* e = getenv("QG_SHAPE");   // tuning sweeps only
         return e ? int(strtol(e, nullptr, 10)) : -1;
     }();
     if (env_shape == SHAPE_D2_W4 || env_shape == SHAPE_D4_W4) shape = env_shape;
-    if (g_override.shape == SHAPE_D2_W4 || g_override.shape == SHAPE_D4_W4) shape = g_override.shape;
+    if (pol && pol->shape >= 0) shape = pol->shape;
+    if (env.shape >= 0) shape = env.shape;
+    if (api.shape >= 0) shape = api.shape;
+    // x in registers only where the kernel is built for the layout (and not
+    // with the argmax epilogue, whose tail shares LDS); elsewhere a request
+    // for it keeps the staged kernel with the default ring.
+    if (shape == SHAPE_XR && (!xr_supported(L, a.m) || a.argmax))
+        shape = (L.J <= 3 && k >= 2) ? SHAPE_D2_W4 : SHAPE_D4_W4;
+    kp.x_vec16 = ((reinterpret_cast<uintptr_t>(a.x) | uintptr_t(a.ldx * 2) |
+                   uintptr_t(a.x_slot_stride * 2)) & 15u) == 0;
     const size_t lds = lds_bytes_for(L, a.m);
     const hipStream_t s = a.stream;
     const int64_t w = waves_per_slot;
