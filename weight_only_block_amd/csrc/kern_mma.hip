@@ -184,28 +184,24 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
         // (1% on the LM head at m = 8).  A Q8PC row scale is re-read at every
         // step of its tile and stays a plain load (3% slower otherwise).
         else it.s = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(mt + ((j / SPG) * 16 + rho) * 2));
+        // x from memory: lanes past m load row m - 1 (in bounds) and zero
+        // the fragment with a select, so that no load sits in a per-lane
+        // branch (a divergent branch around the loads had made the compiler
+        // keep the ring in scratch memory and wait for every load).
         if constexpr (XG && Q4) {
-            // Row rho of x, k = 128 j + 32 g + 8 qs .. + 7 for the four
-            // groups g (lanes past m read nothing).
-            if (row_live) {
-                const uint16_t* src = p.x + int64_t(rho) * p.ldx + j * 128 + qs * 8;
-                it.a0 = load_x16(src);
-                it.a1 = load_x16(src + 32);
-                it.a2 = load_x16(src + 64);
-                it.a3 = load_x16(src + 96);
-            } else {
-                it.a0 = it.a1 = it.a2 = it.a3 = zero4;
-            }
+            // Row rho of x, k = 128 j + 32 g + 8 qs .. + 7 for the four groups g.
+            const uint16_t* src = p.x + int64_t(row_live ? rho : m - 1) * p.ldx + j * 128 + qs * 8;
+            it.a0 = load_x16(src);
+            it.a1 = load_x16(src + 32);
+            it.a2 = load_x16(src + 64);
+            it.a3 = load_x16(src + 96);
+            if (!row_live) it.a0 = it.a1 = it.a2 = it.a3 = zero4;
         } else if constexpr (XG) {
-            // Row rho of x, k = 64 j + 16 qs .. + 15 (lanes past m read nothing).
-            if (row_live) {
-                const uint16_t* src = p.x + int64_t(rho) * p.ldx + j * 64 + qs * 16;
-                it.a0 = load_x16(src);
-                it.a1 = load_x16(src + 8);
-            } else {
-                it.a0 = zero4;
-                it.a1 = zero4;
-            }
+            // Row rho of x, k = 64 j + 16 qs .. + 15.
+            const uint16_t* src = p.x + int64_t(row_live ? rho : m - 1) * p.ldx + j * 64 + qs * 16;
+            it.a0 = load_x16(src);
+            it.a1 = load_x16(src + 8);
+            if (!row_live) it.a0 = it.a1 = zero4;
         }
     };
 
