@@ -37,13 +37,10 @@ METRIC = "effective weight GB/s and % of HBM peak, m=1 quantized GEMV (µs/call)
 # known size.  Valid only for the kernel sources they were taken on (and,
 # for an entry with "m", for that number of activation rows).
 TRAFFIC = {
-    "lm_head": {"source_digest": "3bc72cdfeb32a7bb", "bytes_per_launch": 403444491},
-    "lm_head_q8g128": {"source_digest": "f6d5d5213b6a92fd", "bytes_per_launch": 396858764},
-    "moe_experts": {"source_digest": "b4e88a2430bfea11", "bytes_per_launch": 31808840},
-    "moe_experts_swiglu": {"source_digest": "fbcda5a3ebd34bd0", "bytes_per_launch": 47587822},
-    "moe_experts_merged": {"source_digest": "b4e88a2430bfea11", "bytes_per_launch": 47600825},
-    "lm_head_argmax_fused": {"source_digest": "6c893beab5bda0c6", "bytes_per_launch": 402952282},
-    "lm_head_mma": {"source_digest": "3384f6858735019b", "bytes_per_launch": 409586003, "m": 8},
+    "lm_head": {"source_digest": "0a1485ff9ae54ad5", "bytes_per_launch": 403399232},
+    # mean of the merged gate+up launch (63,244,000 B) and the down launch
+    # (32,019,968 B)
+    "moe_experts_merged": {"source_digest": "926be3e60dc4c95b", "bytes_per_launch": 47631984},
 }
 
 
