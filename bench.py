@@ -642,6 +642,63 @@ def ab_pairs(args, step, torch):
                    "b_wins": wins, "pairs": args.pairs}}
 
 
+TRACE_MHZ = 100.0   # s_memrealtime: the GPU's constant 100 MHz clock
+
+
+def _pct(v, q):
+    return round(float(np.percentile(v, q)) / TRACE_MHZ, 3)
+
+
+def wave_trace(args, step, torch, Q, info, trial, capacity=1 << 16):
+    """Per-wave timeline of one step in the middle of a stream of steps:
+    for each launch of the step, the start spread, the time from a wave's
+    start until its first weights are in, wave durations and end times
+    (percentiles, us from the launch's first wave start), per-XCD ends, and
+    the gap from each launch's last wave end to the next launch's first
+    wave start."""
+    buf = torch.zeros(capacity * 8, dtype=torch.int64, device="cuda")
+    for i in range(args.warmup):
+        step(i)
+    # The traced step is enqueued behind others, as in a steady stream.
+    for i in range(200):
+        step(i)
+    Q.set_wave_trace(buf)
+    step(1000 + trial)
+    records, launches, dropped = Q.wave_trace_state()
+    Q.set_wave_trace(None)
+    for i in range(50):
+        step(i)
+    torch.cuda.synchronize()
+    r = buf[:records * 8].view(-1, 8).cpu().numpy().astype(np.int64)
+    out = {"workload": args.workload, "trial": trial, "kernel": info.get("kernel"), "clock_mhz": TRACE_MHZ,
+           "launches": [], "dropped_launches": dropped}
+    bounds = []
+    for li in range(launches):
+        w = r[r[:, 7] == li]
+        t0, t1, t2 = w[:, 0], w[:, 1], w[:, 2]
+        base = int(t0.min())
+        first = (t1[t1 > 0] - t0[t1 > 0]).astype(np.float64)
+        xcd = {}
+        for x in sorted(set(w[:, 4].tolist())):
+            sel = w[:, 4] == x
+            xcd[str(int(x))] = {"waves": int(sel.sum()), "end_p50_us": _pct(t2[sel] - base, 50),
+                                "end_max_us": _pct(t2[sel] - base, 100)}
+        out["launches"].append({
+            "waves": int(len(w)),
+            "span_us": round(float(t2.max() - base) / TRACE_MHZ, 3),
+            "start_spread_us": _pct(t0 - base, 100),
+            "first_weights_p50_us": _pct(first, 50) if len(first) else None,
+            "first_weights_max_us": _pct(first, 100) if len(first) else None,
+            "wave_us_p10_p50_p90_max": [_pct(t2 - t0, q) for q in (10, 50, 90, 100)],
+            "end_us_p10_p50_p90_max": [_pct(t2 - base, q) for q in (10, 50, 90, 100)],
+            "xcd": xcd})
+        bounds.append((base, int(t2.max())))
+    out["gaps_us"] = [round((bounds[i + 1][0] - bounds[i][1]) / TRACE_MHZ, 3) for i in range(len(bounds) - 1)]
+    if bounds:
+        out["step_us"] = round((bounds[-1][1] - bounds[0][0]) / TRACE_MHZ, 3)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -683,6 +740,9 @@ def main():
     ap.add_argument("--pairs", type=int, default=5)
     ap.add_argument("--sweep", nargs="+", metavar="SPEC",
                     help="--ab '' SPEC for each SPEC in turn on one set of inputs (one JSON line each)")
+    ap.add_argument("--wave-trace", action="store_true",
+                    help="instead of the benchmark line, the per-wave timelines (qg_set_wave_trace) of "
+                         "three steps taken in the middle of a stream of steps, one JSON line each")
     args = ap.parse_args()
     global HOT, STACKED
     HOT = args.hot
@@ -721,6 +781,12 @@ def main():
             secs, rounds = time_steps(torch, step, args.warmup, args.steps)
         return dict(secs=secs, rounds=rounds, alg=alg, wbytes=wbytes, launches=launches, info=info,
                     cpu=cpu)
+
+    if args.wave_trace:
+        step, _, _, _, info, _ = measure_setup(args, torch, Q, synth)
+        for trial in range(3):
+            print(json.dumps({"wave_trace": wave_trace(args, step, torch, Q, info, trial)}), flush=True)
+        return
 
     if args.ab or args.sweep:
         step = measure_setup(args, torch, Q, synth)[0]

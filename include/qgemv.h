@@ -385,6 +385,36 @@ qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char *buf, s
  * Returns QG_ERR_INVALID_ARG (and changes nothing) for values outside these
  * ranges or target_waves above 2^24. */
 qg_status qg_set_launch_override(int64_t target_waves, int32_t contig, int32_t ring_depth);
+/* Per-wave timeline, for diagnostics: off by default, into a buffer the
+ * caller allocates once, with what does not fit dropped and counted (the
+ * native profiler of the MetaInfer-cpp README, section "M6 Reliability 与
+ * Performance Evidence").
+ * With device_records set, every launch with one activation row (m = 1) of
+ * the non-matrix-core kernels (qgemv_q8g64, qgemv_q4g32, qgemv_q8g128,
+ * qgemv_q8pc, the grouped calls and the *_argmax calls) runs a traced copy
+ * of its kernel (the untraced kernels carry no trace code) and reserves one
+ * record per wave in the buffer, launch after launch; each wave writes its
+ * record as it ends: eight uint64
+ * values, [0] start, [1] first weights in (0 where the wave streamed
+ * nothing), [2] end, all in ticks of the GPU's constant 100 MHz clock
+ * (s_memrealtime), [3] the hardware id register (compute unit, SIMD, shader
+ * engine), [4] the XCC (XCD) id, [5] slot, [6] wave index in the slot, [7]
+ * the launch's index since the buffer was set.  Record i of a launch of W
+ * waves per slot is slot * W + wave.  A launch whose waves do not fit in
+ * the space left is not traced and counts as dropped.
+ *   device_records     device memory, 8-byte aligned, capacity_records * 64
+ *                      bytes, owned by the caller and kept alive while
+ *                      traced launches may run; NULL turns tracing off.
+ *   capacity_records   > 0 with a buffer.
+ * Setting a buffer (or NULL) restarts the count.  Process-wide; launches on
+ * several streams at once share the buffer in the order they are enqueued.
+ * The records are valid once the traced launches have completed.
+ * qg_wave_trace_state reports the records reserved, the launches traced and
+ * the launches dropped since the buffer was set.
+ * Returns QG_ERR_INVALID_ARG for a misaligned buffer or a capacity <= 0
+ * with a buffer (changing nothing), or for NULL outputs. */
+qg_status qg_set_wave_trace(void *device_records, int64_t capacity_records);
+qg_status qg_wave_trace_state(int64_t *records, int64_t *launches, int64_t *dropped);
 
 /* ------------------------------------------------------ measurement hook
  * A plain read of `bytes` bytes at buf (device, 16-byte aligned, bytes a

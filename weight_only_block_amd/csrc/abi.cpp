@@ -513,6 +513,21 @@ qg_status qg_set_launch_override(int64_t target_waves, int32_t contig, int32_t r
     return QG_OK;
 }
 
+qg_status qg_set_wave_trace(void* device_records, int64_t capacity_records)
+{
+    if (device_records && (capacity_records <= 0 || reinterpret_cast<uintptr_t>(device_records) % 8 != 0))
+        return QG_ERR_INVALID_ARG;
+    qg::set_wave_trace(device_records, capacity_records);
+    return QG_OK;
+}
+
+qg_status qg_wave_trace_state(int64_t* records, int64_t* launches, int64_t* dropped)
+{
+    if (!records || !launches || !dropped) return QG_ERR_INVALID_ARG;
+    qg::wave_trace_state(records, launches, dropped);
+    return QG_OK;
+}
+
 qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char* buf, size_t buf_len)
 {
     if (!buf || buf_len == 0) return QG_ERR_INVALID_ARG;

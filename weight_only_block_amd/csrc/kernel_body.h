@@ -878,7 +878,30 @@ __device__ __forceinline__ void finish_argmax(uint64_t (&best)[M], const KernelP
 // EPI 0 stores fp32 sums; EPI 1 is the SwiGLU epilogue over gate/up pairs
 // (grouped Q4G32, m = 1 only); EPI 2 is the greedy argmax epilogue (dense,
 // logits store optional).
-template <int FMT, int M, int G, int R, int DEPTH, int WAVES, bool GROUPED, int EPI, int XRJ>
+// One per-wave timeline record (qg_set_wave_trace), written by lane 0 as
+// the wave ends: start, first weights in and end times (s_memrealtime, a
+// constant 100 MHz clock), the hardware and XCC ids, slot, wave index in
+// the slot and the launch's index.
+__device__ __forceinline__ void trace_wave(const KernelParams& p, uint64_t t_start, uint64_t t_first,
+                                           int slot, int64_t gw, int lane)
+{
+    if (!p.trace || lane != 0) return;
+    unsigned hw, xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    const int64_t per_slot = int64_t(gridDim.x) * int64_t(blockDim.x >> 6);
+    unsigned long long* r = p.trace + (int64_t(slot) * per_slot + gw) * 8;
+    r[0] = t_start;
+    r[1] = t_first;
+    r[2] = __builtin_amdgcn_s_memrealtime();
+    r[3] = hw;
+    r[4] = xcc;
+    r[5] = uint64_t(slot);
+    r[6] = uint64_t(gw);
+    r[7] = uint64_t(p.trace_launch);
+}
+
+template <int FMT, int M, int G, int R, int DEPTH, int WAVES, bool GROUPED, int EPI, int XRJ, bool TRACE>
 __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
 {
     // XRJ > 0: x in registers (XRegs) for rows of exactly XRJ steps per tile;
@@ -963,6 +986,13 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
     else lane_meta = lane * R * 4;
     const uint8_t* meta_lane = w + p.code_bytes + lane_meta;
 
+    // Timeline start: the wave has its arguments (and expert id) and is
+    // about to issue its first weight loads.  Read only when tracing: the
+    // clock read is a scalar memory operation, and any wait for scalar
+    // loads would also wait for it.
+    uint64_t tr_start = 0;
+    if constexpr (TRACE) tr_start = __builtin_amdgcn_s_memrealtime();
+
     // Load cursor: (tile, step) of the next item to fetch.
     int64_t ld_tile = t0, ld_j = 0;
     Item<R, META_BYTES> ring[DEPTH];
@@ -1007,6 +1037,15 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
         __syncthreads();
     }
 #undef QG_FILL_RING
+    uint64_t tr_first = 0;
+    if constexpr (TRACE) {
+        // Timeline: the time the first weights have arrived (the empty asm
+        // reads a register of the first load, so the wait for it is placed
+        // here; only traced launches take this branch).
+        const uint32_t first = ring[0].c[0].x;
+        asm volatile("" ::"v"(first));
+        tr_first = __builtin_amdgcn_s_memrealtime();
+    }
     if (GROUPED && bad_expert) {
         for (int64_t n = 0, t = t0; n < my_tiles; ++n, t += tstep) {
             if constexpr (EPI == 1) {
@@ -1021,10 +1060,14 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
                 }
             }
         }
+        if constexpr (TRACE) trace_wave(p, tr_start, tr_first, slot, gw, lane);
         return;
     }
     // (The argmax epilogue needs every wave at its closing barrier.)
-    if (EPI != 2 && n_items == 0) return;
+    if (EPI != 2 && n_items == 0) {
+        if constexpr (TRACE) trace_wave(p, tr_start, tr_first, slot, gw, lane);
+        return;
+    }
     uint64_t best[M];
 #pragma unroll
     for (int i = 0; i < M; ++i) best[i] = 0;
@@ -1110,6 +1153,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_stream(const KernelParams p)
         if (swb.n > 0) swb.flush(p, act, tstep, lane, rho);
     }
     if constexpr (EPI == 2) finish_argmax<M>(best, p, lane, wave);
+    if constexpr (TRACE) trace_wave(p, tr_start, tr_first, slot, gw, lane);
 }
 
 // Launch shape (launch.h): ring depth 2 or 4; work-groups are 4 waves.
@@ -1118,14 +1162,20 @@ template <int FMT, int M, int G, int DEPTH, int WAVES, bool GROUPED, int EPI, in
 hipError_t launch_variant(const KernelParams& kp, int64_t waves, int slots, size_t lds_bytes,
                           hipStream_t stream)
 {
-    auto kern = qgemv_stream<FMT, M, G, kRowSlots, DEPTH, WAVES, GROUPED, EPI, XRJ>;
+    auto kern = qgemv_stream<FMT, M, G, kRowSlots, DEPTH, WAVES, GROUPED, EPI, XRJ, false>;
+    // The timeline records (qg_set_wave_trace) come from a separate
+    // instantiation, so the untraced kernel carries no trace code at all;
+    // built for one activation row only.
+    auto kern_traced = qgemv_stream<FMT, M, G, kRowSlots, DEPTH, WAVES, GROUPED, EPI, XRJ, (M == 1)>;
     // Raise the dynamic-LDS limit once per kernel (static LDS is within the
     // reserve).  A failure is not left behind as the launch's error; it only
     // matters to launches that need more than the default 64 KiB.
     static const hipError_t attr = [&] {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 int(kMaxDynLdsBytes));
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxDynLdsBytes));
+        if (e == hipSuccess && M == 1)
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern_traced),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxDynLdsBytes));
         if (e != hipSuccess) (void)hipGetLastError();
         return e;
     }();
@@ -1137,7 +1187,11 @@ hipError_t launch_variant(const KernelParams& kp, int64_t waves, int slots, size
     const int64_t W = int64_t(grid.x) * WAVES;
     k.tiles_q = kp.tiles / W;
     k.tiles_r = kp.tiles % W;
-    hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), lds_bytes, stream, k);
+    k.trace = M == 1 ? reserve_wave_trace(W * slots, &k.trace_launch) : nullptr;
+    if (k.trace)
+        hipLaunchKernelGGL(kern_traced, grid, dim3(64 * WAVES), lds_bytes, stream, k);
+    else
+        hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), lds_bytes, stream, k);
     return hipGetLastError();
 }
 

@@ -45,7 +45,14 @@ struct KernelParams {
     float cert_t;              // Q4G32: certificate threshold T (q4_cert_threshold)
     int32_t x_vec16;           // x in registers: x, ldx and x_slot_stride allow 16-byte loads
     float inv_U;               // 1.0f / (units per row), for the staging's row index
+    unsigned long long* trace; // per-wave timeline records of this launch (null: off)
+    int64_t trace_launch;      // the launch's index in the timeline
 };
+
+// Per-wave timeline (qg_set_wave_trace): reserves the records of a launch of
+// `waves` waves and returns where they go, or null when tracing is off or
+// the buffer is full.  Host code.
+unsigned long long* reserve_wave_trace(int64_t waves, int64_t* launch_index);
 
 // Threshold T of the Q4G32 fast path's certificate (kernel_body.h,
 // kQ4Kappa): a row's fast sum is accepted when
@@ -110,6 +117,8 @@ struct LaunchOverride {
     int use_policy = 1;    // 0: leave out the exact-shape policy (QG_FORCE_VARIANT only)
 };
 void set_launch_override(const LaunchOverride& o);
+void set_wave_trace(void* buf, int64_t capacity);
+void wave_trace_state(int64_t* records, int64_t* launches, int64_t* dropped);
 
 // Bytes of dynamic LDS a launch of this layout needs for m activation rows.
 size_t lds_bytes_for(const Layout& L, int m);

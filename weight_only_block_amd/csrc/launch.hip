@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "launch.h"
 
@@ -151,6 +152,47 @@ static const ShapePolicy* policy_for(int fmt, int m, int64_t N, int64_t K, bool 
     return nullptr;
 }
 
+// Per-wave timeline (qg_set_wave_trace): a caller buffer of records, filled
+// launch after launch until it is full; later launches go untraced and are
+// counted as dropped.  The flag keeps the untraced path to one relaxed load.
+static std::mutex g_trace_mu;
+static std::atomic<bool> g_trace_on{false};
+static unsigned long long* g_trace_buf = nullptr;
+static int64_t g_trace_cap = 0, g_trace_used = 0, g_trace_launches = 0, g_trace_dropped = 0;
+
+void set_wave_trace(void* buf, int64_t capacity)
+{
+    std::lock_guard<std::mutex> lock(g_trace_mu);
+    g_trace_buf = static_cast<unsigned long long*>(buf);
+    g_trace_cap = buf ? capacity : 0;
+    g_trace_used = g_trace_launches = g_trace_dropped = 0;
+    g_trace_on.store(buf != nullptr, std::memory_order_relaxed);
+}
+
+void wave_trace_state(int64_t* records, int64_t* launches, int64_t* dropped)
+{
+    std::lock_guard<std::mutex> lock(g_trace_mu);
+    *records = g_trace_used;
+    *launches = g_trace_launches;
+    *dropped = g_trace_dropped;
+}
+
+unsigned long long* reserve_wave_trace(int64_t waves, int64_t* launch_index)
+{
+    *launch_index = 0;
+    if (!g_trace_on.load(std::memory_order_relaxed)) return nullptr;
+    std::lock_guard<std::mutex> lock(g_trace_mu);
+    if (!g_trace_buf) return nullptr;
+    if (waves > g_trace_cap - g_trace_used) {
+        ++g_trace_dropped;
+        return nullptr;
+    }
+    unsigned long long* r = g_trace_buf + g_trace_used * 8;
+    g_trace_used += waves;
+    *launch_index = g_trace_launches++;
+    return r;
+}
+
 // Compute units of the current device, looked up once per device.
 static int64_t compute_units()
 {
@@ -206,6 +248,8 @@ hipError_t launch(const LaunchArgs& a)
     kp.keys = static_cast<unsigned long long*>(a.argmax_workspace);
     kp.counter = a.argmax_workspace ? reinterpret_cast<unsigned int*>(kp.keys + a.m) : nullptr;
     kp.cert_t = q4_cert_threshold(L.J);
+    kp.trace = nullptr;
+    kp.trace_launch = 0;
     kp.inv_U = 1.0f / float(L.U);
     const int slots = a.grouped ? a.n_slots : 1;
     // Geometry, first match wins: qg_set_launch_override, QG_FORCE_VARIANT,

@@ -107,6 +107,8 @@ def lib() -> ctypes.CDLL:
             "qg_route_count": ([ctypes.c_char_p], ctypes.c_uint64),
             "qg_variant_name": ([ctypes.c_int, i64, i64, i64, ctypes.c_char_p, sz], st),
             "qg_set_launch_override": ([i64, ctypes.c_int32, ctypes.c_int32], st),
+            "qg_set_wave_trace": ([p, i64], st),
+            "qg_wave_trace_state": ([p, p, p], st),
             "qg_read_stream": ([p, sz, p, ctypes.c_int32, p], st),
         }
         for name, (args, res) in sig.items():
@@ -769,6 +771,33 @@ def read_stream(buf, sink, nbytes=None, waves_per_cu: int = 0, stream=None) -> N
 def set_launch_override(target_waves: int = 0, contig: int = -1, ring_depth: int = 0) -> None:
     """qg_set_launch_override; call with no arguments to restore the defaults."""
     _check(lib().qg_set_launch_override(target_waves, contig, ring_depth), "qg_set_launch_override")
+
+
+_trace_records = None   # the traced buffer, held while the library may write it
+
+
+def set_wave_trace(records=None) -> None:
+    """qg_set_wave_trace over a device tensor of whole 64-byte records (eight
+    int64 each); None turns tracing off.  The tensor is held here until the
+    next call."""
+    global _trace_records
+    if records is None:
+        _check(lib().qg_set_wave_trace(None, 0), "qg_set_wave_trace")
+        _trace_records = None
+        return
+    nbytes = records.numel() * records.element_size()
+    _on_gpu("qg_set_wave_trace", records=records)
+    if not records.is_contiguous() or nbytes < 64:
+        raise QGError(QG_ERR_INVALID_ARG, "qg_set_wave_trace: need a contiguous buffer of >= 64 bytes")
+    _check(lib().qg_set_wave_trace(records.data_ptr(), nbytes // 64), "qg_set_wave_trace")
+    _trace_records = records
+
+
+def wave_trace_state():
+    """(records reserved, launches traced, launches dropped) since the buffer was set."""
+    vals = [ctypes.c_int64(0) for _ in range(3)]
+    _check(lib().qg_wave_trace_state(*[ctypes.byref(v) for v in vals]), "qg_wave_trace_state")
+    return tuple(int(v.value) for v in vals)
 
 
 def expert_stride(N: int, K: int) -> int:
