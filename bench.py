@@ -713,7 +713,7 @@ def main():
                              "moe_experts_swiglu", "q8_small", "qwen3_0.6b", "q4_k2560", "w8a16_qwen3_14b_tp4",
                              "lm_head_mma", "w8a16_qwen3_14b_tp4_mma", "q4_k2560_mma"])
     ap.add_argument("--m", type=int, default=1,
-                    help="activation rows (q4_k2560, w8a16_qwen3_14b_tp4: 1..4; *_mma: 1..16)")
+                    help="activation rows (q4_k2560, w8a16_qwen3_14b_tp4: 1..4; *_mma: 2..16)")
     ap.add_argument("--hot", action="store_true",
                     help="one weight copy and one expert-id set, reused every step: the "
                          "cache-resident (hot) number, reported separately from the default cold one")
@@ -747,8 +747,9 @@ def main():
     global HOT, STACKED
     HOT = args.hot
     STACKED = args.stacked
-    if args.workload.endswith("_mma") and not 1 <= args.m <= 16:
-        print("--m %d: the matrix-core workloads take 1..16 rows" % args.m, file=sys.stderr)
+    if args.workload.endswith("_mma") and not 2 <= args.m <= 16:
+        print("--m %d: the matrix-core workloads take 2..16 rows (m = 1 is the plain kernels' "
+              "case)" % args.m, file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
         print("bench.py measures one GPU: the decode GEMV is single-GPU work here "

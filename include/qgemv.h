@@ -179,13 +179,15 @@ qg_status qgemv_q8pc(const void *w_packed, const uint16_t *x_bf16, float *y,
  * weights use their own packed layout (one 1 KiB wave load = 16 rows x 64 K,
  * the MFMA operand order), made by qpack_*_mma; y is the same product as the
  * plain GEMV:
- *   y[i*ldy + n] = sum_k W[n][k] * x[i*ldx + k],  0 <= i < m <= 16.
+ *   y[i*ldy + n] = sum_k W[n][k] * x[i*ldx + k],  0 <= i < m, 2 <= m <= 16.
  * K must be a multiple of 64 (128 for Q8G128).  The m activation rows are
  * staged in LDS when they fit (m * K * 2 bytes within 159 KiB, less the
  * partial sums of a K split); longer rows are read from memory with each
  * weight item instead, so any K is accepted.  Pointers, strides, ownership
- * and errors as qgemv_q8g64, with m = 1..16.  Each output row is computed
- * on its own (rows do not affect one another's bits). */
+ * and errors as qgemv_q8g64, with m = 2..16: m = 1 returns
+ * QG_ERR_UNSUPPORTED (single-token decode has no matrix to feed the matrix
+ * cores and takes the qgemv_* calls above; m = 0 does nothing).  Each output
+ * row is computed on its own (rows do not affect one another's bits). */
 size_t    qpack_q8g64_mma_size(int64_t N, int64_t K);
 size_t    qpack_q8g128_mma_size(int64_t N, int64_t K);
 size_t    qpack_q8pc_mma_size(int64_t N, int64_t K);

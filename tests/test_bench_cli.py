@@ -33,7 +33,7 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 def test_matrix_core_rows_out_of_range_are_refused():
     r = run_bench("--workload", "lm_head_mma", "--m", "17")
-    assert r.returncode == 2 and "1..16" in r.stderr
+    assert r.returncode == 2 and "2..16" in r.stderr
 
 
 def test_lm_head_algorithmic_bytes(bench):

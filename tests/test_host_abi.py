@@ -344,6 +344,7 @@ def test_mma_pack_roundtrip_sizes_and_validation(fmt):
     K = 1024
     # Every call below must fail validation (no launch on fake addresses).
     assert f(W, X, Y, 17, 16, K, K, 16, None) == Q.QG_ERR_UNSUPPORTED          # m > 16
+    assert f(W, X, Y, 1, 16, K, K, 16, None) == Q.QG_ERR_UNSUPPORTED           # m = 1: VALU calls
     # (Long rows are accepted: x too long to stage in LDS is read from memory.)
     assert f(W, X, Y, 2, 16, 96, 96, 16, None) == Q.QG_ERR_INVALID_ARG
     assert f(W, X, Y, 2, 16, K, K - 2, 16, None) == Q.QG_ERR_INVALID_ARG
@@ -387,9 +388,10 @@ def test_q4g32_mma_pack_layout_and_roundtrip():
     assert np.array_equal(c2, codes) and np.array_equal(s2, s) and np.array_equal(m2, mn)
     assert Q.qpack_mma_size("q4g32", N, 320) == 0          # K not a multiple of 128
     f = Q.lib().qgemv_q4g32_mma
-    assert f(W, X, Y, 1, 16, 320, 320, 16, None) == Q.QG_ERR_INVALID_ARG
+    assert f(W, X, Y, 2, 16, 320, 320, 16, None) == Q.QG_ERR_INVALID_ARG
     assert f(W, X, Y, 17, 16, 256, 256, 16, None) == Q.QG_ERR_UNSUPPORTED
-    assert f(W + 16, X, Y, 1, 16, 256, 256, 16, None) == Q.QG_ERR_ALIGNMENT
+    assert f(W, X, Y, 1, 16, 256, 256, 16, None) == Q.QG_ERR_UNSUPPORTED
+    assert f(W + 16, X, Y, 2, 16, 256, 256, 16, None) == Q.QG_ERR_ALIGNMENT
     assert f(W, X, Y, 0, 16, 256, 256, 16, None) == Q.QG_OK
     assert Q.variant_name(Q.FMT_Q4G32_MMA, 4, 9216, 2560) == "q4g32_mma_m4"
 

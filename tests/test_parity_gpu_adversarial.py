@@ -191,7 +191,7 @@ def test_lm_head_sparse_rows_multi_row(m):
     assert_parity(host(y), y_ref, a_ref, "q8g64 m=%d" % m)
 
 
-@pytest.mark.parametrize("m", [1, 5, 16])
+@pytest.mark.parametrize("m", [2, 5, 16])
 def test_lm_head_sparse_rows_matrix_cores(m):
     N, K = 24576, 2560
     rng = synth.rng_for(72, m)
@@ -208,17 +208,21 @@ def test_w8a16_sparse_rows_per_channel_scale():
     # random finite fp32 scales instead.
     N, K = 1792, 5120
     rng = synth.rng_for(73, 0)
-    x, small = adversarial_x(rng, 1, K)
+    # Two activation rows: the plain kernel runs each on its own (m = 1)
+    # and the matrix cores take both (they start at m = 2).
+    x, small = adversarial_x(rng, 2, K)
     q, _ = sparse_q8(rng, N, K, small, 1)
     s = rng.uniform(1e-3, 2e-2, size=N).astype(np.float32)
     odd = np.arange(N) % 8 == 4
     s[odd] = (10.0 ** rng.uniform(-30, 30, odd.sum()) * rng.choice([-1, 1], odd.sum())).astype(np.float32)
     s = s.view(np.uint32)
-    y = canary((1, N))
-    Q.qgemv_q8pc(dev(Q.qpack_q8pc(q, s)), dev(x), y, N, K)
     y_ref, a_ref = oracle.q8pc(q, s, x, threads=THREADS)
-    assert_parity(host(y), y_ref, a_ref, "q8pc")
-    ym = canary((1, N))
+    w = dev(Q.qpack_q8pc(q, s))
+    for i in range(2):
+        y = canary((1, N))
+        Q.qgemv_q8pc(w, dev(x[i:i + 1]), y, N, K)
+        assert_parity(host(y), y_ref[i:i + 1], a_ref[i:i + 1], "q8pc row %d" % i)
+    ym = canary((2, N))
     Q.qgemv_q8pc_mma(dev(Q.qpack_q8pc_mma(q, s)), dev(x), ym, N, K)
     assert_parity(host(ym), y_ref, a_ref, "q8pc matrix cores")
 
@@ -322,7 +326,7 @@ def test_q4_k2560_cancelling_groups(j, m):
     assert np.all(y_gpu[:, np.arange(N) % 6 == 0] == 0.0)
 
 
-@pytest.mark.parametrize("m", [1, 4, 16])
+@pytest.mark.parametrize("m", [2, 4, 16])
 def test_q4_matrix_cores_cancelling_groups(m):
     label, _, N, K = synth.Q4_K2560[0]
     rng = synth.rng_for(78, m)

@@ -1,7 +1,7 @@
 """GPU: seeded random shapes for every dense entry point against the oracle.
 
 Each case draws a format, a row count, N, K and row strides from a fixed
-seed: the plain kernels at m = 1..4 and the matrix-core kernels at m = 1..16,
+seed: the plain kernels at m = 1..4 and the matrix-core kernels at m = 2..16,
 K any whole number of scale groups (matrix cores: of 64-wide steps, 128 for
 Q8G128 and Q4G32).  Outputs must meet the oracle's bar, and the canary past
 N in each output row must survive.
@@ -36,7 +36,7 @@ def draw_case(i):
     rng = synth.rng_for(104, i)
     mma = bool(i % 3 == 2)
     fmt = ["q8g64", "q4g32", "q8g128", "q8pc"][int(rng.integers(0, 4))]
-    m = int(rng.integers(1, 17 if mma else 5))
+    m = int(rng.integers(2, 17)) if mma else int(rng.integers(1, 5))
     N = int(rng.choice([1, 2, 3, 15, 16, 17, 63, 100, 255, 256, 257, 1000, 2049, 3001]))
     step = MMA_STEP[fmt] if mma else GROUP[fmt]
     K = step * int(rng.integers(1, max(2, 6144 // step)))

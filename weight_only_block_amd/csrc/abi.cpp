@@ -92,11 +92,13 @@ qg_status check_gate_up(int64_t N, int64_t K, qg::Layout* L)
 }
 
 // Dense GEMV; with idx_out the argmax epilogue (y may then be null).
-// Matrix-core GEMV (MmaLayout), m = 1..16 (any K: rows of x too long to
+// Matrix-core GEMV (MmaLayout), m = 2..16 (any K: rows of x too long to
 // stage in LDS are read from memory).
 qg_status check_mma(int fmt, int64_t m, int64_t N, int64_t K, qg::MmaLayout* L)
 {
-    if (m < 1 || m > 16) return QG_ERR_UNSUPPORTED;
+    // Single-token decode (m = 1) is the VALU kernels' job: the matrix cores
+    // start at two rows.
+    if (m < 2 || m > 16) return QG_ERR_UNSUPPORTED;
     if (!qg::make_mma_layout(fmt, N, K, L)) return QG_ERR_INVALID_ARG;
     return QG_OK;
 }

@@ -1,4 +1,4 @@
-// Batched decode GEMV (m = 1..16 activation rows) on the gfx950 matrix
+// Batched decode GEMV (m = 2..16 activation rows) on the gfx950 matrix
 // cores, for the 8-bit formats in the matrix-core layout (layout.h,
 // MmaLayout).  The larger-batch decode of the Qwen3 C++ Reference Runtime
 // (MetaInfer-cpp) README ("B8/B16" kernels with the input rows reused from

@@ -137,7 +137,7 @@ QG_DECLARE_LAUNCHER(launch_q8g128);
 QG_DECLARE_LAUNCHER(launch_q8pc);
 #undef QG_DECLARE_LAUNCHER
 // Matrix-core kernel (kern_mma.hip): 8-bit formats in the MmaLayout,
-// m = 1..16 activation rows.
+// m = 2..16 activation rows.
 struct MmaParams {
     const uint8_t* w;
     const uint16_t* x;

@@ -120,7 +120,7 @@ static inline bool make_gate_up_layout(int64_t N, int64_t K, Layout* L, int64_t*
 }
 
 // Matrix-core ("mma") layout of the 8-bit formats, for the kernel that
-// feeds the 16x16x32 bf16 MFMA (m = 1..16 activation rows share the B-side
+// feeds the 16x16x32 bf16 MFMA (m = 2..16 activation rows share the B-side
 // weights).  A tile is 16 rows; a step covers 64 consecutive K.  Item
 // (tile t, step j) is one 1 KiB block at (t*J + j)*1024 in which lane l
 // holds the 16 signed codes of row t*16 + (l mod 16) at

@@ -481,7 +481,7 @@ def qgemv_q8pc(w_packed, x, y, N: int, K: int, m=None, ldx=None, ldy=None, strea
 
 def qgemv_q8g64_mma(w_packed, x, y, N: int, K: int, m=None, ldx=None, ldy=None, stream=None,
                     check=True):
-    """Batched decode on the matrix cores, m = 1..16: as qgemv_q8g64 with W
+    """Batched decode on the matrix cores, m = 2..16: as qgemv_q8g64 with W
     packed by qpack_q8g64_mma."""
     return _dense("qgemv_q8g64_mma", w_packed, x, y, N, K, m, ldx, ldy, stream, check)
 
