@@ -37,10 +37,10 @@ METRIC = "effective weight GB/s and % of HBM peak, m=1 quantized GEMV (µs/call)
 # known size.  Valid only for the kernel sources they were taken on (and,
 # for an entry with "m", for that number of activation rows).
 TRAFFIC = {
-    "lm_head": {"source_digest": "0a1485ff9ae54ad5", "bytes_per_launch": 403399232},
-    # mean of the merged gate+up launch (63,244,000 B) and the down launch
-    # (32,019,968 B)
-    "moe_experts_merged": {"source_digest": "926be3e60dc4c95b", "bytes_per_launch": 47631984},
+    "lm_head": {"source_digest": "2ef4ddc43df3520a", "bytes_per_launch": 403332862},
+    # mean of the merged gate+up launch (63,255,159 B) and the down launch
+    # (32,023,356 B)
+    "moe_experts_merged": {"source_digest": "ff36137d50d08a11", "bytes_per_launch": 47639258},
 }
 
 
