@@ -13,7 +13,9 @@
 //    (layout.h), read exactly once per call.
 //  * The activation rows are staged once per work-group in LDS, for Q4G32
 //    together with two fp32 sums per 32-wide group: X = sum x and
-//    XA = sum |x|.
+//    XA = sum |x|.  For one row and tiles of 2, 3 or 5 steps, each lane
+//    may instead hold just its own units of x (and their sums) in
+//    registers, with a ring of exactly one tile (XRegs).
 //  * Every output must be within 2e-3 * sum |w x| of the exact sum, for any
 //    inputs (rows of zero weights must give zero, a row whose only nonzero
 //    weight meets a 1e-5 activation must give that one product).
