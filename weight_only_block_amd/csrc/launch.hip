@@ -331,6 +331,41 @@ hipError_t launch(const LaunchArgs& a)
     }
 }
 
+// Exact-shape policy of the matrix-core kernel's work-group count, admitted
+// like kPolicy above (interleaved pairs, at least 4 of 5 won, median gain
+// of at least 0.5%; medians are us per step of the Qwen3-14B TP4 W8A16 layer
+// on the matrix cores, default -> entry).  per_cu: work-groups per CU (0:
+// default); even: when the tiles outnumber the resident work-groups, the
+// fewest work-groups that give every one the same number of tiles, so that
+// no round runs part-empty.
+struct MmaShapePolicy {
+    int fmt, m;
+    int64_t N, K;
+    int per_cu;
+    bool even;
+};
+static const MmaShapePolicy kMmaPolicy[] = {
+    // gate/up 5120 -> 8704, m = 4: even rounds 48.03 -> 46.57 (5/5)
+    {FMT_Q8PC, 4, 8704, 5120, 0, true},
+    // down 4352 -> 5120, m = 4: even rounds 48.05 -> 47.70 (5/5)
+    {FMT_Q8PC, 4, 5120, 4352, 0, true},
+    // gate/up, m = 8: even rounds 49.14 -> 47.81 (5/5)
+    {FMT_Q8PC, 8, 8704, 5120, 0, true},
+    // gate/up, m = 16 (x read from memory): three work-groups per CU, so the
+    // 544 tiles run in one round, 78.57 -> 75.28 (5/5)
+    {FMT_Q8PC, 16, 8704, 5120, 3, false},
+    {-1, 0, 0, 0, 0, false},   // (end)
+};
+
+static const MmaShapePolicy* mma_policy_for(int fmt, int m, int64_t N, int64_t K)
+{
+    for (const MmaShapePolicy& e : kMmaPolicy) {
+        if (e.fmt < 0) break;
+        if (e.fmt == fmt && e.m == m && e.N == N && e.K == K) return &e;
+    }
+    return nullptr;
+}
+
 hipError_t launch_mma_sized(int fmt, const MmaParams& kp, size_t lds, hipStream_t s)
 {
     // Two 4-wave work-groups per CU.  With at least two tiles per wave the
@@ -385,12 +420,21 @@ hipError_t launch_mma_sized(int fmt, const MmaParams& kp, size_t lds, hipStream_
         // how many fit in a CU's LDS; a 16-wave group takes a CU's share of
         // waves), each looping over its tiles: more than that would run in
         // uneven rounds.
+        // QG_FORCE_VARIANT's policy=0 leaves the shape policy out here too.
+        const MmaShapePolicy* pol =
+            forced_variant(compute_units(), kp.N, kp.K, kp.m).use_policy ? mma_policy_for(fmt, kp.m, kp.N, kp.K)
+                                                                         : nullptr;
         const size_t per_wg = (xg ? 0 : lds) + mma_split_lds_bytes(split);
         int64_t per_cu = int64_t(kMaxLdsBytes / per_wg);
-        const int64_t most = split == 16 ? 1 : 2;
+        int64_t most = split == 16 ? 1 : 2;
+        if (pol && pol->per_cu > 0 && split != 16) most = pol->per_cu;
         per_cu = per_cu < 1 ? 1 : (per_cu > most ? most : per_cu);
         const int64_t resident = compute_units() * per_cu;
-        const int64_t wgs = kp.tiles < resident ? kp.tiles : resident;
+        int64_t wgs = kp.tiles < resident ? kp.tiles : resident;
+        if (pol && pol->even && kp.tiles > resident) {
+            const int64_t rounds = (kp.tiles + resident - 1) / resident;
+            wgs = (kp.tiles + rounds - 1) / rounds;
+        }
         return launch_mma(fmt, split, xg, kp, wgs * split, per_wg, s);
     }
     const int64_t k = (kp.tiles + cap - 1) / cap;
