@@ -37,10 +37,10 @@ METRIC = "effective weight GB/s and % of HBM peak, m=1 quantized GEMV (µs/call)
 # known size.  Valid only for the kernel sources they were taken on (and,
 # for an entry with "m", for that number of activation rows).
 TRAFFIC = {
-    "lm_head": {"source_digest": "2ef4ddc43df3520a", "bytes_per_launch": 403332862},
-    # mean of the merged gate+up launch (63,255,159 B) and the down launch
-    # (32,023,356 B)
-    "moe_experts_merged": {"source_digest": "ff36137d50d08a11", "bytes_per_launch": 47639258},
+    "lm_head": {"source_digest": "9e23ef406b780c76", "bytes_per_launch": 403347454},
+    # mean of the merged gate+up launch (63,255,142 B) and the down launch
+    # (32,023,364 B)
+    "moe_experts_merged": {"source_digest": "4f8b8b779c875005", "bytes_per_launch": 47639254},
 }
 
 
