@@ -268,3 +268,38 @@ def test_graph_replays_match_eager_calls(fmt, N, K, m):
         ye = canary((m, N))
         gemv(w, x, ye, N, K, m=m)
         assert np.array_equal(got, host(ye)), "replay %d" % r
+
+
+# ------------------------------------------------ per-call variant forcing
+
+@pytest.mark.parametrize("spec", ["ksplit=1", "ksplit=4", "ksplit=16", "ksplit=4,xg=1", "ksplit=4,xg=0",
+                                  "mmawaves=64", "policy=0"])
+def test_forced_matrix_core_variants_meet_the_bar(spec, monkeypatch):
+    # QG_FORCE_VARIANT is read at every call, so one process can force each
+    # K split and x path in turn; every one must meet the oracle's bar.
+    N, K, m = 1792, 5120, 6
+    rng = synth.rng_for(109, 0)
+    q, s = synth.q8pc_weights(rng, N, K)
+    x = synth.activations(rng, m, K)
+    w = dev(Q.qpack_q8pc_mma(q, s))
+    monkeypatch.setenv("QG_FORCE_VARIANT", spec)
+    y = run("q8pc", q, s, x, packed=w)
+    monkeypatch.delenv("QG_FORCE_VARIANT")
+    check("q8pc", q, s, x, y, "forced %s" % spec)
+
+
+def test_work_group_policy_keeps_the_bits():
+    # The shape policy only changes how many work-groups share the tiles
+    # (even rounds at this shape); each tile is computed the same way.
+    N, K, m = 8704, 5120, 4
+    rng = synth.rng_for(110, 0)
+    q, s = synth.q8pc_weights(rng, N, K)
+    x = synth.activations(rng, m, K)
+    w = dev(Q.qpack_q8pc_mma(q, s))
+    y_policy = run("q8pc", q, s, x, packed=w)
+    os.environ["QG_FORCE_VARIANT"] = "policy=0"
+    try:
+        y_default = run("q8pc", q, s, x, packed=w)
+    finally:
+        del os.environ["QG_FORCE_VARIANT"]
+    assert np.array_equal(y_policy.view(np.uint32), y_default.view(np.uint32))

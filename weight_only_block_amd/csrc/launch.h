@@ -115,6 +115,12 @@ struct LaunchOverride {
     int contig;            // 1: contiguous tile runs per wave, 0: grid-stride, -1: default
     int shape;             // SHAPE_D2_W4 / SHAPE_D4_W4 / SHAPE_XR, -1: default
     int use_policy = 1;    // 0: leave out the exact-shape policy (QG_FORCE_VARIANT only)
+    // Matrix-core kernel (QG_FORCE_VARIANT only): K split 1, 4 or 16 (-1:
+    // default), x read from memory (1) or staged (0) (-1: default), and the
+    // wave count that decides whether to split (0: default).
+    int mma_ksplit = -1;
+    int mma_xg = -1;
+    int64_t mma_waves = 0;
 };
 void set_launch_override(const LaunchOverride& o);
 void set_wave_trace(void* buf, int64_t capacity);

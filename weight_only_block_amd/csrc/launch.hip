@@ -54,14 +54,19 @@ static LaunchOverride current_override()
 // capture in one process pick up a change at the next call, as the per-call
 // environment knobs of the vllm.cpp pull request #1936 commit log): a comma
 // list of waves=<total waves>, wpcu=<waves per compute unit>, contig=0|1 and
-// ring=2|4|xr (xr: x in registers, where the layout allows it), optionally
-// restricted to one shape with n=<N>, k=<K> and m=<m> (calls of other
-// shapes are then not forced), and policy=0 to leave out the exact-shape
-// policy below (for A/B runs of the policy itself).  Unknown keys and bad
-// values are ignored; an unset or empty variable forces nothing.
+// ring=2|4|xr (xr: x in registers, where the layout allows it) for the plain
+// kernels, ksplit=1|4|16, xg=0|1 and mmawaves=<waves> for the matrix-core
+// kernel, optionally restricted to one shape with n=<N>, k=<K> and m=<m>
+// (calls of other shapes are then not forced), and policy=0 to leave out the
+// exact-shape policies below (for A/B runs of the policies themselves).
+// Unknown keys and bad values are ignored; an unset or empty variable
+// forces nothing.
 static LaunchOverride forced_variant(int64_t cus, int64_t N, int64_t K, int m)
 {
-    LaunchOverride o = {0, -1, -1, 1};
+    LaunchOverride o;
+    o.target_waves = 0;
+    o.contig = -1;
+    o.shape = -1;
     const char* e = getenv("QG_FORCE_VARIANT");
     if (!e) return o;
     bool other_shape = false;
@@ -81,6 +86,9 @@ static LaunchOverride forced_variant(int64_t cus, int64_t N, int64_t K, int m)
         else if (klen == 1 && e[0] == 'k' && num && v != K) other_shape = true;
         else if (klen == 1 && e[0] == 'm' && num && v != m) other_shape = true;
         else if (klen == 6 && !strncmp(e, "policy", 6) && num && (v == 0 || v == 1)) o.use_policy = int(v);
+        else if (klen == 6 && !strncmp(e, "ksplit", 6) && num && (v == 1 || v == 4 || v == 16)) o.mma_ksplit = int(v);
+        else if (klen == 2 && !strncmp(e, "xg", 2) && num && (v == 0 || v == 1)) o.mma_xg = int(v);
+        else if (klen == 8 && !strncmp(e, "mmawaves", 8) && num && v > 0 && v <= (1L << 24)) o.mma_waves = v;
         else if (klen == 4 && !strncmp(e, "ring", 4)) {
             if (num && v == 2) o.shape = SHAPE_D2_W4;
             else if (num && v == 4) o.shape = SHAPE_D4_W4;
@@ -89,7 +97,13 @@ static LaunchOverride forced_variant(int64_t cus, int64_t N, int64_t K, int m)
         if (!end) break;
         e = end + 1;
     }
-    if (other_shape) return LaunchOverride{0, -1, -1, 1};
+    if (other_shape) {
+        LaunchOverride none;
+        none.target_waves = 0;
+        none.contig = -1;
+        none.shape = -1;
+        return none;
+    }
     return o;
 }
 
@@ -253,9 +267,7 @@ hipError_t launch(const LaunchArgs& a)
     kp.inv_U = 1.0f / float(L.U);
     const int slots = a.grouped ? a.n_slots : 1;
     // Geometry, first match wins: qg_set_launch_override, QG_FORCE_VARIANT,
-    // the exact-shape policy, then the defaults (with QG_TARGET_WAVES,
-    // QG_CONTIG and QG_SHAPE, read once, over the default wave count,
-    // mapping and ring).
+    // the exact-shape policy, then the defaults.
     const int64_t cus = compute_units();
     const LaunchOverride api = current_override();
     const LaunchOverride env = forced_variant(cus, a.swiglu ? a.n_out : L.N, L.K, a.m);
@@ -268,15 +280,8 @@ hipError_t launch(const LaunchArgs& a)
     // tiles per wave, then the fewest waves that cover the tiles with k
     // each, so all waves get k tiles (a few k-1), never k for some and k/2
     // for others.
-    static const int64_t env_waves = [] {
-        const char* e = getenv("QG_TARGET_WAVES");
-        const long v = e ? strtol(e, nullptr, 10) : 0;
-        return v > 0 ? int64_t(v) : int64_t(0);
-    }();
     int64_t target_waves =
-        env_waves ? env_waves
-                  : cus * (a.grouped ? kWavesPerCuGrouped
-                                     : (a.m > 1 ? kWavesPerCuDenseMulti : kWavesPerCuDense));
+        cus * (a.grouped ? kWavesPerCuGrouped : (a.m > 1 ? kWavesPerCuDenseMulti : kWavesPerCuDense));
     if (pol && pol->waves_per_cu > 0) target_waves = cus * pol->waves_per_cu;
     if (env.target_waves > 0) target_waves = env.target_waves;
     if (api.target_waves > 0) target_waves = api.target_waves;
@@ -292,21 +297,12 @@ hipError_t launch(const LaunchArgs& a)
     // Routed-expert launches give each wave a contiguous run of k tiles (the
     // whole 31.5 MB call is in flight at once anyway, so a common window
     // buys nothing, and adjacent tiles measured ~3% faster); dense sweeps
-    // keep the grid-stride window.  QG_CONTIG=0/1 overrides (tuning sweeps).
-    static const int env_contig = [] {
-        const char* e = getenv("QG_CONTIG");
-        return e ? int(strtol(e, nullptr, 10)) : -1;
-    }();
-    bool contig = env_contig >= 0 ? env_contig != 0 : a.grouped;
+    // keep the grid-stride window.
+    bool contig = a.grouped;
     if (pol && pol->contig >= 0) contig = pol->contig != 0;
     if (env.contig >= 0) contig = env.contig != 0;
     if (api.contig >= 0) contig = api.contig != 0;
     kp.contig_k = contig ? k : 0;
-    static const int env_shape = [] {
-        const char* e = getenv("QG_SHAPE");   // tuning sweeps only
-        return e ? int(strtol(e, nullptr, 10)) : -1;
-    }();
-    if (env_shape == SHAPE_D2_W4 || env_shape == SHAPE_D4_W4) shape = env_shape;
     if (pol && pol->shape >= 0) shape = pol->shape;
     if (env.shape >= 0) shape = env.shape;
     if (api.shape >= 0) shape = api.shape;
@@ -375,20 +371,12 @@ hipError_t launch_mma_sized(int fmt, const MmaParams& kp, size_t lds, hipStream_
     // least 64 scale groups and the LDS allows, else four (with fewer
     // groups per wave the per-tile fold outweighs the wider stream:
     // 5120 x 1280 Q8PC at m = 8 measured 6.3 us with four, 7.5 with sixteen).
-    // QG_MMA_KSPLIT = 1, 4 or 16 forces the split (tuning sweeps).
-    static const int64_t env_waves = [] {
-        const char* e = getenv("QG_MMA_WAVES");   // tuning sweeps only
-        const long v = e ? strtol(e, nullptr, 10) : 0;
-        return v > 0 ? int64_t(v) : int64_t(0);
-    }();
-    static const int env_split = [] {
-        const char* e = getenv("QG_MMA_KSPLIT");
-        return e ? int(strtol(e, nullptr, 10)) : -1;
-    }();
-    static const int env_xg = [] {
-        const char* e = getenv("QG_MMA_XG");        // tuning sweeps only
-        return e ? int(strtol(e, nullptr, 10)) : -1;
-    }();
+    // QG_FORCE_VARIANT's ksplit=1|4|16 forces the split, xg=0|1 the x path
+    // and mmawaves the wave count the choice is made for (tuning sweeps).
+    const LaunchOverride env = forced_variant(compute_units(), kp.N, kp.K, kp.m);
+    const int64_t env_waves = env.mma_waves;
+    const int env_split = env.mma_ksplit;
+    const int env_xg = env.mma_xg;
     const int64_t cap = env_waves ? env_waves : compute_units() * 8;
     const int64_t groups_per_row = fmt == FMT_Q8G128 ? kp.J / 2 : kp.J;
     int split = (kp.tiles < 2 * cap && groups_per_row >= 4) ? 4 : 1;
@@ -402,7 +390,7 @@ hipError_t launch_mma_sized(int fmt, const MmaParams& kp, size_t lds, hipStream_
     // 11.1 us on 1792 x 5120 and 17.2 -> 13.6 us on 5120 x 4352).  Q4G32
     // keeps staging as long as x fits.  Without a split, x is read from
     // memory only when it does not fit in LDS at all.
-    // QG_MMA_XG = 0/1 forces staging on (where x fits) / x from memory.
+    // xg=0/1 forces staging on (where x fits) / x from memory.
     bool xg = false;
     if (split == 16 && lds + mma_split_lds_bytes(16) > kMaxDynLdsBytes) split = 4;
     if (split == 4) {
@@ -421,9 +409,7 @@ hipError_t launch_mma_sized(int fmt, const MmaParams& kp, size_t lds, hipStream_
         // waves), each looping over its tiles: more than that would run in
         // uneven rounds.
         // QG_FORCE_VARIANT's policy=0 leaves the shape policy out here too.
-        const MmaShapePolicy* pol =
-            forced_variant(compute_units(), kp.N, kp.K, kp.m).use_policy ? mma_policy_for(fmt, kp.m, kp.N, kp.K)
-                                                                         : nullptr;
+        const MmaShapePolicy* pol = env.use_policy ? mma_policy_for(fmt, kp.m, kp.N, kp.K) : nullptr;
         const size_t per_wg = (xg ? 0 : lds) + mma_split_lds_bytes(split);
         int64_t per_cu = int64_t(kMaxLdsBytes / per_wg);
         int64_t most = split == 16 ? 1 : 2;
