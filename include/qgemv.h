@@ -209,9 +209,12 @@ qg_status qgemv_q8g128_mma(const void *w_packed, const uint16_t *x_bf16, float *
                            int64_t N, int64_t K, int64_t ldx, int64_t ldy, void *hip_stream);
 qg_status qgemv_q8pc_mma(const void *w_packed, const uint16_t *x_bf16, float *y, int64_t m,
                          int64_t N, int64_t K, int64_t ldx, int64_t ldy, void *hip_stream);
-/* Q4G32 on the matrix cores, same contract: one MFMA per 32-group (its
- * B operand the group's codes widened to bf16, its sum then scaled, plus
- * the min times the group's activation sum).  Packed by qpack_q4g32_mma
+/* Q4G32 on the matrix cores, same contract: one MFMA per 32-group, whose
+ * B operand is the group's codes less the group's zero point
+ * z = clamp(rint(-min / scale), 0, 15), widened to bf16 exactly; that sum is
+ * scaled and (min + scale * z) times the group's activation sum is added,
+ * so neither term can cancel (each is at most twice the largest weight of
+ * the group in size).  Packed by qpack_q4g32_mma
  * (1 KiB wave load = 16 rows x 128 K); K must be a multiple of 128 (else
  * QG_ERR_INVALID_ARG).  codes, scales and mins are the canonical Q4G32
  * arrays of qpack_q4g32. */
@@ -404,8 +407,10 @@ qg_status qg_set_launch_override(int64_t target_waves, int32_t contig, int32_t r
  * of its kernel (the untraced kernels carry no trace code) and reserves one
  * record per wave in the buffer, launch after launch; each wave writes its
  * record as it ends: eight uint64
- * values, [0] start, [1] first weights in (0 where the wave streamed
- * nothing), [2] end, all in ticks of the GPU's constant 100 MHz clock
+ * values, [0] start (the wave has its arguments and, in grouped calls, its
+ * expert id, and is about to issue its first weight loads), [1] first
+ * weights in (0 where the wave streamed nothing), [2] end, all in ticks of
+ * the GPU's constant 100 MHz clock
  * (s_memrealtime), [3] the hardware id register (compute unit, SIMD, shader
  * engine), [4] the XCC (XCD) id, [5] slot, [6] wave index in the slot, [7]
  * the launch's index since the buffer was set.  Record i of a launch of W
