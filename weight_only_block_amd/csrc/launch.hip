@@ -113,6 +113,11 @@ static LaunchOverride forced_variant(int64_t cus, int64_t N, int64_t K, int m)
 // every other shape takes the defaults.  This is the per-shape, measured
 // operator policy of the MetaInfer-cpp README (milestone M6.5-E,
 // MeasuredOperatorPolicy), for launch geometry.
+// Policy key of the grouped gate/up calls with the SwiGLU epilogue (their
+// pair layout is a Q4G32 layout; they are keyed apart from plain grouped
+// Q4G32 calls, with N = the gate rows).
+constexpr int kPolicySwiglu = 5;
+
 struct ShapePolicy {
     int fmt, m;
     int64_t N, K;
@@ -144,7 +149,11 @@ static const ShapePolicy kPolicy[] = {
     {FMT_Q8PC, 4, 1792, 5120, false, 0, -1, SHAPE_D2_W4},
     {FMT_Q8PC, 4, 8704, 5120, false, 0, -1, SHAPE_D2_W4},
     // Qwen3-0.6B-shaped layer: x in registers 30.55 -> 30.35 (4/5),
-    // ring 2 30.33 -> 30.13 (4/5), x in registers 30.38 -> 30.19 (4/5)
+    // ring 2 30.33 -> 30.13 (4/5), x in registers 30.38 -> 30.19 (4/5);
+    // the 1024 x 1024 matrices (k, v, and the Q8G64 N = K = 1024 GEMV)
+    // ring 2: layer 25.23 -> 24.38 (5/5, graph replay), the single GEMV
+    // 3.95 -> 3.55 (graph) and 3.94 -> 3.64 (eager, 5/5 each)
+    {FMT_Q8G64, 1, 1024, 1024, false, 0, -1, SHAPE_D2_W4},
     {FMT_Q8G64, 1, 1024, 2048, false, 0, -1, SHAPE_XR},
     {FMT_Q8G64, 1, 3072, 1024, false, 0, -1, SHAPE_D2_W4},
     {FMT_Q8G64, 1, 1024, 3072, false, 0, -1, SHAPE_XR},
@@ -154,6 +163,9 @@ static const ShapePolicy kPolicy[] = {
     {FMT_Q4G32, 1, 1536, 4096, true, 0, -1, SHAPE_XR},
     {FMT_Q4G32, 1, 4096, 1536, true, 0, -1, SHAPE_XR},
     {FMT_Q4G32, 1, 3072, 4096, true, 0, -1, SHAPE_XR},
+    // Routed gate/up with the SwiGLU epilogue: x in registers, fused flow
+    // 20.76 -> 20.62 (5/5)
+    {kPolicySwiglu, 1, 1536, 4096, true, 0, -1, SHAPE_XR},
     {-1, 0, 0, 0, false, 0, -1, -1},   // (end)
 };
 
@@ -274,7 +286,8 @@ hipError_t launch(const LaunchArgs& a)
     // The swiglu pair layout is a Q4G32 layout of Nv rows; its shapes are
     // looked up with N = the gate rows, as the call names them.
     const ShapePolicy* pol =
-        env.use_policy ? policy_for(a.swiglu ? 5 : L.fmt, a.m, a.swiglu ? a.n_out : L.N, L.K, a.grouped)
+        env.use_policy ? policy_for(a.swiglu ? kPolicySwiglu : L.fmt, a.m, a.swiglu ? a.n_out : L.N, L.K,
+                                    a.grouped)
                        : nullptr;
     // About target_waves waves in total, never more waves than tiles; k
     // tiles per wave, then the fewest waves that cover the tiles with k
