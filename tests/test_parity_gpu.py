@@ -402,24 +402,27 @@ def test_graph_replays_match_eager_calls():
     ("q4g32", (9216, 9216), 2560),
     ("q8g128", (701, 1299), 2048),           # a part ending inside a tile
     ("q8pc", (8704, 8704), 5120)])
-def test_stacked_rows_equal_separate_calls_bitwise(fmt, parts, K):
+@pytest.mark.parametrize("m", [1, 2])
+def test_stacked_rows_equal_separate_calls_bitwise(fmt, parts, K, m):
     # A matrix made of several matrices' rows stacked in order (the stacked
     # projections of a layer) gives each part's outputs bit for bit, because
-    # every output row is computed the same way in any matrix.
+    # every output row is computed the same way in any matrix, whatever
+    # launch shape the stacked and the separate calls take (at m = 1 the
+    # stacked gate+up matrices hold x in registers, their parts stage it).
     gen = {"q8g64": synth.q8g64_weights, "q4g32": synth.q4g32_weights,
            "q8g128": synth.q8g128_weights, "q8pc": synth.q8pc_weights}[fmt]
     pack = getattr(Q, "qpack_" + fmt)
     call = getattr(Q, "qgemv_" + fmt)
     mats = [gen(synth.rng_for(20, j, K), N, K) for j, N in enumerate(parts)]
     stacked = tuple(np.concatenate(arrs) for arrs in zip(*mats))
-    x = dev(synth.activations(synth.rng_for(20, 99, K), 2, K))
+    x = dev(synth.activations(synth.rng_for(20, 99, K), m, K))
     Ns = sum(parts)
-    ys = canary((2, Ns))
+    ys = canary((m, Ns))
     call(dev(pack(*stacked)), x, ys, Ns, K)
     ys = host(ys)
     off = 0
     for j, (w, N) in enumerate(zip(mats, parts)):
-        y = canary((2, N))
+        y = canary((m, N))
         call(dev(pack(*w)), x, y, N, K)
         assert np.array_equal(host(y).view(np.uint32), ys[:, off:off + N].view(np.uint32)), "part %d" % j
         off += N

@@ -154,6 +154,13 @@ static const ShapePolicy kPolicy[] = {
     // ring 2: layer 25.23 -> 24.38 (5/5, graph replay), the single GEMV
     // 3.95 -> 3.55 (graph) and 3.94 -> 3.64 (eager, 5/5 each)
     {FMT_Q8G64, 1, 1024, 1024, false, 0, -1, SHAPE_D2_W4},
+    // Projections stacked into one launch (q+k+v and gate+up sharing an
+    // activation): the 0.6B layer's gate+up 6144 x 1024, x in registers,
+    // stacked layer 16.08 -> 15.37 (4/5, graph replay), then contiguous
+    // 15.36 -> 15.20 (5/5); the Q4G32 K=2560 family's gate+up 18432 x 2560,
+    // x in registers, 17.06 -> 16.09 (5/5)
+    {FMT_Q8G64, 1, 6144, 1024, false, 0, 1, SHAPE_XR},
+    {FMT_Q4G32, 1, 18432, 2560, false, 0, -1, SHAPE_XR},
     {FMT_Q8G64, 1, 1024, 2048, false, 0, -1, SHAPE_XR},
     {FMT_Q8G64, 1, 3072, 1024, false, 0, -1, SHAPE_D2_W4},
     {FMT_Q8G64, 1, 1024, 3072, false, 0, -1, SHAPE_XR},
