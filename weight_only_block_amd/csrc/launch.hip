@@ -347,30 +347,40 @@ hipError_t launch(const LaunchArgs& a)
     }
 }
 
-// Exact-shape policy of the matrix-core kernel's work-group count, admitted
-// like kPolicy above (interleaved pairs, at least 4 of 5 won, median gain
-// of at least 0.5%; medians are us per step of the Qwen3-14B TP4 W8A16 layer
-// on the matrix cores, default -> entry).  per_cu: work-groups per CU (0:
-// default); even: when the tiles outnumber the resident work-groups, the
-// fewest work-groups that give every one the same number of tiles, so that
-// no round runs part-empty.
+// Exact-shape policy of the matrix-core kernel's launch, admitted like
+// kPolicy above (interleaved pairs, at least 4 of 5 won, median gain of at
+// least 0.5%; medians are us per step of the Qwen3-14B TP4 W8A16 layer, or
+// of the Q4G32 K=2560 family, on the matrix cores, default -> entry).
+// per_cu: work-groups per CU (0: default); even: when the tiles outnumber
+// the resident work-groups, the fewest work-groups that give every one the
+// same number of tiles, so that no round runs part-empty; ksplit (1, 4 or
+// 16) and xg (0: x staged, 1: x read from memory) as the keys of
+// QG_FORCE_VARIANT (-1: the default choice).
 struct MmaShapePolicy {
     int fmt, m;
     int64_t N, K;
     int per_cu;
     bool even;
+    int ksplit;
+    int xg;
 };
 static const MmaShapePolicy kMmaPolicy[] = {
     // gate/up 5120 -> 8704, m = 4: even rounds 48.03 -> 46.57 (5/5)
-    {FMT_Q8PC, 4, 8704, 5120, 0, true},
+    {FMT_Q8PC, 4, 8704, 5120, 0, true, -1, -1},
     // down 4352 -> 5120, m = 4: even rounds 48.05 -> 47.70 (5/5)
-    {FMT_Q8PC, 4, 5120, 4352, 0, true},
+    {FMT_Q8PC, 4, 5120, 4352, 0, true, -1, -1},
     // gate/up, m = 8: even rounds 49.14 -> 47.81 (5/5)
-    {FMT_Q8PC, 8, 8704, 5120, 0, true},
+    {FMT_Q8PC, 8, 8704, 5120, 0, true, -1, -1},
     // gate/up, m = 16 (x read from memory): three work-groups per CU, so the
     // 544 tiles run in one round, 78.57 -> 75.28 (5/5)
-    {FMT_Q8PC, 16, 8704, 5120, 3, false},
-    {-1, 0, 0, 0, 0, false},   // (end)
+    {FMT_Q8PC, 16, 8704, 5120, 3, false, -1, -1},
+    // o 1280 -> 5120, m = 16: x read from memory, 75.02 -> 74.38 (5/5)
+    {FMT_Q8PC, 16, 5120, 1280, 0, false, 4, 1},
+    // Q4G32 gate/up 2560 -> 9216, m = 16: sixteen waves share each tile
+    // (one staged copy of x per CU instead of one per four-wave group),
+    // three-GEMV step 58.86 -> 51.23 (5/5)
+    {FMT_Q4G32, 16, 9216, 2560, 0, false, 16, -1},
+    {-1, 0, 0, 0, 0, false, -1, -1},   // (end)
 };
 
 static const MmaShapePolicy* mma_policy_for(int fmt, int m, int64_t N, int64_t K)
@@ -394,9 +404,12 @@ hipError_t launch_mma_sized(int fmt, const MmaParams& kp, size_t lds, hipStream_
     // QG_FORCE_VARIANT's ksplit=1|4|16 forces the split, xg=0|1 the x path
     // and mmawaves the wave count the choice is made for (tuning sweeps).
     const LaunchOverride env = forced_variant(compute_units(), kp.N, kp.K, kp.m);
+    // QG_FORCE_VARIANT's policy=0 leaves the shape policy out here too.
+    const MmaShapePolicy* pol = env.use_policy ? mma_policy_for(fmt, kp.m, kp.N, kp.K) : nullptr;
     const int64_t env_waves = env.mma_waves;
-    const int env_split = env.mma_ksplit;
-    const int env_xg = env.mma_xg;
+    // The forced K split and x path, else the policy's, else the defaults.
+    const int env_split = env.mma_ksplit > 0 ? env.mma_ksplit : (pol ? pol->ksplit : -1);
+    const int env_xg = env.mma_xg >= 0 ? env.mma_xg : (pol ? pol->xg : -1);
     const int64_t cap = env_waves ? env_waves : compute_units() * 8;
     const int64_t groups_per_row = fmt == FMT_Q8G128 ? kp.J / 2 : kp.J;
     int split = (kp.tiles < 2 * cap && groups_per_row >= 4) ? 4 : 1;
@@ -428,8 +441,6 @@ hipError_t launch_mma_sized(int fmt, const MmaParams& kp, size_t lds, hipStream_
         // how many fit in a CU's LDS; a 16-wave group takes a CU's share of
         // waves), each looping over its tiles: more than that would run in
         // uneven rounds.
-        // QG_FORCE_VARIANT's policy=0 leaves the shape policy out here too.
-        const MmaShapePolicy* pol = env.use_policy ? mma_policy_for(fmt, kp.m, kp.N, kp.K) : nullptr;
         const size_t per_wg = (xg ? 0 : lds) + mma_split_lds_bytes(split);
         int64_t per_cu = int64_t(kMaxLdsBytes / per_wg);
         int64_t most = split == 16 ? 1 : 2;
