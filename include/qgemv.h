@@ -387,9 +387,10 @@ qg_status qg_variant_name(int fmt, int64_t m, int64_t N, int64_t K, char *buf, s
  * QG_FORCE_VARIANT ("waves=N,wpcu=N,contig=0|1,ring=2|4|xr", any subset),
  * read at every call, does the same with lower precedence; both take
  * precedence over the library's per-shape policy.  The same variable also
- * takes ksplit=1|4|16, xg=0|1 and mmawaves=N for the matrix-core kernels
- * (K split, x read from memory or staged, the wave count the split is
- * chosen for), n=N,k=K,m=M to force only calls of that shape, and policy=0
+ * takes ksplit=1|4|16, xg=0|1, mmawaves=N, mmacu=N and mmaeven=0|1 for the
+ * matrix-core kernels (K split, x read from memory or staged, the wave
+ * count the split is chosen for, work-groups per CU and even rounds of a
+ * split launch), n=N,k=K,m=M to force only calls of that shape, and policy=0
  * to leave out the per-shape policies.  The plain kernels compute each
  * output the same way under every choice (the same bits); a different
  * matrix-core K split changes how each output's partial sums are grouped

@@ -121,6 +121,10 @@ struct LaunchOverride {
     int mma_ksplit = -1;
     int mma_xg = -1;
     int64_t mma_waves = 0;
+    // Split launches: work-groups per CU (0: default) and even rounds (1 on,
+    // 0 off, -1: default).
+    int mma_per_cu = 0;
+    int mma_even = -1;
 };
 void set_launch_override(const LaunchOverride& o);
 void set_wave_trace(void* buf, int64_t capacity);

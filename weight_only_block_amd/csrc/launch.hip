@@ -55,8 +55,8 @@ static LaunchOverride current_override()
 // environment knobs of the vllm.cpp pull request #1936 commit log): a comma
 // list of waves=<total waves>, wpcu=<waves per compute unit>, contig=0|1 and
 // ring=2|4|xr (xr: x in registers, where the layout allows it) for the plain
-// kernels, ksplit=1|4|16, xg=0|1 and mmawaves=<waves> for the matrix-core
-// kernel, optionally restricted to one shape with n=<N>, k=<K> and m=<m>
+// kernels, ksplit=1|4|16, xg=0|1, mmawaves=<waves>, mmacu=<work-groups
+// per CU> and mmaeven=0|1 for the matrix-core kernel, optionally restricted to one shape with n=<N>, k=<K> and m=<m>
 // (calls of other shapes are then not forced), and policy=0 to leave out the
 // exact-shape policies below (for A/B runs of the policies themselves).
 // Unknown keys and bad values are ignored; an unset or empty variable
@@ -89,6 +89,8 @@ static LaunchOverride forced_variant(int64_t cus, int64_t N, int64_t K, int m)
         else if (klen == 6 && !strncmp(e, "ksplit", 6) && num && (v == 1 || v == 4 || v == 16)) o.mma_ksplit = int(v);
         else if (klen == 2 && !strncmp(e, "xg", 2) && num && (v == 0 || v == 1)) o.mma_xg = int(v);
         else if (klen == 8 && !strncmp(e, "mmawaves", 8) && num && v > 0 && v <= (1L << 24)) o.mma_waves = v;
+        else if (klen == 5 && !strncmp(e, "mmacu", 5) && num && v >= 1 && v <= 8) o.mma_per_cu = int(v);
+        else if (klen == 7 && !strncmp(e, "mmaeven", 7) && num && (v == 0 || v == 1)) o.mma_even = int(v);
         else if (klen == 4 && !strncmp(e, "ring", 4)) {
             if (num && v == 2) o.shape = SHAPE_D2_W4;
             else if (num && v == 4) o.shape = SHAPE_D4_W4;
@@ -445,10 +447,12 @@ hipError_t launch_mma_sized(int fmt, const MmaParams& kp, size_t lds, hipStream_
         int64_t per_cu = int64_t(kMaxLdsBytes / per_wg);
         int64_t most = split == 16 ? 1 : 2;
         if (pol && pol->per_cu > 0 && split != 16) most = pol->per_cu;
+        if (env.mma_per_cu > 0 && split != 16) most = env.mma_per_cu;
         per_cu = per_cu < 1 ? 1 : (per_cu > most ? most : per_cu);
         const int64_t resident = compute_units() * per_cu;
         int64_t wgs = kp.tiles < resident ? kp.tiles : resident;
-        if (pol && pol->even && kp.tiles > resident) {
+        const bool even = env.mma_even >= 0 ? env.mma_even == 1 : (pol && pol->even);
+        if (even && kp.tiles > resident) {
             const int64_t rounds = (kp.tiles + resident - 1) / resident;
             wgs = (kp.tiles + rounds - 1) / rounds;
         }
