@@ -181,8 +181,9 @@ qg_status qgemv_q8pc(const void *w_packed, const uint16_t *x_bf16, float *y,
  * plain GEMV:
  *   y[i*ldy + n] = sum_k W[n][k] * x[i*ldx + k],  0 <= i < m, 2 <= m <= 16.
  * K must be a multiple of 64 (128 for Q8G128).  The m activation rows are
- * staged in LDS when they fit (m * K * 2 bytes within 159 KiB, less the
- * partial sums of a K split); longer rows are read from memory with each
+ * staged in LDS when they fit (m * K * 2 bytes, plus K * 2 for Q4G32's
+ * per-group activation sums, within 159 KiB, less the partial sums of a K
+ * split); longer rows are read from memory with each
  * weight item instead, so any K is accepted.  Pointers, strides, ownership
  * and errors as qgemv_q8g64, with m = 2..16: m = 1 returns
  * QG_ERR_UNSUPPORTED (single-token decode has no matrix to feed the matrix

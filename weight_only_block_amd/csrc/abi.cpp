@@ -129,9 +129,11 @@ qg_status run_mma(int fmt, int kind, const void* w_packed, const uint16_t* x, fl
     kp.meta_tile_bytes = L.meta_tile_bytes;
     kp.tiles_q = kp.tiles_r = 0;   // set per launch shape
     kp.inv_cpr = 1.0f / float(K / 8);
+    // LDS a work-group needs to stage x: m bf16 rows, and for Q4G32 also
+    // the rows' sums over each 32-group (K / 32 groups x 16 rows of fp32).
+    const size_t staged = size_t(m) * size_t(K) * 2 + (fmt == qg::FMT_Q4G32 ? size_t(K) * 2 : 0);
     (void)hipGetLastError();
-    if (qg::launch_mma_sized(fmt, kp, size_t(m) * size_t(K) * 2, static_cast<hipStream_t>(stream)) !=
-        hipSuccess)
+    if (qg::launch_mma_sized(fmt, kp, staged, static_cast<hipStream_t>(stream)) != hipSuccess)
         return QG_ERR_HIP;
     g_route[kind][m - 1][0].fetch_add(1, std::memory_order_relaxed);
     return QG_OK;

@@ -16,7 +16,9 @@
 // fp32 row scale for Q8PC).  Q4G32 re-centres each 32-group on the integer
 // nearest its zero point (z = clamp(rint(-min / scale), 0, 15), m' =
 // min + scale z), feeds the exact differences c - z as B, and adds the
-// group's activation sum X (a second MFMA against an all-ones B):
+// group's activation sum X (from a per-group table formed once per
+// work-group when x is staged in LDS, else a second MFMA against an
+// all-ones B):
 // acc += s * D + m' * X.  No bias is left inside D, so the rounding error
 // of an output stays a few fp32 ulps of sum |w x| (the same argument as the
 // VALU kernels').  Each output is a complete sum when its tile ends, so
@@ -85,6 +87,26 @@ __device__ __forceinline__ bf16x8 widen_q4(uint32_t u, uint32_t zb)
 __device__ __forceinline__ float half_bits(uint32_t h)
 {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xffffu));
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// acc + the sum of eight bf16 values (four pairs), one v_dot2 per pair.
+// The pairs are copied into plain integers before the bit casts: with
+// this compiler, bit-casting the elements of a vector straight from its
+// reference was lowered as four casts of element 0.
+__device__ __forceinline__ float sum8(u32x4 v, float acc)
+{
+    uint32_t e[4];
+    e[0] = v.x;
+    e[1] = v.y;
+    e[2] = v.z;
+    e[3] = v.w;
+    const bf16x2 one = __builtin_bit_cast(bf16x2, kOnesBf16x2);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, e[q]), one, acc, false);
+    return acc;
 }
 
 // LDS position (16-byte chunk) of chunk c of activation row i: chunks are
@@ -172,8 +194,10 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
         }
         return v;
     };
-    const bool row_live = rho < m;
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    // A rows past m repeat row m - 1: each output row of an MFMA depends on
+    // its own A row only, and rows past m are never stored, so nothing needs
+    // zeroing and no load or LDS read sits behind a per-lane branch.
+    const int xrow = rho < m ? rho : m - 1;
     auto load = [&](MmaItem& it, int64_t tile, int64_t j) {
         it.c = __builtin_nontemporal_load(
             reinterpret_cast<const u32x4*>(code_lane + (tile * J + j) * 1024));
@@ -184,24 +208,21 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
         // (1% on the LM head at m = 8).  A Q8PC row scale is re-read at every
         // step of its tile and stays a plain load (3% slower otherwise).
         else it.s = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(mt + ((j / SPG) * 16 + rho) * 2));
-        // x from memory: lanes past m load row m - 1 (in bounds) and zero
-        // the fragment with a select, so that no load sits in a per-lane
-        // branch (a divergent branch around the loads had made the compiler
-        // keep the ring in scratch memory and wait for every load).
+        // x from memory: row xrow (in bounds for every lane), loaded with no
+        // per-lane branch (a divergent branch around the loads had made the
+        // compiler keep the ring in scratch memory and wait for every load).
         if constexpr (XG && Q4) {
-            // Row rho of x, k = 128 j + 32 g + 8 qs .. + 7 for the four groups g.
-            const uint16_t* src = p.x + int64_t(row_live ? rho : m - 1) * p.ldx + j * 128 + qs * 8;
+            // Row xrow of x, k = 128 j + 32 g + 8 qs .. + 7 for the four groups g.
+            const uint16_t* src = p.x + int64_t(xrow) * p.ldx + j * 128 + qs * 8;
             it.a0 = load_x16(src);
             it.a1 = load_x16(src + 32);
             it.a2 = load_x16(src + 64);
             it.a3 = load_x16(src + 96);
-            if (!row_live) it.a0 = it.a1 = it.a2 = it.a3 = zero4;
         } else if constexpr (XG) {
-            // Row rho of x, k = 64 j + 16 qs .. + 15.
-            const uint16_t* src = p.x + int64_t(row_live ? rho : m - 1) * p.ldx + j * 64 + qs * 16;
+            // Row xrow of x, k = 64 j + 16 qs .. + 15.
+            const uint16_t* src = p.x + int64_t(xrow) * p.ldx + j * 64 + qs * 16;
             it.a0 = load_x16(src);
             it.a1 = load_x16(src + 8);
-            if (!row_live) it.a0 = it.a1 = zero4;
         }
     };
 
@@ -264,11 +285,36 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
         x_store(base);
     }
     __syncthreads();
+    // Q4G32 with x staged: the sums X of each activation row over each
+    // 32-group, formed once per work-group from the staged copy (two chains
+    // of eight v_dot2 against ones, then an add) into a [group][16 rows]
+    // table after x, and read with one LDS load per group.  Rows past m are
+    // not formed: their outputs are never stored.
+    constexpr bool kXTable = Q4 && !XG;
+    float* xtab = reinterpret_cast<float*>(xs + x_total);
+    if constexpr (kXTable) {
+        const int ngroups = cpr / 4;
+        const float inv_ng = 4.0f * p.inv_cpr;
+        for (int idx = threadIdx.x; idx < m * ngroups; idx += kThreads) {
+            int i = int(float(idx) * inv_ng);
+            if (i * ngroups > idx) --i;
+            else if ((i + 1) * ngroups <= idx) ++i;
+            const int gi = idx - i * ngroups;
+            float X0 = 0.f, X1 = 0.f;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                X0 = sum8(xs[xs_chunk(i, 4 * gi + c, cpr)], X0);
+                X1 = sum8(xs[xs_chunk(i, 4 * gi + 2 + c, cpr)], X1);
+            }
+            xtab[gi * 16 + i] = X0 + X1;
+        }
+        __syncthreads();
+    }
     // (With the K split every wave takes part in each tile's closing barrier.)
     if (KSPLIT == 1 && n_items == 0) return;
     // K split: parked partial sums, two buffers of [wave][lane][4] floats
-    // after the staged activations (one barrier per tile).
-    f32x4* part = reinterpret_cast<f32x4*>(xs + x_total);
+    // after the staged activations and the sum table (one barrier per tile).
+    f32x4* part = reinterpret_cast<f32x4*>(xs + x_total + (kXTable ? cpr : 0));
     int buf = 0;
 
     const u32x4 ones4 = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
@@ -279,25 +325,29 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
 
     auto consume = [&](const MmaItem& it) {
         if constexpr (Q4) {
-            // Per 32-group: D = sum x (c - z) and X = sum x (one MFMA each),
-            // then acc += s D + m' X.
+            // Per 32-group: D = sum x (c - z) (one MFMA) and X = sum x (the
+            // table, or a second MFMA against ones when x comes from
+            // memory), then acc += s D + m' X.
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int c = int(j) * 16 + 4 * g + qs;
                 u32x4 au;
                 if constexpr (XG) au = g == 0 ? it.a0 : g == 1 ? it.a1 : g == 2 ? it.a2 : it.a3;
-                else au = row_live ? xs[xs_chunk(rho, c, cpr)] : zero4;
+                else au = xs[xs_chunk(xrow, c, cpr)];
                 const bf16x8 a = __builtin_bit_cast(bf16x8, au);
                 const float s = half_bits(it.m4[g]);
                 const float mn = half_bits(it.m4[g] >> 16);
                 const float t = -mn * __builtin_amdgcn_rcpf(s);
-                // z = clamp(rint(-min / scale), 0, 15); a NaN ratio gives 0.
-                const float z = t >= 0.5f ? (t < 15.0f ? rintf(t) : 15.0f) : 0.0f;
+                // z = clamp(rint(-min / scale), 0, 15), branch-free; a NaN
+                // ratio gives 0 (fmaxf returns the number).
+                const float z = fminf(fmaxf(rintf(t), 0.0f), 15.0f);
                 const float mp = fmaf(s, z, mn);
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
                 const f32x4 Dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     a, widen_q4(it.c[g], __builtin_amdgcn_perm(0u, uint32_t(z), 0u)), zero, 0, 0, 0);
-                const f32x4 Xg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones, zero, 0, 0, 0);
+                f32x4 Xg;
+                if constexpr (XG) Xg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones, zero, 0, 0, 0);
+                else Xg = *reinterpret_cast<const f32x4*>(xtab + ((int(j) * 4 + g) * 16 + 4 * qs));
 #pragma unroll
                 for (int v = 0; v < 4; ++v) acc[v] = fmaf(mp, Xg[v], fmaf(s, Dg[v], acc[v]));
             }
@@ -308,8 +358,8 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
                 a0u = it.a0;
                 a1u = it.a1;
             } else {
-                a0u = row_live ? xs[xs_chunk(rho, c0, cpr)] : zero4;
-                a1u = row_live ? xs[xs_chunk(rho, c0 + 1, cpr)] : zero4;
+                a0u = xs[xs_chunk(xrow, c0, cpr)];
+                a1u = xs[xs_chunk(xrow, c0 + 1, cpr)];
             }
             const bf16x8 a0 = __builtin_bit_cast(bf16x8, a0u);
             const bf16x8 a1 = __builtin_bit_cast(bf16x8, a1u);
