@@ -12,8 +12,9 @@
 //    lane div 16 in lane order), widened to bf16 (every int8 is exact).
 //  * D (16 x 16, fp32): lane l holds D[4*(l div 16) + v][l mod 16].
 //
-// Per scale group:  acc += s * D   (s: the row's fp16 group scale, or its
-// fp32 row scale for Q8PC).  Q4G32 re-centres each 32-group on the integer
+// Per scale group:  acc += s * D   (s: the row's fp16 group scale); Q8PC's
+// one fp32 row scale multiplies the D of a whole tile (or of a wave's part
+// of it) once, at its end.  Q4G32 re-centres each 32-group on the integer
 // nearest its zero point (z = clamp(rint(-min / scale), 0, 15), m' =
 // min + scale z), feeds the exact differences c - z as B, and adds the
 // group's activation sum X (from a per-group table formed once per
@@ -150,9 +151,9 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
     const int m = p.m;
     const int64_t J = p.J;
     const int cpr = int(p.K / 8);   // 16-byte chunks per activation row
-    // Steps per scale group: 1 (Q8G64, and Q8PC, whose row scale is applied
-    // per step), 2 (Q8G128).  A Q4G32 step (128 K) holds four whole groups,
-    // so K splits fall between steps there too.
+    // Steps per scale group: 1 (Q8G64), 2 (Q8G128); Q8PC scales once per
+    // tile.  A Q4G32 step (128 K) holds four whole groups, so K splits fall
+    // between steps there too.
     constexpr int SPG = FMT == FMT_Q8G128 ? 2 : 1;
     constexpr bool Q4 = FMT == FMT_Q4G32;
     static_assert(!(XG && KSPLIT == 16), "x from memory is built for whole tiles or four waves");
@@ -198,10 +199,26 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
     // its own A row only, and rows past m are never stored, so nothing needs
     // zeroing and no load or LDS read sits behind a per-lane branch.
     const int xrow = rho < m ? rho : m - 1;
-    auto load = [&](MmaItem& it, int64_t tile, int64_t j) {
-        it.c = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(code_lane + (tile * J + j) * 1024));
-        const uint8_t* mt = meta + tile * p.meta_tile_bytes;
+    // Load cursor: the step j of the next item to load and the byte offsets
+    // of its code block and of its tile's meta, advanced by additions (the
+    // jump to the wave's next tile is the same every time).
+    struct Cursor {
+        int64_t j, code, meta;
+    };
+    const int64_t jump_code = (W * J + j_lo - j_hi) * 1024;
+    const int64_t jump_meta = W * p.meta_tile_bytes;
+    auto advance = [&](Cursor& cu) {
+        cu.code += 1024;
+        if (++cu.j == j_hi) {
+            cu.j = j_lo;
+            cu.code += jump_code;
+            cu.meta += jump_meta;
+        }
+    };
+    auto load = [&](MmaItem& it, const Cursor& cu) {
+        const int64_t j = cu.j;
+        it.c = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(code_lane + cu.code));
+        const uint8_t* mt = meta + cu.meta;
         if constexpr (Q4) it.m4 = *reinterpret_cast<const u32x4*>(mt + (j * 16 + rho) * 16);
         else if (FMT == FMT_Q8PC) it.s = *reinterpret_cast<const uint32_t*>(mt + rho * 4);
         // Group scales are read once per call: non-temporal, like the codes
@@ -267,15 +284,16 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
 
     // Spare ring slots load item 0 of the matrix (never consumed) so every
     // path issues the same loads.
-    int64_t ld_tile = gw, ld_j = j_lo;
+    Cursor ld = {j_lo, (gw * J + j_lo) * 1024, gw * p.meta_tile_bytes};
+    const Cursor spare = {0, 0, 0};
     MmaItem ring[DEPTH];
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
         if (d < n_items) {
-            load(ring[d], ld_tile, ld_j);
-            if (++ld_j == j_hi) { ld_j = j_lo; ld_tile += W; }
+            load(ring[d], ld);
+            advance(ld);
         } else {
-            load(ring[d], 0, 0);
+            load(ring[d], spare);
         }
     }
 
@@ -365,16 +383,29 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
             const bf16x8 a1 = __builtin_bit_cast(bf16x8, a1u);
             const bf16x8 b0 = widen8(it.c.x, it.c.y);
             const bf16x8 b1 = widen8(it.c.z, it.c.w);
-            if (j % SPG == 0) D = f32x4{0.f, 0.f, 0.f, 0.f};
-            D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, D, 0, 0, 0);
-            D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, D, 0, 0, 0);
-            if (j % SPG == SPG - 1) {
-                const float s = FMT == FMT_Q8PC ? __uint_as_float(it.s) : half_bits(it.s);
+            if constexpr (FMT == FMT_Q8PC) {
+                // One fp32 scale per row: the products of all the wave's
+                // steps of the tile accumulate in D, scaled once at its end.
+                D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, D, 0, 0, 0);
+                D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, D, 0, 0, 0);
+            } else {
+                if (j % SPG == 0) D = f32x4{0.f, 0.f, 0.f, 0.f};
+                D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, D, 0, 0, 0);
+                D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, D, 0, 0, 0);
+                if (j % SPG == SPG - 1) {
+                    const float s = half_bits(it.s);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[v] = fmaf(s, D[v], acc[v]);
+                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(s, D[v], acc[v]);
+                }
             }
         }
         if (++j == j_hi) {
+            if constexpr (FMT == FMT_Q8PC) {
+                const float s = __uint_as_float(it.s);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] = s * D[v];
+                D = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
             if constexpr (KSPLIT == 1) {
                 const int64_t row = tile * 16 + rho;
 #pragma unroll
@@ -410,8 +441,8 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
             consume(ring[d]);
-            load(ring[d], ld_tile, ld_j);
-            if (++ld_j == j_hi) { ld_j = j_lo; ld_tile += W; }
+            load(ring[d], ld);
+            advance(ld);
         }
     }
 #pragma unroll
@@ -419,8 +450,8 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
         if (n + d < n_items) {
             consume(ring[d]);
             if (n + DEPTH + d < n_items) {
-                load(ring[d], ld_tile, ld_j);
-                if (++ld_j == j_hi) { ld_j = j_lo; ld_tile += W; }
+                load(ring[d], ld);
+                advance(ld);
             }
         }
     }
