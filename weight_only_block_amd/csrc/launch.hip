@@ -373,15 +373,16 @@ static const MmaShapePolicy kMmaPolicy[] = {
     {FMT_Q8PC, 4, 5120, 4352, 0, true, -1, -1},
     // gate/up, m = 8: even rounds 49.14 -> 47.81 (5/5)
     {FMT_Q8PC, 8, 8704, 5120, 0, true, -1, -1},
-    // gate/up, m = 16 (x read from memory): three work-groups per CU, so the
-    // 544 tiles run in one round, 78.57 -> 75.28 (5/5)
-    {FMT_Q8PC, 16, 8704, 5120, 3, false, -1, -1},
-    // o 1280 -> 5120, m = 16: x read from memory, 75.02 -> 74.38 (5/5)
+    // o 1280 -> 5120: a four-way K split with x read from memory, m = 4
+    // 43.86 -> 42.87, m = 8 45.47 -> 44.61, m = 16 75.02 -> 74.38 (5/5 each)
+    {FMT_Q8PC, 4, 5120, 1280, 0, false, 4, 1},
+    {FMT_Q8PC, 8, 5120, 1280, 0, false, 4, 1},
     {FMT_Q8PC, 16, 5120, 1280, 0, false, 4, 1},
-    // Q4G32 gate/up 2560 -> 9216, m = 16: sixteen waves share each tile
-    // (one staged copy of x per CU instead of one per four-wave group),
-    // three-GEMV step 58.86 -> 51.23 (5/5)
-    {FMT_Q4G32, 16, 9216, 2560, 0, false, 16, -1},
+    // Q4G32 gate/up 2560 -> 9216, m = 16: a four-way K split with x read
+    // from memory, three-GEMV step 47.38 -> 45.90 (5/5; it had taken a
+    // sixteen-way split, 58.86 -> 51.23, before the per-group sums moved
+    // into an LDS table)
+    {FMT_Q4G32, 16, 9216, 2560, 0, false, 4, 1},
     {-1, 0, 0, 0, 0, false, -1, -1},   // (end)
 };
 
