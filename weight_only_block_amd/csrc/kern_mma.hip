@@ -339,6 +339,10 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
     const bf16x8 ones = __builtin_bit_cast(bf16x8, ones4);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     f32x4 D = acc;
+    // Group scaling deferred by one step (group formats): the last finished
+    // group's D and scale, zero when none is pending.
+    f32x4 D_done = acc;
+    float s_done = 0.f;
     int64_t tile = gw, j = j_lo;
 
     auto consume = [&](const MmaItem& it) {
@@ -389,13 +393,20 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
                 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, D, 0, 0, 0);
                 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, D, 0, 0, 0);
             } else {
-                if (j % SPG == 0) D = f32x4{0.f, 0.f, 0.f, 0.f};
+                // A finished group's acc += s D waits until the next
+                // group's MFMAs are issued, so the wave does not stall on
+                // the MFMA result; the adds keep their order (the same bits).
+                const bool opens = j % SPG == 0;
+                if (opens) D = f32x4{0.f, 0.f, 0.f, 0.f};
                 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, D, 0, 0, 0);
                 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, D, 0, 0, 0);
-                if (j % SPG == SPG - 1) {
-                    const float s = half_bits(it.s);
+                if (opens) {
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(s, D[v], acc[v]);
+                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(s_done, D_done[v], acc[v]);
+                }
+                if (j % SPG == SPG - 1) {
+                    D_done = D;
+                    s_done = half_bits(it.s);
                 }
             }
         }
@@ -405,6 +416,13 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
 #pragma unroll
                 for (int v = 0; v < 4; ++v) acc[v] = s * D[v];
                 D = f32x4{0.f, 0.f, 0.f, 0.f};
+            } else if constexpr (!Q4) {
+                // The tile's last group; the next tile opens with a zero
+                // pending group (0 * 0 added to a zero acc leaves +0).
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] = fmaf(s_done, D_done[v], acc[v]);
+                D_done = f32x4{0.f, 0.f, 0.f, 0.f};
+                s_done = 0.f;
             }
             if constexpr (KSPLIT == 1) {
                 const int64_t row = tile * 16 + rho;
