@@ -89,9 +89,9 @@ def test_lm_head_batched_full_size(fmt, m):
     check(fmt, q, s, x, y, "lm_head %s m=%d" % (fmt, m))
 
 
-# m = 4, 8 and 16 take the shape policy's work-group counts on some of
-# these shapes (even rounds, three work-groups per CU).
-@pytest.mark.parametrize("m", [4, 8, 15, 16])
+# m = 2 to 4, 8 and 16 take the shape policy's launch choices on some of
+# these shapes (even rounds; a four-way K split with x read from memory).
+@pytest.mark.parametrize("m", [2, 3, 4, 8, 15, 16])
 @pytest.mark.parametrize("j,label,N,K", [(j, c[0], c[2], c[3])
                                          for j, c in enumerate(synth.W8A16_QWEN3_14B_TP4)])
 def test_w8a16_qwen3_14b_tp4_batched(j, label, N, K, m):

@@ -359,7 +359,7 @@ hipError_t launch(const LaunchArgs& a)
 // 16) and xg (0: x staged, 1: x read from memory) as the keys of
 // QG_FORCE_VARIANT (-1: the default choice).
 struct MmaShapePolicy {
-    int fmt, m;
+    int fmt, m_lo, m_hi;   // the entry covers m_lo <= m <= m_hi
     int64_t N, K;
     int per_cu;
     bool even;
@@ -367,30 +367,34 @@ struct MmaShapePolicy {
     int xg;
 };
 static const MmaShapePolicy kMmaPolicy[] = {
-    // gate/up 5120 -> 8704, m = 4: even rounds 48.03 -> 46.57 (5/5)
-    {FMT_Q8PC, 4, 8704, 5120, 0, true, -1, -1},
-    // down 4352 -> 5120, m = 4: even rounds 48.05 -> 47.70 (5/5)
-    {FMT_Q8PC, 4, 5120, 4352, 0, true, -1, -1},
+    // gate/up 5120 -> 8704, m = 4: even rounds 48.03 -> 46.57 (5/5); after
+    // the per-tile Q8PC scaling, m = 2 45.69 -> 44.00, m = 3 45.71 -> 44.07
+    // (5/5 each)
+    {FMT_Q8PC, 2, 4, 8704, 5120, 0, true, -1, -1},
+    // down 4352 -> 5120, m = 4: even rounds 48.05 -> 47.70 (5/5); m = 2
+    // 45.69 -> 45.37, m = 3 45.75 -> 45.45 (5/5 each)
+    {FMT_Q8PC, 2, 4, 5120, 4352, 0, true, -1, -1},
     // gate/up, m = 8: even rounds 49.14 -> 47.81 (5/5)
-    {FMT_Q8PC, 8, 8704, 5120, 0, true, -1, -1},
+    {FMT_Q8PC, 8, 8, 8704, 5120, 0, true, -1, -1},
     // o 1280 -> 5120: a four-way K split with x read from memory, m = 4
-    // 43.86 -> 42.87, m = 8 45.47 -> 44.61, m = 16 75.02 -> 74.38 (5/5 each)
-    {FMT_Q8PC, 4, 5120, 1280, 0, false, 4, 1},
-    {FMT_Q8PC, 8, 5120, 1280, 0, false, 4, 1},
-    {FMT_Q8PC, 16, 5120, 1280, 0, false, 4, 1},
+    // 43.86 -> 42.87, m = 8 45.47 -> 44.61, m = 16 75.02 -> 74.38; m = 2
+    // 45.70 -> 44.70, m = 3 45.73 -> 44.75 (5/5 each)
+    {FMT_Q8PC, 2, 4, 5120, 1280, 0, false, 4, 1},
+    {FMT_Q8PC, 8, 8, 5120, 1280, 0, false, 4, 1},
+    {FMT_Q8PC, 16, 16, 5120, 1280, 0, false, 4, 1},
     // Q4G32 gate/up 2560 -> 9216, m = 16: a four-way K split with x read
     // from memory, three-GEMV step 47.38 -> 45.90 (5/5; it had taken a
     // sixteen-way split, 58.86 -> 51.23, before the per-group sums moved
     // into an LDS table)
-    {FMT_Q4G32, 16, 9216, 2560, 0, false, 4, 1},
-    {-1, 0, 0, 0, 0, false, -1, -1},   // (end)
+    {FMT_Q4G32, 16, 16, 9216, 2560, 0, false, 4, 1},
+    {-1, 0, 0, 0, 0, 0, false, -1, -1},   // (end)
 };
 
 static const MmaShapePolicy* mma_policy_for(int fmt, int m, int64_t N, int64_t K)
 {
     for (const MmaShapePolicy& e : kMmaPolicy) {
         if (e.fmt < 0) break;
-        if (e.fmt == fmt && e.m == m && e.N == N && e.K == K) return &e;
+        if (e.fmt == fmt && e.m_lo <= m && m <= e.m_hi && e.N == N && e.K == K) return &e;
     }
     return nullptr;
 }
