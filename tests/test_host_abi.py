@@ -356,36 +356,65 @@ def test_mma_pack_roundtrip_sizes_and_validation(fmt):
     assert Q.variant_name(fid, 16, 151936, 2560) == "%s_mma_m16" % fmt
 
 
+def test_q8g64_mma_pack_layout():
+    # The 8-bit matrix-core packing against the documented formula: block
+    # (tile t, step j) at (t J + j) KiB, lane l = 16 qs + rho holding the
+    # codes of row 16 t + rho at k = 64 j + 16 qs .. + 15; then the fp16
+    # scales at [tile][group][row].
+    N = 40
+    for K in (192, 1280):
+        q = ((np.arange(N)[:, None] * 5 + np.arange(K)[None, :] * 3) % 251 - 125).astype(np.int8)
+        sc = (np.arange(N * K // 64, dtype=np.uint16).reshape(N, K // 64) + 0x3C00).astype(np.uint16)
+        buf = Q.qpack_q8g64_mma(q, sc)
+        # float16 arrays are taken as their bits; other float arrays are refused.
+        assert np.array_equal(Q.qpack_q8g64_mma(q, sc.view(np.float16)), buf)
+        with pytest.raises(Q.QGError):
+            Q.qpack_q8g64_mma(q, sc.view(np.float16).astype(np.float32))
+        tiles, J = (N + 15) // 16, K // 64
+        for (t, j, qs, rho) in [(0, 0, 0, 0), (1, J - 1, 3, 7), (2, J // 2, 1, 7), (1, 1, 2, 15)]:
+            n = 16 * t + rho
+            off = (t * J + j) * 1024 + (16 * qs + rho) * 16
+            assert np.array_equal(buf[off:off + 16].view(np.int8), q[n, 64 * j + 16 * qs:64 * j + 16 * qs + 16])
+            moff = tiles * J * 1024 + (t * J + j) * 32 + rho * 2
+            assert int(buf[moff:moff + 2].view(np.uint16)[0]) == int(sc[n, j])
+
+
 def test_q4g32_mma_pack_layout_and_roundtrip():
     # Layout of the Q4G32 matrix-core packing, checked against the
     # documented formula: in block (tile t, step j), lane l = 16 qs + rho,
     # dword g holds the codes of row 16 t + rho at k = 128 j + 32 g + 8 qs + e
     # in canonical byte order (e at nibble position e: byte e // 2, low
-    # nibble for even e); then the meta dwords scale | min << 16 at
-    # [tile][step][row][group].
-    N, K = 37, 384
-    n_idx = np.arange(N)[:, None]
-    k_idx = np.arange(K)[None, :]
-    c = (k_idx * 7 + n_idx * 3) % 16
-    codes = synth.pack_nibbles(c)
-    s = (np.arange(N * K // 32, dtype=np.uint16).reshape(N, K // 32) + 0x3C00).astype(np.uint16)
-    mn = (np.arange(N * K // 32, dtype=np.uint16).reshape(N, K // 32) + 0x8000).astype(np.uint16)
-    buf = Q.qpack_q4g32_mma(codes, s, mn)
-    tiles, J = (N + 15) // 16, K // 128
-    assert buf.nbytes == Q.qpack_mma_size("q4g32", N, K) == -(-(tiles * J * 1024 + tiles * J * 256) // 256) * 256
-    pos = tuple(range(8))
-    for (t, j, qs, rho, g) in [(0, 0, 0, 0, 0), (1, 2, 3, 5, 1), (2, 1, 2, 4, 3), (0, 2, 1, 15, 2)]:
-        n = 16 * t + rho
-        word = int(buf[(t * J + j) * 1024 + (16 * qs + rho) * 16 + 4 * g:][:4].view(np.uint32)[0])
-        for e in range(8):
-            assert (word >> (4 * pos[e])) & 15 == c[n, 128 * j + 32 * g + 8 * qs + e]
-        meta = buf[tiles * J * 1024 + ((t * J + j) * 16 + rho) * 16 + 4 * g:][:4].view(np.uint16)
-        assert meta[0] == s[n, 4 * j + g] and meta[1] == mn[n, 4 * j + g]
-    # Padding rows of the last tile are all zero.
-    pad = buf[(2 * J) * 1024:(3 * J) * 1024].reshape(J, 64, 16)[:, [16 * q + r for q in range(4) for r in range(5, 16)]]
-    assert not pad.any()
-    c2, s2, m2 = Q.qunpack_mma("q4g32", buf, N, K)
-    assert np.array_equal(c2, codes) and np.array_equal(s2, s) and np.array_equal(m2, mn)
+    # nibble for even e); the block sits at (t J + j) KiB; then the meta
+    # dwords scale | min << 16 at [tile][step][row][group].
+    N = 37
+    for K in (384, 1024):
+        n_idx = np.arange(N)[:, None]
+        k_idx = np.arange(K)[None, :]
+        c = (k_idx * 7 + n_idx * 3) % 16
+        codes = synth.pack_nibbles(c)
+        s = (np.arange(N * K // 32, dtype=np.uint16).reshape(N, K // 32) + 0x3C00).astype(np.uint16)
+        mn = (np.arange(N * K // 32, dtype=np.uint16).reshape(N, K // 32) + 0x8000).astype(np.uint16)
+        buf = Q.qpack_q4g32_mma(codes, s, mn)
+        tiles, J = (N + 15) // 16, K // 128
+        assert buf.nbytes == Q.qpack_mma_size("q4g32", N, K) == -(-(tiles * J * 1024 + tiles * J * 256) // 256) * 256
+
+        def block(t, j):
+            return (t * J + j) * 1024
+
+        pos = tuple(range(8))
+        for (t, j, qs, rho, g) in [(0, 0, 0, 0, 0), (1, 2, 3, 5, 1), (2, 1, 2, 4, 3), (0, 2, 1, 15, 2),
+                                   (1, J - 1, 0, 7, 0), (2, J - 1, 3, 3, 2)]:
+            n = 16 * t + rho
+            word = int(buf[block(t, j) + (16 * qs + rho) * 16 + 4 * g:][:4].view(np.uint32)[0])
+            for e in range(8):
+                assert (word >> (4 * pos[e])) & 15 == c[n, 128 * j + 32 * g + 8 * qs + e]
+            meta = buf[tiles * J * 1024 + ((t * J + j) * 16 + rho) * 16 + 4 * g:][:4].view(np.uint16)
+            assert meta[0] == s[n, 4 * j + g] and meta[1] == mn[n, 4 * j + g]
+        # Padding rows of the last tile are all zero.
+        pad = np.stack([buf[block(2, j):block(2, j) + 1024] for j in range(J)]).reshape(J, 64, 16)
+        assert not pad[:, [16 * q + r for q in range(4) for r in range(5, 16)]].any()
+        c2, s2, m2 = Q.qunpack_mma("q4g32", buf, N, K)
+        assert np.array_equal(c2, codes) and np.array_equal(s2, s) and np.array_equal(m2, mn)
     assert Q.qpack_mma_size("q4g32", N, 320) == 0          # K not a multiple of 128
     f = Q.lib().qgemv_q4g32_mma
     assert f(W, X, Y, 2, 16, 320, 320, 16, None) == Q.QG_ERR_INVALID_ARG

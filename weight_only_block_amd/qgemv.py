@@ -222,10 +222,23 @@ def qpack_q4g32_size(N: int, K: int) -> int:
     return int(lib().qpack_q4g32_size(N, K))
 
 
+def _fp16_bits(a, where: str) -> np.ndarray:
+    """fp16 scales or mins as their uint16 bit patterns: float16 arrays are
+    reinterpreted, integer arrays taken as the bit patterns themselves, and
+    other float arrays refused (converting them by value would pack wrong
+    bits)."""
+    a = np.asarray(a)
+    if a.dtype == np.float16:
+        return np.ascontiguousarray(a).view(np.uint16)
+    if a.dtype.kind == "f":
+        raise QGError(QG_ERR_INVALID_ARG, where + " (fp16 values must be float16 or uint16 bit patterns)")
+    return np.ascontiguousarray(a, dtype=np.uint16)
+
+
 def qpack_q8g64(q: np.ndarray, scales_f16: np.ndarray) -> np.ndarray:
     """Canonical q [N][K] int8 and scales [N][K/64] fp16 bits -> packed uint8 buffer."""
     q = np.ascontiguousarray(q, dtype=np.int8)
-    s = np.ascontiguousarray(scales_f16, dtype=np.uint16)
+    s = _fp16_bits(scales_f16, "qpack_q8g64")
     N, K = q.shape
     size = qpack_q8g64_size(N, K)
     if size == 0 or s.shape != (N, K // 64):
@@ -255,7 +268,7 @@ def qpack_q8pc_size(N: int, K: int) -> int:
 def qpack_q8g128(q: np.ndarray, scales_f16: np.ndarray) -> np.ndarray:
     """Canonical q [N][K] int8 and scales [N][K/128] fp16 bits -> packed uint8 buffer."""
     q = np.ascontiguousarray(q, dtype=np.int8)
-    s = np.ascontiguousarray(scales_f16, dtype=np.uint16)
+    s = _fp16_bits(scales_f16, "qpack_q8g128")
     N, K = q.shape
     size = qpack_q8g128_size(N, K)
     if size == 0 or s.shape != (N, K // 128):
@@ -278,9 +291,8 @@ def qpack_q8pc(q: np.ndarray, scales_f32: np.ndarray) -> np.ndarray:
     """Canonical q [N][K] int8 and one fp32 scale per row (float32 [N], or its
     bit patterns as uint32) -> packed uint8 buffer."""
     q = np.ascontiguousarray(q, dtype=np.int8)
-    s = np.ascontiguousarray(scales_f32)
-    if s.dtype != np.uint32:
-        s = np.ascontiguousarray(s, dtype=np.float32)
+    s = np.asarray(scales_f32)
+    s = np.ascontiguousarray(s, dtype=np.float32 if s.dtype.kind == "f" else np.uint32)
     N, K = q.shape
     size = qpack_q8pc_size(N, K)
     if size == 0 or s.shape != (N,):
@@ -304,8 +316,8 @@ def qpack_q4g32(codes: np.ndarray, scales_f16: np.ndarray, mins_f16: np.ndarray)
     """Canonical codes [N][K/2] (even k in the low nibble), scales and mins
     [N][K/32] fp16 bits -> packed uint8 buffer."""
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
-    s = np.ascontiguousarray(scales_f16, dtype=np.uint16)
-    mn = np.ascontiguousarray(mins_f16, dtype=np.uint16)
+    s = _fp16_bits(scales_f16, "qpack_q4g32")
+    mn = _fp16_bits(mins_f16, "qpack_q4g32")
     N, half_k = codes.shape
     K = 2 * half_k
     size = qpack_q4g32_size(N, K)
@@ -329,9 +341,13 @@ def qunpack_q4g32(packed: np.ndarray, N: int, K: int):
 
 def _mma_pack(fmt, q, scales, scale_dtype, scale_shape):
     q = np.ascontiguousarray(q, dtype=np.int8)
-    s = np.ascontiguousarray(scales)
-    if s.dtype != scale_dtype:
-        s = np.ascontiguousarray(s, dtype=scale_dtype if scale_dtype != np.uint32 else np.float32)
+    if scale_dtype == np.uint16:
+        s = _fp16_bits(scales, "qpack_%s_mma" % fmt)
+    else:
+        # Q8PC: float arrays by value (as float32), integer arrays as the
+        # float32 bit patterns.
+        s = np.asarray(scales)
+        s = np.ascontiguousarray(s, dtype=np.float32 if s.dtype.kind == "f" else np.uint32)
     N, K = q.shape
     size = int(getattr(lib(), "qpack_%s_mma_size" % fmt)(N, K))
     if size == 0 or s.shape != scale_shape(N, K):
@@ -362,8 +378,8 @@ def qpack_q4g32_mma(codes: np.ndarray, scales_f16: np.ndarray, mins_f16: np.ndar
     """Q4G32 canonical arrays (as qpack_q4g32) in the matrix-core layout
     (for qgemv_q4g32_mma; K % 128 == 0)."""
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
-    s = np.ascontiguousarray(scales_f16, dtype=np.uint16)
-    mn = np.ascontiguousarray(mins_f16, dtype=np.uint16)
+    s = _fp16_bits(scales_f16, "qpack_q4g32_mma")
+    mn = _fp16_bits(mins_f16, "qpack_q4g32_mma")
     N, half_k = codes.shape
     K = 2 * half_k
     size = qpack_mma_size("q4g32", N, K)
