@@ -346,16 +346,42 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
     int64_t tile = gw, j = j_lo;
 
     auto consume = [&](const MmaItem& it) {
-        if constexpr (Q4) {
-            // Per 32-group: D = sum x (c - z) (one MFMA) and X = sum x (the
-            // table, or a second MFMA against ones when x comes from
-            // memory), then acc += s D + m' X.
+        if constexpr (Q4 && !XG) {
+            // Per 32-group: D = sum x (c - z) (one MFMA) and X = sum x from
+            // the table, then acc += s D + m' X.  The four groups' MFMAs
+            // are issued first, into separate results, so that no group
+            // waits for the one before it; the adds keep the group order.
+            f32x4 Dq[4];
+            float sq[4], mq[4];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int c = int(j) * 16 + 4 * g + qs;
-                u32x4 au;
-                if constexpr (XG) au = g == 0 ? it.a0 : g == 1 ? it.a1 : g == 2 ? it.a2 : it.a3;
-                else au = xs[xs_chunk(xrow, c, cpr)];
+                const bf16x8 a = __builtin_bit_cast(bf16x8, xs[xs_chunk(xrow, c, cpr)]);
+                const float s = half_bits(it.m4[g]);
+                const float mn = half_bits(it.m4[g] >> 16);
+                const float t = -mn * __builtin_amdgcn_rcpf(s);
+                // z = clamp(rint(-min / scale), 0, 15), branch-free; a NaN
+                // ratio gives 0 (fmaxf returns the number).
+                const float z = fminf(fmaxf(rintf(t), 0.0f), 15.0f);
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                Dq[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    a, widen_q4(it.c[g], __builtin_amdgcn_perm(0u, uint32_t(z), 0u)), zero, 0, 0, 0);
+                sq[g] = s;
+                mq[g] = fmaf(s, z, mn);
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 Xg = *reinterpret_cast<const f32x4*>(xtab + ((int(j) * 4 + g) * 16 + 4 * qs));
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] = fmaf(mq[g], Xg[v], fmaf(sq[g], Dq[g][v], acc[v]));
+            }
+        } else if constexpr (Q4) {
+            // x from memory: as above, with X = a second MFMA against ones,
+            // group by group (four pending groups would not fit in
+            // registers beside this variant's ring).
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const u32x4 au = g == 0 ? it.a0 : g == 1 ? it.a1 : g == 2 ? it.a2 : it.a3;
                 const bf16x8 a = __builtin_bit_cast(bf16x8, au);
                 const float s = half_bits(it.m4[g]);
                 const float mn = half_bits(it.m4[g] >> 16);
@@ -367,9 +393,7 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
                 const f32x4 Dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     a, widen_q4(it.c[g], __builtin_amdgcn_perm(0u, uint32_t(z), 0u)), zero, 0, 0, 0);
-                f32x4 Xg;
-                if constexpr (XG) Xg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones, zero, 0, 0, 0);
-                else Xg = *reinterpret_cast<const f32x4*>(xtab + ((int(j) * 4 + g) * 16 + 4 * qs));
+                const f32x4 Xg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones, zero, 0, 0, 0);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) acc[v] = fmaf(mp, Xg[v], fmaf(s, Dg[v], acc[v]));
             }
