@@ -118,6 +118,20 @@ def test_ragged_shapes_and_strides(fmt, K, N, m):
     check(fmt, q, s, x, y[:, :N], "%s N=%d K=%d m=%d" % (fmt, N, K, m))
 
 
+# Rows of x that are not a whole number of 128-wide groups (K = 64 mod
+# 128) are swizzled in LDS in groups of 8 chunks instead of 16.
+@pytest.mark.parametrize("m", [2, 9, 16])
+@pytest.mark.parametrize("N,K", [(1000, 320), (70000, 192), (40, 1344)])
+@pytest.mark.parametrize("fmt", ["q8g64", "q8pc"])
+def test_rows_of_an_odd_number_of_steps(fmt, N, K, m):
+    gen = FMT[fmt][0]
+    rng = synth.rng_for(112, N, K, m)
+    q, s = gen(rng, N, K)
+    x = synth.activations(rng, m, K)
+    y = run(fmt, q, s, x)
+    check(fmt, q, s, x, y, "%s N=%d K=%d m=%d" % (fmt, N, K, m))
+
+
 # The launch picks how a tile's K is shared: by no wave (many tiles), by
 # the four waves of a work-group (4..63 scale groups per row), or by
 # sixteen (64 or more groups, when the staged x leaves room in LDS); where

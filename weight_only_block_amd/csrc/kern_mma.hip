@@ -199,6 +199,15 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
     // its own A row only, and rows past m are never stored, so nothing needs
     // zeroing and no load or LDS read sits behind a per-lane branch.
     const int xrow = rho < m ? rho : m - 1;
+    // Reads of the staged x: the swizzle moves chunk c of row xrow within
+    // its group of 8, and a step's chunks (8 j + t, t < 8, for the 8-bit
+    // formats; 16 j + u, u < 16, for Q4G32) keep their multiple of 8, so
+    // each lane's places within a step are constants and a step adds j.
+    const u32x4* xs_row = xs + xrow * cpr;
+    const int o0 = (2 * qs) ^ (xrow & 7), o1 = (2 * qs + 1) ^ (xrow & 7);
+    int oq[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) oq[g] = (4 * g + qs) ^ (xrow & 7);
     // Load cursor: the step j of the next item to load and the byte offsets
     // of its code block and of its tile's meta, advanced by additions (the
     // jump to the wave's next tile is the same every time).
@@ -355,8 +364,7 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
             float sq[4], mq[4];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int c = int(j) * 16 + 4 * g + qs;
-                const bf16x8 a = __builtin_bit_cast(bf16x8, xs[xs_chunk(xrow, c, cpr)]);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, xs_row[int(j) * 16 + oq[g]]);
                 const float s = half_bits(it.m4[g]);
                 const float mn = half_bits(it.m4[g] >> 16);
                 const float t = -mn * __builtin_amdgcn_rcpf(s);
@@ -398,14 +406,13 @@ __global__ __launch_bounds__(mma_threads<KSPLIT>()) void qgemv_mma(const MmaPara
                 for (int v = 0; v < 4; ++v) acc[v] = fmaf(mp, Xg[v], fmaf(s, Dg[v], acc[v]));
             }
         } else {
-            const int c0 = int(j) * 8 + 2 * qs;
             u32x4 a0u, a1u;
             if constexpr (XG) {
                 a0u = it.a0;
                 a1u = it.a1;
             } else {
-                a0u = xs[xs_chunk(xrow, c0, cpr)];
-                a1u = xs[xs_chunk(xrow, c0 + 1, cpr)];
+                a0u = xs_row[int(j) * 8 + o0];
+                a1u = xs_row[int(j) * 8 + o1];
             }
             const bf16x8 a0 = __builtin_bit_cast(bf16x8, a0u);
             const bf16x8 a1 = __builtin_bit_cast(bf16x8, a1u);
