@@ -1,12 +1,16 @@
 // Batched decode GEMV (m = 2..16 activation rows) on the gfx950 matrix
-// cores, for the 8-bit formats in the matrix-core layout (layout.h,
-// MmaLayout).  The larger-batch decode of the Qwen3 C++ Reference Runtime
-// (MetaInfer-cpp) README ("B8/B16" kernels with the input rows reused from
-// LDS) is the operation; with up to 16 rows sharing each weight the dot
-// products become a 16 x 16 x 32 bf16 matrix product per 64-wide step:
+// cores, for the 8-bit formats and Q4G32 in the matrix-core layout
+// (layout.h, MmaLayout).  The larger-batch decode of the Qwen3 C++
+// Reference Runtime (MetaInfer-cpp) README ("B8/B16" kernels with the input
+// rows reused from LDS) is the operation; with up to 16 rows sharing each
+// weight the dot products become a 16 x 16 x 32 bf16 matrix product per 32
+// of K (two per 64-wide step of the 8-bit formats, four per 128-wide step
+// of Q4G32):
 //
-//  * A (16 x 32): the activation rows (row i = lane mod 16, zero past m),
-//    read from LDS, where x is staged once per work-group.
+//  * A (16 x 32): the activation rows (row i = lane mod 16; rows past m
+//    repeat row m - 1, whose outputs are never stored), read from LDS,
+//    where x is staged once per work-group, or from memory with each item
+//    when the rows are too long to stage.
 //  * B (32 x 16): 16 weight rows, 16 signed codes per lane exactly as one
 //    wave load brings them in (the layout puts row lane mod 16, k-slice
 //    lane div 16 in lane order), widened to bf16 (every int8 is exact).
