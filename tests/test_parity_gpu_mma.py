@@ -132,6 +132,20 @@ def test_rows_of_an_odd_number_of_steps(fmt, N, K, m):
     check(fmt, q, s, x, y, "%s N=%d K=%d m=%d" % (fmt, N, K, m))
 
 
+# Whole tiles per wave (many rows) with activation rows that are 4-byte but
+# not 16-byte aligned: x is staged into LDS in 4-byte pieces.
+@pytest.mark.parametrize("m", [2, 7, 16])
+@pytest.mark.parametrize("fmt", ["q8g64", "q8g128", "q8pc"])
+def test_whole_tiles_with_unaligned_rows(fmt, m):
+    N, K = 70000, 256
+    gen = FMT[fmt][0]
+    rng = synth.rng_for(113, m)
+    q, s = gen(rng, N, K)
+    x = synth.activations(rng, m, K)
+    y = run(fmt, q, s, x, ldx=K + 2)
+    check(fmt, q, s, x, y, "%s N=%d K=%d m=%d ldx=K+2" % (fmt, N, K, m))
+
+
 # The launch picks how a tile's K is shared: by no wave (many tiles), by
 # the four waves of a work-group (4..63 scale groups per row), or by
 # sixteen (64 or more groups, when the staged x leaves room in LDS); where
